@@ -1,0 +1,161 @@
+// Host-side plumbing of librtp: status strings, thread-local error text,
+// descriptor validation and workspace sizing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rtp_internal.hpp"
+
+namespace rtp {
+
+static thread_local char g_err[512] = "";
+
+rtp_status fail(rtp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rtp_status ok() {
+  g_err[0] = '\0';
+  return RTP_OK;
+}
+
+rtp_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RTP_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+rtp_status check_desc(const rtp_layer_desc* d, Layer* L) {
+  if (!d) return fail(RTP_EINVAL, "descriptor is NULL");
+  if (d->batch < 1) return fail(RTP_EINVAL, "batch must be >= 1 (got %d)", d->batch);
+  if (d->n_kv_heads < 1 || d->n_kv_heads > kMaxHeads)
+    return fail(RTP_EINVAL, "n_kv_heads must be in [1, %d] (got %d)", kMaxHeads, d->n_kv_heads);
+  if (d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
+    return fail(RTP_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(RTP_EUNSUPPORTED, "GQA group size %d not supported (1, 2, 4, 8)", G);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RTP_EUNSUPPORTED, "head_dim %d not supported (64, 128)", d->head_dim);
+  if (d->idx_dim != kIdxDim) return fail(RTP_EUNSUPPORTED, "idx_dim must be 16 (got %d)", d->idx_dim);
+  if (d->n_cap < 1 || d->n_cap >= (int64_t(1) << 30))
+    return fail(RTP_EINVAL, "n_cap must be in [1, 2^30) (got %lld)", (long long)d->n_cap);
+  if (!d->kv_role) return fail(RTP_EINVAL, "kv_role is NULL");
+  if (d->n_sinks < 0) return fail(RTP_EINVAL, "n_sinks must be >= 0 (got %d)", d->n_sinks);
+  if (d->window < 1) return fail(RTP_EINVAL, "window must be >= 1 (got %d)", d->window);
+  L->B = d->batch;
+  L->Hq = d->n_q_heads;
+  L->Hkv = d->n_kv_heads;
+  L->D = d->head_dim;
+  L->G = G;
+  L->n_cap = d->n_cap;
+  L->n_ret = L->n_loc = 0;
+  for (int g = 0; g < d->n_kv_heads; ++g) {
+    uint8_t r = d->kv_role[g];
+    if (r > 1) return fail(RTP_EINVAL, "kv_role[%d] must be 0 or 1 (got %u)", g, (unsigned)r);
+    if (r) L->ret_kv[L->n_ret++] = g;
+    else L->loc_kv[L->n_loc++] = g;
+  }
+  L->n_sinks = d->n_sinks;
+  L->window = d->window;
+  return ok();
+}
+
+HeadMap ret_map(const Layer& L) {
+  HeadMap m{};
+  m.n = L.n_ret;
+  for (int i = 0; i < L.n_ret; ++i) m.kv[i] = L.ret_kv[i];
+  return m;
+}
+HeadMap loc_map(const Layer& L) {
+  HeadMap m{};
+  m.n = L.n_loc;
+  for (int i = 0; i < L.n_loc; ++i) m.kv[i] = L.loc_kv[i];
+  return m;
+}
+
+size_t score_ws_bytes(const Layer& L, int64_t n_ctx) {
+  int64_t nblk = (n_ctx + kScoreTile - 1) / kScoreTile;
+  return round_up(size_t(L.B) * L.n_ret * L.G * nblk * 2 * sizeof(float), 256);
+}
+
+SelLayout sel_layout(const Layer& L, int64_t n_ctx) {
+  SelLayout s{};
+  size_t rows = size_t(L.B) * L.n_ret * L.G;
+  s.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
+  size_t off = 0;
+  s.hist_mass = off;
+  off = round_up(off + rows * 3 * kBins * sizeof(uint64_t), 256);
+  s.hist_cnt = off;
+  off = round_up(off + rows * 3 * kBins * sizeof(uint32_t), 256);
+  s.state = off;
+  off = round_up(off + rows * sizeof(SelRowState), 256);
+  s.lookback = off;
+  off = round_up(off + rows * size_t(s.nblk) * sizeof(uint64_t), 256);
+  s.tile_ctr = off;
+  off = round_up(off + 256, 256);
+  s.total = off;
+  return s;
+}
+
+size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx) {
+  const int64_t nsplit = (n_ctx + kDecRange - 1) / kDecRange;
+  const size_t rows = size_t(L.B) * L.n_ret * L.G;
+  return round_up(rows * size_t(nsplit) * (L.D + 2) * sizeof(float), 256);
+}
+
+size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
+  int64_t nsplit;
+  size_t rows;
+  if (sparse) {
+    nsplit = (n_ctx + kDecRange - 1) / kDecRange;
+    rows = size_t(L.B) * L.n_ret * L.G;
+    return round_up(dec_sparse_starts_offset(L, n_ctx) + rows * size_t(nsplit + 1) * sizeof(int32_t), 256);
+  } else {
+    int64_t s_end = L.n_sinks < n_ctx ? L.n_sinks : n_ctx;
+    int64_t w_start = n_ctx - L.window > s_end ? n_ctx - L.window : s_end;
+    int64_t len = s_end + (n_ctx - w_start);
+    nsplit = (len + kWinRange - 1) / kWinRange;
+    rows = size_t(L.B) * L.n_loc * L.G;
+  }
+  return round_up(rows * size_t(nsplit) * (L.D + 2) * sizeof(float), 256);
+}
+
+}  // namespace rtp
+
+using namespace rtp;
+
+extern "C" size_t rtp_workspace_bytes(const rtp_layer_desc* desc, int64_t n_ctx, int which) {
+  Layer L;
+  if (check_desc(desc, &L) != RTP_OK || n_ctx < 1) return 0;
+  switch (which) {
+    case RTP_CALL_INDEXER_SCORE: return score_ws_bytes(L, n_ctx);
+    case RTP_CALL_TOPP_SELECT: return sel_layout(L, n_ctx).total;
+    case RTP_CALL_SPARSE_DECODE: return dec_ws_bytes(L, n_ctx, true);
+    case RTP_CALL_WINDOW_SINK: return dec_ws_bytes(L, n_ctx, false);
+    case RTP_CALL_PREFILL: return prefill_ws_bytes(L, n_ctx);
+    default: return 0;
+  }
+}
+
+extern "C" const char* rtp_status_string(rtp_status s) {
+  switch (s) {
+    case RTP_OK: return "RTP_OK";
+    case RTP_EINVAL: return "RTP_EINVAL";
+    case RTP_EUNSUPPORTED: return "RTP_EUNSUPPORTED";
+    case RTP_EWORKSPACE: return "RTP_EWORKSPACE";
+    case RTP_EDEVICE: return "RTP_EDEVICE";
+  }
+  return "RTP_UNKNOWN";
+}
+
+extern "C" const char* rtp_last_error(void) { return g_err; }
+
+extern "C" const char* rtp_version(void) { return "rtp 0.1.0 (gfx950)"; }

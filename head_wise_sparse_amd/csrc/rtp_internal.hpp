@@ -1,0 +1,135 @@
+// Internal declarations shared by the HIP sources of librtp (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstddef>
+
+#include "rtp.h"
+
+namespace rtp {
+
+constexpr int kIdxDim = 16;
+constexpr int kMaxHeads = 64;     // KV heads a descriptor may hold
+
+// ---------------------------------------------------------------- host-side helpers
+// Record a failure message for rtp_last_error() and return the status.
+rtp_status fail(rtp_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rtp_status ok();
+// Map a HIP error from a launch to RTP_EDEVICE (records the message).
+rtp_status check_launch(const char* what);
+
+// Head bookkeeping derived from a validated descriptor.
+struct Layer {
+  int B, Hq, Hkv, D, G;
+  int64_t n_cap;
+  int n_ret, n_loc;               // retrieval / local KV heads
+  int ret_kv[kMaxHeads];          // retrieval rank -> KV head
+  int loc_kv[kMaxHeads];          // local rank -> KV head
+  int n_sinks, window;
+};
+
+// Validate the descriptor (shared by every call).
+rtp_status check_desc(const rtp_layer_desc* d, Layer* L);
+bool aligned(const void* p, size_t a);
+
+// Kernel-argument table mapping a rank to its KV head (passed by value).
+struct HeadMap {
+  int n;
+  int kv[kMaxHeads];
+};
+HeadMap ret_map(const Layer& L);
+HeadMap loc_map(const Layer& L);
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- per-call workspace layouts
+// Indexer scoring: per-block (max, sum) partials.
+constexpr int kScoreThreads = 256;
+constexpr int kScoreItems = 8;                                  // tokens per thread
+constexpr int kScoreTile = kScoreThreads * kScoreItems;         // tokens per block
+size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
+
+// Top-p selection.
+constexpr int kSelThreads = 256;
+constexpr int kSelItems = 8;
+constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per block
+constexpr int kBins = 2048;                                     // 11-bit digits (last level 10 bits)
+struct SelRowState {             // one per score row, lives in the workspace
+  uint64_t target;               // mass the set must reach (fixed point)
+  uint64_t above;                // mass of tokens strictly above the current prefix
+  uint32_t prefix;               // key bits resolved so far
+  uint32_t cnt_above;            // tokens strictly above the current prefix
+  uint32_t done[3];              // blocks finished per histogram level
+  uint32_t take_ties;            // tokens to take among those tied at the threshold
+  uint32_t pad[6];
+};
+static_assert(sizeof(SelRowState) == 64, "row state is one 64-byte line");
+struct SelLayout {
+  size_t hist_mass, hist_cnt, state, lookback, tile_ctr, total;
+  int nblk;
+};
+SelLayout sel_layout(const Layer& L, int64_t n_ctx);
+
+// Decode attention (sparse and window share the layout).
+constexpr int kDecThreads = 256;
+constexpr int kDecRange = 2048;          // token-index range per block (sparse path)
+constexpr int kWinRange = 256;           // list positions per block (window path)
+size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);
+size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows][nsplit+1] after partials
+
+// Prefill.
+size_t prefill_ws_bytes(const Layer& L, int64_t C);
+
+}  // namespace rtp
+
+// ---------------------------------------------------------------- device helpers
+namespace rtp_dev {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// float -> bf16 round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Monotone key of an fp32 score: a larger score gives a larger key; -0 and +0 tie.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Fixed-point softmax weight of a score: round(exp(s - m) * 2^42), exp argument clamped to <= 0.
+__device__ __forceinline__ uint64_t fixed_weight(float s, float m) {
+  float w = __expf(fminf(s - m, 0.0f));
+  return (uint64_t)__builtin_rintf(w * 4398046511104.0f);   // 2^42; w*2^42 < 2^43 fits a float
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace rtp_dev

@@ -1,0 +1,194 @@
+// rtp_indexer_score: 16-dim pre-RoPE indexer scores for every cached token and
+// every retrieval query head, plus the softmax statistics (max, sum of exp) of each
+// score row.  (Abstract, observation (2): long-range retrieval through a
+// 16-dimensional indexer; research-map summary, "Approach": low-dimensional
+// pre-RoPE projection.)
+//
+// Work split: one block per (token tile of 2048, batch b, retrieval KV head r).
+// The 32-byte indexer key of each token is read from HBM once and scored against
+// all G query heads of the GQA group (the G score rows share that key stream).
+// Per-block (max, sum) partials are combined by a one-wave finalize kernel.
+#include <cmath>
+
+#include "rtp_internal.hpp"
+
+using namespace rtp;
+using namespace rtp_dev;
+
+namespace {
+
+template <int G, int D>
+__global__ __launch_bounds__(kScoreThreads) void k_indexer_score(
+    const uint16_t* __restrict__ q_pre, const uint16_t* __restrict__ w_q, int64_t w_stride,
+    const uint16_t* __restrict__ k_idx, float idx_scale, float* __restrict__ scores,
+    float2* __restrict__ part, int n_ctx, int64_t n_cap, int Hq, HeadMap map, int nblk) {
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int grp = blockIdx.y;              // b * n_ret + r
+  const int b = grp / map.n, r = grp % map.n;
+  const int g = map.kv[r];
+
+  __shared__ float s_q[G][D];
+  __shared__ float s_qidx[G][kIdxDim];
+  __shared__ float s_red[kScoreThreads / 64][G];
+
+  // ---- q_idx = q_pre . W_q_idx for the G heads of this group (fp32, not rounded)
+  for (int i = tid; i < G * D; i += kScoreThreads) {
+    const int t = i / D, d = i % D;
+    s_q[t][d] = bf16_to_f32(q_pre[(int64_t(b) * Hq + g * G + t) * D + d]);
+  }
+  __syncthreads();
+  {
+    constexpr int P = kScoreThreads / (G * kIdxDim);     // threads per output
+    const int o = tid / P, pi = tid % P;
+    const int t = o / kIdxDim, c = o % kIdxDim;
+    const uint16_t* w = w_q + int64_t(r * G + t) * w_stride;
+    float acc = 0.0f;
+    for (int d = pi; d < D; d += P) acc = fmaf(s_q[t][d], bf16_to_f32(w[d * kIdxDim + c]), acc);
+#pragma unroll
+    for (int off = P / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (pi == 0) s_qidx[t][c] = acc * idx_scale;
+  }
+  __syncthreads();
+  float qi[G][kIdxDim];
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int c = 0; c < kIdxDim; ++c) qi[t][c] = s_qidx[t][c];
+
+  // ---- score the tile: each thread takes tokens base + it*256 + tid (coalesced 32-byte rows)
+  const int64_t base = int64_t(blk) * kScoreTile;
+  const uint4* kp = reinterpret_cast<const uint4*>(k_idx + int64_t(grp) * n_cap * kIdxDim);
+  uint4 kr[kScoreItems][2];
+#pragma unroll
+  for (int it = 0; it < kScoreItems; ++it) {
+    const int64_t j = base + it * kScoreThreads + tid;
+    if (j < n_ctx) {
+      kr[it][0] = kp[2 * j];
+      kr[it][1] = kp[2 * j + 1];
+    }
+  }
+  float sc[kScoreItems][G];
+#pragma unroll
+  for (int it = 0; it < kScoreItems; ++it) {
+    const int64_t j = base + it * kScoreThreads + tid;
+    float kf[kIdxDim];
+    const uint32_t w8[8] = {kr[it][0].x, kr[it][0].y, kr[it][0].z, kr[it][0].w,
+                            kr[it][1].x, kr[it][1].y, kr[it][1].z, kr[it][1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[2 * e] = bf16_lo(w8[e]);
+      kf[2 * e + 1] = bf16_hi(w8[e]);
+    }
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      float s = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kIdxDim; ++c) s = fmaf(qi[t][c], kf[c], s);
+      sc[it][t] = (j < n_ctx) ? s : -INFINITY;
+      if (j < n_ctx) scores[(int64_t(grp) * G + t) * n_cap + j] = s;
+    }
+  }
+
+  // ---- per-block max and sum of exp for each of the G rows
+  const int wave = tid / 64, lane = tid % 64;
+  float mt[G];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < kScoreItems; ++it) m = fmaxf(m, sc[it][t]);
+    m = wave_max(m);
+    if (lane == 0) s_red[wave][t] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    float m = s_red[0][t];
+#pragma unroll
+    for (int w = 1; w < kScoreThreads / 64; ++w) m = fmaxf(m, s_red[w][t]);
+    mt[t] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    float z = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kScoreItems; ++it) z += __expf(sc[it][t] - mt[t]);
+    z = wave_sum(z);
+    if (lane == 0) s_red[wave][t] = z;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kScoreThreads / 64; ++w) z += s_red[w][tid];
+    part[(int64_t(grp) * G + tid) * nblk + blk] = make_float2(mt[tid], z);
+  }
+}
+
+// One wave per score row: combine the per-block partials into (row_max, row_sum).
+__global__ __launch_bounds__(64) void k_score_finalize(const float2* __restrict__ part, int nblk,
+                                                       float* __restrict__ row_max, float* __restrict__ row_sum) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const float2* p = part + int64_t(row) * nblk;
+  float m = -INFINITY;
+  for (int i = lane; i < nblk; i += 64) m = fmaxf(m, p[i].x);
+  m = wave_max(m);
+  float z = 0.0f;
+  for (int i = lane; i < nblk; i += 64) z += p[i].y * __expf(p[i].x - m);
+  z = wave_sum(z);
+  if (lane == 0) {
+    row_max[row] = m;
+    row_sum[row] = z;
+  }
+}
+
+template <int G, int D>
+void launch_score(dim3 grid, hipStream_t st, const uint16_t* q_pre, const uint16_t* w_q, int64_t ws,
+                  const uint16_t* k_idx, float scale, float* scores, float2* part, int n_ctx, int64_t n_cap,
+                  int Hq, const HeadMap& map, int nblk) {
+  hipLaunchKernelGGL((k_indexer_score<G, D>), grid, dim3(kScoreThreads), 0, st, q_pre, w_q, ws, k_idx, scale,
+                     scores, part, n_ctx, n_cap, Hq, map, nblk);
+}
+
+}  // namespace
+
+extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
+                                        const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
+                                        float idx_scale, float* scores, float* row_max, float* row_sum, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  Layer L;
+  rtp_status st = check_desc(desc, &L);
+  if (st != RTP_OK) return st;
+  if (n_ctx < 1 || n_ctx > L.n_cap)
+    return fail(RTP_EINVAL, "n_ctx must be in [1, n_cap=%lld] (got %lld)", (long long)L.n_cap, (long long)n_ctx);
+  if (L.n_ret == 0) return ok();
+  if (!q_pre || !w_q_idx || !k_idx || !scores || !row_max || !row_sum)
+    return fail(RTP_EINVAL, "rtp_indexer_score: NULL tensor pointer");
+  if (w_head_stride < 0) return fail(RTP_EINVAL, "w_head_stride must be >= 0");
+  if (!std::isfinite(idx_scale)) return fail(RTP_EINVAL, "idx_scale must be finite");
+  if (!aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(q_pre, 16) || !aligned(w_q_idx, 2))
+    return fail(RTP_EINVAL, "rtp_indexer_score: tensors must be 16-byte aligned");
+  const size_t need = score_ws_bytes(L, n_ctx);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(RTP_EWORKSPACE, "rtp_indexer_score: workspace needs %zu bytes, 256-aligned (got %zu)", need,
+                ws_bytes);
+
+  const int nblk = int((n_ctx + kScoreTile - 1) / kScoreTile);
+  const HeadMap map = ret_map(L);
+  const dim3 grid(nblk, L.B * L.n_ret);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float2* part = reinterpret_cast<float2*>(ws);
+  const int n = int(n_ctx);
+#define RTP_SCORE_CASE(GG, DD)                                                                              \
+  if (L.G == GG && L.D == DD)                                                                               \
+    launch_score<GG, DD>(grid, s, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, n, L.n_cap, \
+                         L.Hq, map, nblk);
+  RTP_SCORE_CASE(1, 64) RTP_SCORE_CASE(2, 64) RTP_SCORE_CASE(4, 64) RTP_SCORE_CASE(8, 64)
+  RTP_SCORE_CASE(1, 128) RTP_SCORE_CASE(2, 128) RTP_SCORE_CASE(4, 128) RTP_SCORE_CASE(8, 128)
+#undef RTP_SCORE_CASE
+  if ((st = check_launch("k_indexer_score")) != RTP_OK) return st;
+  hipLaunchKernelGGL(k_score_finalize, dim3(L.B * L.n_ret * L.G), dim3(64), 0, s, part, nblk, row_max, row_sum);
+  return check_launch("k_score_finalize");
+}

@@ -33,6 +33,8 @@ bits, so they can be handed to torch with ``.view(torch.bfloat16)``):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, Optional, Tuple
 
@@ -62,22 +64,38 @@ def _rng(cid: int, tid: int, a: int = 0, b: int = 0) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([BASE_SEED, cid, tid, a, b]))
 
 
+_ROPE_CACHE: Dict[Tuple[int, int, int], Tuple[np.ndarray, np.ndarray]] = {}
+
+
 def _rope_tables(positions: np.ndarray, d: int) -> Tuple[np.ndarray, np.ndarray]:
+    """float32 cos/sin tables [n][D/2] (angles computed in float64)."""
+    contiguous = positions.size > 1 and positions[-1] - positions[0] == positions.size - 1 \
+        and np.all(np.diff(positions) == 1)
+    key = (int(positions[0]), int(positions.size), d) if contiguous else None
+    if key is not None and key in _ROPE_CACHE:
+        return _ROPE_CACHE[key]
     half = d // 2
     inv_freq = ROPE_BASE ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
     ang = positions.astype(np.float64)[:, None] * inv_freq[None, :]
-    return np.cos(ang), np.sin(ang)
+    tab = (np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32))
+    if key is not None:
+        if len(_ROPE_CACHE) > 4:
+            _ROPE_CACHE.clear()
+        _ROPE_CACHE[key] = tab
+    return tab
 
 
 def _rope_bf16(x_bits: np.ndarray, positions: np.ndarray) -> np.ndarray:
-    """Rotate-half RoPE on bf16 rows [n][D] at the given positions -> bf16 bits."""
-    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    """Rotate-half RoPE (float32 arithmetic) on bf16 rows [n][D] at the given positions -> bf16 bits."""
+    x = bf16_bits_to_f32(x_bits)
     d = x.shape[-1]
     half = d // 2
-    cos, sin = _rope_tables(positions, d)
+    cos, sin = _rope_tables(np.asarray(positions), d)
     x1, x2 = x[..., :half], x[..., half:]
-    y = np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
-    return f32_to_bf16_bits(y.astype(np.float32))
+    y = np.empty_like(x)
+    y[..., :half] = x1 * cos - x2 * sin
+    y[..., half:] = x2 * cos + x1 * sin
+    return f32_to_bf16_bits(y)
 
 
 def _normal_bf16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
@@ -238,26 +256,32 @@ def make_decode_inputs(cfg: DecodeConfig, n_cap: Optional[int] = None,
     k = np.zeros((B, Hkv, ncap, D), np.uint16)
     v = np.zeros((B, Hkv, ncap, D), np.uint16)
     k_idx = np.zeros((B, Hkv_r, ncap, IDX_DIM), np.uint16)
-    needle_pos = np.zeros((B, Hkv_r, cfg.n_needles), np.int64)
+    n_needles = min(cfg.n_needles, N)
+    needle_pos = np.zeros((B, Hkv_r, n_needles), np.int64)
     pos = np.arange(N)
     wq64 = bf16_bits_to_f32(w_q).astype(np.float64)
     wk64 = bf16_bits_to_f32(w_k).astype(np.float64)
-    for b in range(B):
-        for g in range(Hkv):
-            k_pre = _normal_bf16(_rng(cid, T_K, b, g), (N, D))
-            k[b, g, :N] = _rope_bf16(k_pre, pos)
-            v[b, g, :N] = _normal_bf16(_rng(cid, T_V, b, g), (N, D))
-            if g in ret:
-                r = ret.index(g)
-                proj = bf16_bits_to_f32(k_pre).astype(np.float64) @ wk64[r]
-                k_idx[b, r, :N] = f32_to_bf16_bits(proj.astype(np.float32))
-                if cfg.n_needles:
-                    npos = np.sort(_rng(cid, T_NEEDLE, b, r).choice(N, size=cfg.n_needles, replace=False))
-                    needle_pos[b, r] = npos
-                    qi = [bf16_bits_to_f32(q_pre[b, g * G + t]).astype(np.float64) @ wq64[r * G + t]
-                          for t in range(G)]
-                    needle = 4.0 * np.mean(np.stack(qi), axis=0)
-                    k_idx[b, r, npos] = f32_to_bf16_bits(needle.astype(np.float32))[None, :]
+    _rope_tables(pos, D)                       # fill the table cache once
+
+    def one(bg):
+        b, g = bg
+        k_pre = _normal_bf16(_rng(cid, T_K, b, g), (N, D))
+        k[b, g, :N] = _rope_bf16(k_pre, pos)
+        v[b, g, :N] = _normal_bf16(_rng(cid, T_V, b, g), (N, D))
+        if g in ret:
+            r = ret.index(g)
+            proj = bf16_bits_to_f32(k_pre).astype(np.float64) @ wk64[r]
+            k_idx[b, r, :N] = f32_to_bf16_bits(proj.astype(np.float32))
+            if n_needles:
+                npos = np.sort(_rng(cid, T_NEEDLE, b, r).choice(N, size=n_needles, replace=False))
+                needle_pos[b, r] = npos
+                qi = [bf16_bits_to_f32(q_pre[b, g * G + t]).astype(np.float64) @ wq64[r * G + t]
+                      for t in range(G)]
+                needle = 4.0 * np.mean(np.stack(qi), axis=0)
+                k_idx[b, r, npos] = f32_to_bf16_bits(needle.astype(np.float32))[None, :]
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, [(b, g) for b in range(B) for g in range(Hkv)]))
     return DecodeInputs(cfg, ncap, q_pre, q, k, v, k_idx, w_q, w_k, cfg.kv_role, needle_pos, q_scale)
 
 

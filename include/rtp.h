@@ -1,0 +1,204 @@
+/*
+ * rtp.h -- C ABI of the head-wise sparse attention library (RTPurbo hot path)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Full Attention Strikes Back: Transferring Full Attention into Sparse
+ * within Hundred Training Steps" (arXiv 2605.16928).  Its abstract (OpenAlex
+ * record and podcast episode page) and the atlas.scime.ai research-map summary
+ * describe it in prose only:
+ *   - a small subset of attention heads ("retrieval heads") keep the full KV
+ *     cache; the others ("local heads") attend to a few sink tokens plus a
+ *     sliding window (abstract, observation (1); summary, "Approach");
+ *   - retrieval heads pick tokens with a 16-dimensional pre-RoPE indexer and a
+ *     query-adaptive top-p threshold over the indexer's softmax mass (abstract,
+ *     observations (2) and (3); summary, "Approach"), then attend over the
+ *     gathered K/V of that set (abstract: "lightweight token indexer for sparse
+ *     attention");
+ *   - during prefill retrieval heads stay dense (summary, "Limitations").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor pointers are DEVICE pointers into caller-owned memory, contiguous
+ *    in the layouts written next to each argument, 16-byte aligned.  bf16 means
+ *    IEEE bfloat16 raw bits (uint16_t); results are rounded to nearest even.
+ *  - Ownership: the library allocates nothing.  Scratch space comes from the
+ *    caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned); size it with
+ *    rtp_workspace_bytes().  A workspace may be reused by later calls on the same
+ *    stream; calls that run concurrently need distinct workspaces.
+ *  - Errors: every argument is validated on the host before anything is
+ *    enqueued.  On error nothing is launched and no output is touched; the
+ *    status is returned and rtp_last_error() (thread-local) explains it.
+ *    RTP_OK means the work was enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream).  There is no implicit synchronisation and no host<->device
+ *    copy; counts and thresholds stay on the device.  RTP_EDEVICE reports a
+ *    failed launch; faults inside kernels surface at the caller's next sync.
+ *  - Heads: G = n_q_heads / n_kv_heads; KV head g serves query heads
+ *    g*G .. g*G+G-1.  Retrieval KV heads (kv_role[g] == 1) are numbered by rank
+ *    r = 0,1,.. in increasing g; retrieval query head g*G+t has the compact index
+ *    r*G + t, which indexes w_q_idx, scores, row stats and selected sets.
+ *  - Supported: head_dim 64 or 128; G in {1,2,4,8}; idx_dim == 16;
+ *    n_cap < 2^30; batch >= 1 (prefill: batch == 1).
+ */
+#ifndef RTP_H
+#define RTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rtp_status {
+  RTP_OK = 0,
+  RTP_EINVAL = 1,        /* bad argument: null pointer, bad size, bad value, misaligned */
+  RTP_EUNSUPPORTED = 2,  /* valid but not implemented: head_dim, group size, idx_dim */
+  RTP_EWORKSPACE = 3,    /* ws_bytes smaller than rtp_workspace_bytes() */
+  RTP_EDEVICE = 4        /* a HIP launch or runtime call failed */
+} rtp_status;
+
+/* One attention layer.  Everything here lives in HOST memory. */
+typedef struct rtp_layer_desc {
+  int32_t batch;          /* sequences in the batch (B) */
+  int32_t n_q_heads;      /* Hq */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;       /* D */
+  int32_t idx_dim;        /* indexer dimension; must be 16 (abstract, observation (2)) */
+  int64_t n_cap;          /* cache capacity = token stride of every per-token tensor */
+  const uint8_t* kv_role; /* [Hkv] HOST array: 1 = retrieval head, 0 = local head */
+  int32_t n_sinks;        /* local heads: sink tokens at the start of the sequence (>= 0) */
+  int32_t window;         /* local heads: sliding window, counting the query token (>= 1) */
+} rtp_layer_desc;
+
+/* Which call rtp_workspace_bytes() sizes. */
+typedef enum rtp_call {
+  RTP_CALL_INDEXER_SCORE = 0,
+  RTP_CALL_TOPP_SELECT = 1,
+  RTP_CALL_SPARSE_DECODE = 2,
+  RTP_CALL_WINDOW_SINK = 3,
+  RTP_CALL_PREFILL = 4
+} rtp_call;
+
+/* Workspace bytes that call `which` needs for this layer at context n_ctx
+ * (prefill: n_ctx = chunk rows C).  Returns 0 for an invalid descriptor. */
+size_t rtp_workspace_bytes(const rtp_layer_desc* desc, int64_t n_ctx, int which);
+
+/*
+ * rtp_indexer_score -- indexer scores of every cached token for every retrieval
+ * query head, plus the softmax statistics of each score row.
+ * (abstract, observation (2); summary, "Approach": 16-dim pre-RoPE projection)
+ *
+ *   q_idx[b,c]   = q_pre[b, h(c)] . W_q_idx[c]            (fp32, never rounded)
+ *   s[b,c,j]     = idx_scale * <q_idx[b,c], k_idx[b, r(c), j]>   for 0 <= j < n_ctx
+ *   row_max[b,c] = max_j s[b,c,j];   row_sum[b,c] = sum_j exp(s[b,c,j] - row_max[b,c])
+ *
+ *   q_pre   bf16 [B][Hq][D]         pre-RoPE queries (all heads; only retrieval heads read)
+ *   w_q_idx bf16 [Hq_r][D][16]      query projections; head c starts at c*w_head_stride
+ *                                   elements (w_head_stride == 0: one matrix shared by all)
+ *   k_idx   bf16 [B][Hkv_r][n_cap][16]  stored pre-RoPE key projections
+ *   scores  fp32 [B][Hq_r][n_cap]   written for j < n_ctx
+ *   row_max, row_sum fp32 [B][Hq_r]
+ * n_ctx in [1, n_cap].  A layer with no retrieval head is valid and does nothing.
+ */
+rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ctx,
+                             const uint16_t* q_pre, const uint16_t* w_q_idx, int64_t w_head_stride,
+                             const uint16_t* k_idx, float idx_scale,
+                             float* scores, float* row_max, float* row_sum,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_topp_select -- the query-adaptive top-p token set of every score row.
+ * (abstract, observation (3): dynamic top-p instead of fixed top-k; summary,
+ * "Approach": query-adaptive top-p threshold)
+ *
+ * With pi_j = exp(s_j - row_max) / row_sum, tokens are ranked by score (higher
+ * first; equal scores: lower index first) and the set is the shortest prefix of
+ * that ranking whose mass reaches top_p.  top_p >= 1 keeps all n_ctx tokens.
+ * The mass is accumulated in 2^-42 fixed point (order independent, so results
+ * are bit-reproducible); a token whose rank sits within ~1e-6 of the p boundary
+ * may differ from an exact computation.
+ *
+ *   scores   fp32 [B][Hq_r][n_cap]  (j < n_ctx read), row_max/row_sum fp32 [B][Hq_r]
+ *            (row_sum is accepted for interface symmetry; the fixed-point total is used)
+ *   top_p    in (0, 1]; values > 1 act as 1; <= 0 or NaN -> RTP_EINVAL
+ *   sel_idx  int32 [B][Hq_r][n_cap]: the first sel_count entries of each row hold
+ *            the selected token indices in increasing order; the rest is untouched
+ *   sel_count int32 [B][Hq_r]
+ */
+rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
+                           const float* scores, const float* row_max, const float* row_sum,
+                           float top_p, int32_t* sel_idx, int32_t* sel_count,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_sparse_decode_attn -- decode attention of the retrieval heads over their
+ * selected tokens only (abstract: sparse attention through the token indexer).
+ *
+ *   out[b,h] = sum_{j in S(b,c)} softmax_j(sm_scale * q[b,h].k[b,g,j]) v[b,g,j]
+ *
+ *   q        bf16 [B][Hq][D]  post-RoPE queries
+ *   k_cache, v_cache bf16 [B][Hkv][n_cap][D]
+ *   sel_idx, sel_count  as written by rtp_topp_select (indices < n_ctx, increasing)
+ *   out      bf16 [B][Hq][D]; only retrieval heads' rows are written.  A row
+ *            with sel_count == 0 is written as zeros.
+ * Rows of one GQA group are processed together: a cached row selected by several
+ * heads of the group is read from HBM once.
+ */
+rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t n_ctx,
+                                  const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* sel_idx, const int32_t* sel_count, float sm_scale,
+                                  uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_window_sink_attn -- decode attention of the local heads over
+ * [0, min(n_sinks, n_ctx)) U [max(0, n_ctx - window), n_ctx): sinks plus a sliding
+ * window that includes the query token (summary, "Approach").
+ *
+ *   q bf16 [B][Hq][D]; k_cache, v_cache bf16 [B][Hkv][n_cap][D];
+ *   out bf16 [B][Hq][D]: only local heads' rows are written.
+ * The two decode calls write disjoint rows of `out`, so they may run concurrently
+ * on different streams (with distinct workspaces).
+ */
+rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n_ctx,
+                                const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                float sm_scale, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_prefill_attn -- one causal prefill chunk of one sequence (batch must be 1):
+ * query rows at absolute positions [c0, c0 + C).
+ *   - retrieval heads: dense causal attention, row i over keys [0, i]
+ *     (summary, "Limitations": retrieval heads stay dense in prefill);
+ *   - local heads: row i over [0, min(n_sinks, i+1)) U [max(0, i-window+1), i]
+ *     (summary, "Approach");
+ *   - the chunk's indexer keys, k_idx_cache[r][c0+t] = bf16(k_pre[t][g(r)] . W_k_idx[r]),
+ *     for every retrieval KV head (pre-RoPE key projection, summary "Approach").
+ *
+ *   q        bf16 [C][Hq][D]  post-RoPE queries of the chunk
+ *   k_cache, v_cache bf16 [Hkv][n_cap][D]: rows [0, c0 + C) valid (the caller has
+ *            appended the chunk's post-RoPE keys and values)
+ *   k_pre    bf16 [C][Hkv][D] pre-RoPE keys of the chunk (retrieval heads read)
+ *   w_k_idx  bf16 [Hkv_r][D][16]; head r starts at r*w_head_stride (0 = shared)
+ *   k_idx_cache bf16 [Hkv_r][n_cap][16]: rows [c0, c0+C) are written
+ *   out      bf16 [C][Hq][D]
+ * Requires c0 >= 0, C >= 1, c0 + C <= n_cap, head_dim == 128.
+ */
+rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, int32_t C,
+                            const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const uint16_t* k_pre, const uint16_t* w_k_idx, int64_t w_head_stride,
+                            uint16_t* k_idx_cache, float sm_scale, uint16_t* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* rtp_status_string(rtp_status s);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* rtp_last_error(void);
+
+/* Library version string. */
+const char* rtp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTP_H */

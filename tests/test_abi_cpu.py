@@ -1,0 +1,123 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol rtp.h declares, sizes
+workspaces, and rejects bad arguments on the host before anything is enqueued.
+
+No call here reaches a kernel launch (there is no GPU in this tier): every call
+fails host validation, and the fake device pointers are never dereferenced.
+"""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+from head_wise_sparse_amd import rtp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000            # 256-byte aligned stand-in address, never dereferenced
+
+
+def _lib():
+    if not os.path.exists(rtp.LIB_PATH):
+        pytest.fail("librtp.so is not built (run python -m head_wise_sparse_amd.build)")
+    return rtp.load()
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "rtp.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(rtp_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declarations_are_exported():
+    lib = _lib()
+    names = _declared()
+    assert {"rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn", "rtp_window_sink_attn",
+            "rtp_prefill_attn", "rtp_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(rtp.EXPORTED)
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert [lib.rtp_status_string(i).decode() for i in range(5)] == [
+        "RTP_OK", "RTP_EINVAL", "RTP_EUNSUPPORTED", "RTP_EWORKSPACE", "RTP_EDEVICE"]
+    assert "gfx950" in rtp.rtp_version()
+
+
+def _layer(**kw):
+    d = dict(batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128, n_cap=131072,
+             kv_role=[1, 0, 0, 1, 0, 0, 0, 0], n_sinks=4, window=4096)
+    d.update(kw)
+    return rtp.Layer(**d)
+
+
+def test_workspace_sizes():
+    L = _layer()
+    for w in range(5):
+        assert rtp.rtp_workspace_bytes(L, 131072 if w != 4 else 4096, w) > 0
+    # selection workspace: 3 histogram levels of 2048 (u64 mass + u32 count) per row
+    assert rtp.rtp_workspace_bytes(L, 131072, rtp.CALL_TOPP_SELECT) >= 32 * 3 * 2048 * 12
+    assert rtp.rtp_workspace_bytes(_layer(head_dim=96), 1000, 0) == 0          # invalid descriptor
+    assert rtp.rtp_workspace_bytes(L, 0, 0) == 0
+    assert rtp.rtp_workspace_bytes(L, 10, 9) == 0
+
+
+def _call_score(L, n_ctx=1000, ws_bytes=1 << 20, scale=1.0, ptr=FAKE):
+    lib = _lib()
+    return lib.rtp_indexer_score(L.desc if L else None, n_ctx, ptr, ptr, 0, ptr, scale, ptr, ptr, ptr,
+                                 FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(head_dim=96), rtp.RTP_EUNSUPPORTED, "head_dim"),
+    (dict(n_q_heads=30), rtp.RTP_EINVAL, "multiple"),
+    (dict(n_q_heads=24, n_kv_heads=2, kv_role=[1, 0]), rtp.RTP_EUNSUPPORTED, "group"),
+    (dict(idx_dim=32), rtp.RTP_EUNSUPPORTED, "idx_dim"),
+    (dict(window=0), rtp.RTP_EINVAL, "window"),
+    (dict(n_sinks=-1), rtp.RTP_EINVAL, "n_sinks"),
+    (dict(batch=0), rtp.RTP_EINVAL, "batch"),
+    (dict(n_cap=1 << 30), rtp.RTP_EINVAL, "n_cap"),
+    (dict(kv_role=[2, 0, 0, 0, 0, 0, 0, 0]), rtp.RTP_EINVAL, "kv_role"),
+])
+def test_descriptor_validation(kw, status, msg):
+    st = _call_score(_layer(**kw))
+    assert st == status
+    assert msg in _lib().rtp_last_error().decode()
+
+
+def test_call_validation():
+    lib = _lib()
+    L = _layer()
+    assert _call_score(None) == rtp.RTP_EINVAL
+    assert _call_score(L, n_ctx=0) == rtp.RTP_EINVAL
+    assert _call_score(L, n_ctx=L.n_cap + 1) == rtp.RTP_EINVAL
+    assert _call_score(L, ws_bytes=16) == rtp.RTP_EWORKSPACE
+    assert _call_score(L, scale=math.nan) == rtp.RTP_EINVAL
+    assert _call_score(L, ptr=FAKE + 2) == rtp.RTP_EINVAL                      # misaligned
+    assert _call_score(L, ptr=None) == rtp.RTP_EINVAL                          # NULL tensors
+    for p in (0.0, -0.5, math.nan):
+        assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, p, FAKE, FAKE, FAKE, 1 << 30, None) \
+            == rtp.RTP_EINVAL
+    assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, FAKE, 64, None) \
+        == rtp.RTP_EWORKSPACE
+    assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, 1 << 30,
+                                      None) == rtp.RTP_EINVAL
+    assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, math.inf, FAKE, FAKE, 1 << 30,
+                                      None) == rtp.RTP_EINVAL
+    assert lib.rtp_window_sink_attn(L.desc, 1000, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 8, None) \
+        == rtp.RTP_EWORKSPACE
+    L1 = _layer(batch=1, n_cap=32768)
+    assert lib.rtp_prefill_attn(_layer().desc, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0.1, FAKE, FAKE,
+                                1 << 30, None) == rtp.RTP_EINVAL                # batch must be 1
+    assert lib.rtp_prefill_attn(L1.desc, 32700, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0.1, FAKE, FAKE,
+                                1 << 30, None) == rtp.RTP_EINVAL                # c0 + C > n_cap
+    assert lib.rtp_prefill_attn(L1.desc, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0.1, FAKE, FAKE,
+                                1 << 30, None) == rtp.RTP_EINVAL                # C >= 1
+
+
+def test_binding_raises_with_message():
+    L = _layer(head_dim=96)
+    with pytest.raises(rtp.RtpError, match="RTP_EUNSUPPORTED: head_dim"):
+        rtp._check(_call_score(L))

@@ -1,0 +1,346 @@
+"""GPU parity of the decode path against the fp64 oracle, through the C ABI.
+
+Each call is checked on its own with oracle-made inputs (so a mismatch names the
+call), then the whole decode step is checked end to end on every decode
+configuration.  Sizes span several tiles and ragged tails; edge cases cover ties,
+p = 1, p -> 0, tiny and capacity-padded contexts, empty and full sets.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from head_wise_sparse_amd import rtp
+from head_wise_sparse_amd import workloads as W
+from oracle import rtp_oracle as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _inputs(name, **over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _CACHE:
+        cfg = W.CONFIGS[name]
+        if over:
+            cfg = W.scaled_decode(cfg, **over)
+        _CACHE.clear()
+        x = W.make_decode_inputs(cfg)
+        _CACHE[key] = (x, P.DeviceDecode(x))
+    return _CACHE[key]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ----------------------------------------------------------------------------- indexer scores
+@pytest.mark.parametrize("name,over", [("decode_tiny_2k", {}), ("decode_b8_32k", {}),
+                                       ("decode_b8_32k", dict(n_ctx=3001, batch=2)),
+                                       ("decode_b4_128k", {})])
+def test_indexer_scores(name, over):
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs(name, **over)
+    cfg = x.cfg
+    L = P.layer_for(cfg)
+    B, R, N = cfg.batch, cfg.n_kv_r * cfg.group, cfg.n_ctx
+    scores = torch.full((B * R * N,), float("nan"), dtype=torch.float32, device="cuda")
+    rmax = torch.empty(B * R, dtype=torch.float32, device="cuda")
+    rsum = torch.empty(B * R, dtype=torch.float32, device="cuda")
+    ws = rtp.workspace(L, N, rtp.CALL_INDEXER_SCORE)
+    rtp.rtp_indexer_score(L, N, d.q_pre, d.w_q_idx, cfg.head_dim * 16, d.k_idx, 1.0, scores, rmax, rsum, ws)
+    torch.cuda.synchronize()
+    sg = scores.view(B, R, N).cpu().numpy().astype(np.float64)
+    mg, zg = rmax.view(B, R).cpu().numpy(), rsum.view(B, R).cpu().numpy()
+    G = cfg.group
+    for b in range(B):
+        for ci in range(R):
+            r = ci // G
+            g = cfg.retrieval_kv[r]
+            qi = O.indexer_query(O.bf16_to_f64(x.q_pre[b, g * G + ci % G]), O.bf16_to_f64(x.w_q_idx[ci]))
+            so = O.indexer_scores(qi, O.bf16_to_f64(x.k_idx[b, r, :N]))
+            scale = P.score_scale(x, b, ci, r, N)
+            err = np.abs(sg[b, ci] - so)
+            assert np.all(err <= P.SCORE_RTOL * scale), f"row ({b},{ci}): worst {np.max(err / scale):.2e}"
+            assert abs(mg[b, ci] - so.max()) <= P.SCORE_RTOL * scale.max()
+            z = np.exp(so - so.max()).sum()
+            assert abs(zg[b, ci] - z) <= 1e-4 * z
+
+
+def test_indexer_scores_exact_on_integer_inputs():
+    """Small-integer bf16 inputs make every product and sum exact in fp32: bitwise equality."""
+    P.require_gpu()
+    torch = _torch()
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, D, N = 2, 8, 2, 64, 5000
+    L = rtp.Layer(B, Hq, Hkv, D, N + 100, [1, 1], 0, 1)
+    f = lambda a: W.f32_to_bf16_bits(a.astype(np.float32))
+    q_pre = f(rng.integers(-2, 3, (B, Hq, D)))
+    w = np.zeros((Hq, D, 16), np.float32)
+    for c in range(Hq):
+        w[c, rng.choice(D, 16, replace=False), np.arange(16)] = rng.integers(-2, 3, 16)
+    w = f(w)
+    k_idx = f(rng.integers(-3, 4, (B, 2, N + 100, 16)))
+    scores = torch.zeros(B * Hq * (N + 100), dtype=torch.float32, device="cuda")
+    rm = torch.empty(B * Hq, dtype=torch.float32, device="cuda")
+    rs = torch.empty_like(rm)
+    rtp.rtp_indexer_score(L, N, P.dev(q_pre), P.dev(w), D * 16, P.dev(k_idx), 1.0, scores, rm, rs,
+                          rtp.workspace(L, N, rtp.CALL_INDEXER_SCORE))
+    torch.cuda.synchronize()
+    sg = scores.view(B, Hq, N + 100).cpu().numpy()
+    for b in range(B):
+        for c in range(Hq):
+            qi = O.bf16_to_f64(q_pre[b, c]) @ O.bf16_to_f64(w[c])
+            so = O.bf16_to_f64(k_idx[b, c // 4, :N]) @ qi
+            assert np.array_equal(sg[b, c, :N].astype(np.float64), so)
+            assert np.all(sg[b, c, N:] == 0)                  # rows past n_ctx untouched
+
+
+# ----------------------------------------------------------------------------- top-p selection
+def _run_select(L, n_ctx, scores32: np.ndarray, p: float, n_cap=None):
+    """scores32: [rows][n_ctx] float32 -> list of selected index arrays."""
+    torch = _torch()
+    rows = scores32.shape[0]
+    cap = L.n_cap
+    s = np.zeros((rows, cap), np.float32)
+    s[:, :n_ctx] = scores32
+    st = torch.from_numpy(s).cuda()
+    m = torch.from_numpy(scores32.max(axis=1).astype(np.float32)).cuda()
+    z = torch.from_numpy(np.exp(scores32.astype(np.float64) - scores32.max(axis=1, keepdims=True))
+                         .sum(axis=1).astype(np.float32)).cuda()
+    sel = torch.full((rows * cap,), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    rtp.rtp_topp_select(L, n_ctx, st, m, z, p, sel, cnt, rtp.workspace(L, n_ctx, rtp.CALL_TOPP_SELECT))
+    torch.cuda.synchronize()
+    seln, cntn = sel.view(rows, cap).cpu().numpy(), cnt.cpu().numpy()
+    out = []
+    for r in range(rows):
+        c = int(cntn[r])
+        assert 1 <= c <= n_ctx
+        assert np.all(seln[r, c:] == -7), "entries past sel_count must be untouched"
+        out.append(seln[r, :c])
+    return out
+
+
+def _check_rows(scores32, sets, p):
+    ident = 0
+    for r in range(scores32.shape[0]):
+        s64 = scores32[r].astype(np.float64)
+        _, info = O.topp_select(s64, p)
+        same, _ = P.check_set(sets[r], info, p)
+        ident += same
+    return ident
+
+
+@pytest.mark.parametrize("name,p", [("decode_tiny_2k", 0.9), ("decode_b8_32k", 0.95), ("decode_b4_128k", 0.9),
+                                    ("decode_b4_128k", 0.95), ("decode_b4_128k", 0.99)])
+def test_topp_select_on_oracle_scores(name, p):
+    """Selection alone: the oracle's scores rounded to fp32 feed both sides, so both take
+    the ranking decision in the kernel's precision."""
+    P.require_gpu()
+    x, _ = _inputs(name)
+    cfg = x.cfg
+    G = cfg.group
+    rows = []
+    for b in range(cfg.batch):
+        for ci in range(cfg.n_kv_r * G):
+            r = ci // G
+            g = cfg.retrieval_kv[r]
+            qi = O.indexer_query(O.bf16_to_f64(x.q_pre[b, g * G + ci % G]), O.bf16_to_f64(x.w_q_idx[ci]))
+            rows.append(O.indexer_scores(qi, O.bf16_to_f64(x.k_idx[b, r, :cfg.n_ctx])).astype(np.float32))
+    s32 = np.stack(rows)
+    L = rtp.Layer(s32.shape[0], 1, 1, 128, cfg.n_ctx, [1], 0, 1)          # one score row per batch entry
+    sets = _run_select(L, cfg.n_ctx, s32, p)
+    ident = _check_rows(s32, sets, p)
+    assert ident >= 0.9 * len(sets)
+
+
+def _edge_rows():
+    rng = np.random.default_rng(11)
+    yield "all_tied", np.zeros((2, 5000), np.float32), 0.5
+    two = np.zeros((1, 4097), np.float32)
+    two[0, rng.choice(4097, 300, replace=False)] = 1.0
+    yield "two_levels_tied", two, 0.37
+    yield "p_one", rng.standard_normal((3, 2049)).astype(np.float32), 1.0
+    yield "p_tiny", np.round(rng.standard_normal((3, 3000)), 1).astype(np.float32), 1e-7
+    yield "single_token", np.float32([[3.5], [-2.0]]), 0.9
+    z = rng.standard_normal((2, 6000)).astype(np.float32)
+    z[:, ::7] = 0.0
+    z[:, 3::7] = -0.0
+    yield "signed_zeros", z, 0.8
+    yield "wide_spread", (rng.standard_normal((2, 9000)) * 300).astype(np.float32), 0.95
+    yield "narrow_spread", (5 + rng.standard_normal((2, 20000)) * 1e-3).astype(np.float32), 0.9
+    yield "ragged_many_tiles", rng.standard_normal((4, 2048 * 5 + 3)).astype(np.float32) * 3, 0.99
+
+
+@pytest.mark.parametrize("case", list(_edge_rows()), ids=lambda c: c[0])
+def test_topp_select_edge_cases(case):
+    P.require_gpu()
+    _, s32, p = case
+    n = s32.shape[1]
+    L = rtp.Layer(s32.shape[0], 1, 1, 64, n + 37, [1], 0, 1)      # capacity larger than the context
+    sets = _run_select(L, n, s32, p)
+    _check_rows(s32, sets, p)
+    if case[0] == "all_tied":
+        assert all(np.array_equal(s, np.arange(2500)) for s in sets)   # lowest indices first
+    if case[0] == "p_tiny":
+        for r, s in enumerate(sets):
+            assert s.tolist() == [int(np.flatnonzero(s32[r] == s32[r].max())[0])]
+
+
+# ----------------------------------------------------------------------------- sparse decode
+def _sel_tensors(sets, B, R, cap):
+    torch = _torch()
+    sel = np.zeros((B, R, cap), np.int32)
+    cnt = np.zeros((B, R), np.int32)
+    for (b, ci), s in sets.items():
+        sel[b, ci, :len(s)] = s
+        cnt[b, ci] = len(s)
+    return torch.from_numpy(sel).cuda(), torch.from_numpy(cnt).cuda()
+
+
+@pytest.mark.parametrize("name,over", [("decode_tiny_2k", {}), ("decode_b8_32k", {}),
+                                       ("decode_b8_32k", dict(batch=2, n_ctx=5000))])
+def test_sparse_decode_on_oracle_sets(name, over):
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs(name, **over)
+    cfg = x.cfg
+    N, B, G = cfg.n_ctx, cfg.batch, cfg.group
+    R = cfg.n_kv_r * G
+    ora = O.decode_step(x.q_pre, x.q, x.k, x.v, x.k_idx, x.w_q_idx, x.kv_role, N, cfg.top_p, cfg.n_sinks,
+                        cfg.window)
+    L = P.layer_for(cfg)
+    sel, cnt = _sel_tensors(ora["sel"], B, R, N)
+    out = torch.zeros(B * cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, 1 / math.sqrt(cfg.head_dim), out,
+                               rtp.workspace(L, N, rtp.CALL_SPARSE_DECODE))
+    torch.cuda.synchronize()
+    g = rtp.from_device_bf16(out).reshape(B, cfg.n_q_heads, cfg.head_dim)
+    heads = [gg * G + t for gg in cfg.retrieval_kv for t in range(G)]
+    P.check_outputs(g[:, heads], ora["out"][:, heads], "sparse decode")
+    loc = [h for h in range(cfg.n_q_heads) if h not in heads]
+    assert np.all(g[:, loc] == 0), "local-head rows must not be written"
+
+
+def test_sparse_decode_special_sets():
+    """Empty set -> zeros; one token -> that V row; every token -> dense attention;
+    overlapping random sets inside a GQA group."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=1, n_ctx=7000)
+    cfg = x.cfg
+    N, G = cfg.n_ctx, cfg.group
+    rng = np.random.default_rng(3)
+    sets = {(0, 0): np.zeros(0, np.int64), (0, 1): np.array([4321]), (0, 2): np.arange(N),
+            (0, 3): np.sort(rng.choice(N, 3000, replace=False)),
+            (0, 4): np.sort(rng.choice(N, 50, replace=False)), (0, 5): np.arange(0, N, 3),
+            (0, 6): np.arange(2040, 2060), (0, 7): np.array([0, N - 1])}
+    L = P.layer_for(cfg)
+    sel, cnt = _sel_tensors(sets, 1, 8, N)
+    out = torch.zeros(cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, 1 / math.sqrt(128), out,
+                               rtp.workspace(L, N, rtp.CALL_SPARSE_DECODE))
+    torch.cuda.synchronize()
+    g = rtp.from_device_bf16(out).reshape(cfg.n_q_heads, 128)
+    for (b, ci), s in sets.items():
+        h = cfg.retrieval_kv[ci // G] * G + ci % G
+        kv = cfg.retrieval_kv[ci // G]
+        if len(s) == 0:
+            assert np.all(g[h] == 0)
+            continue
+        ref = O.attend(O.bf16_to_f64(x.q[0, h]), O.bf16_to_f64(x.k[0, kv, :N]), O.bf16_to_f64(x.v[0, kv, :N]), s,
+                       1 / math.sqrt(128))
+        P.check_outputs(g[h][None], ref[None], f"set {ci}")
+    assert np.array_equal(g[cfg.retrieval_kv[0] * G + 1], x.v[0, cfg.retrieval_kv[0], 4321])
+
+
+# ----------------------------------------------------------------------------- window + sinks
+@pytest.mark.parametrize("name,over", [("decode_tiny_2k", {}), ("decode_b8_32k", {}),
+                                       ("decode_b8_32k", dict(batch=1, n_ctx=3)),
+                                       ("decode_b8_32k", dict(batch=1, n_ctx=700, window=5000)),
+                                       ("decode_b8_32k", dict(batch=1, n_ctx=999, window=1, n_sinks=0)),
+                                       ("decode_b8_32k", dict(batch=2, n_ctx=4000, window=3, n_sinks=7)),
+                                       ("decode_tiny_2k", dict(n_sinks=300, window=1800))])
+def test_window_sink_decode(name, over):
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs(name, **over)
+    cfg = x.cfg
+    N, B, G = cfg.n_ctx, cfg.batch, cfg.group
+    L = P.layer_for(cfg)
+    out = torch.zeros(B * cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+    rtp.rtp_window_sink_attn(L, N, d.q, d.k, d.v, 1 / math.sqrt(cfg.head_dim), out,
+                             rtp.workspace(L, N, rtp.CALL_WINDOW_SINK))
+    torch.cuda.synchronize()
+    g = rtp.from_device_bf16(out).reshape(B, cfg.n_q_heads, cfg.head_dim)
+    lset = O.local_set(N, cfg.n_sinks, cfg.window)
+    ref = np.zeros((B, cfg.n_q_heads, cfg.head_dim))
+    loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
+    for b in range(B):
+        for h in loc:
+            kv = h // G
+            ref[b, h] = O.attend(O.bf16_to_f64(x.q[b, h]), O.bf16_to_f64(x.k[b, kv, :N]),
+                                 O.bf16_to_f64(x.v[b, kv, :N]), lset, 1 / math.sqrt(cfg.head_dim))
+    P.check_outputs(g[:, loc], ref[:, loc], "window decode")
+    ret = [h for h in range(cfg.n_q_heads) if h not in loc]
+    assert np.all(g[:, ret] == 0), "retrieval-head rows must not be written"
+
+
+# ----------------------------------------------------------------------------- whole decode step
+def _decode_step(name, p, **over):
+    torch = _torch()
+    x, d = _inputs(name, **over)
+    cfg = x.cfg
+    L = P.layer_for(cfg)
+    step = rtp.DecodeStep(L, cfg.n_ctx, p)
+    out = step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+    torch.cuda.synchronize()
+    return x, d, step, out
+
+
+@pytest.mark.parametrize("name,p", [("decode_tiny_2k", 0.9), ("decode_b8_32k", 0.95), ("decode_b4_128k", 0.9),
+                                    ("decode_b4_128k", 0.95), ("decode_b4_128k", 0.99), ("decode_b1_1m", 0.95)])
+def test_decode_step_end_to_end(name, p):
+    P.require_gpu()
+    x, d, step, out = _decode_step(name, p)
+    cfg = x.cfg
+    N, B, G = cfg.n_ctx, cfg.batch, cfg.group
+    R = cfg.n_kv_r * G
+    ora = O.decode_step(x.q_pre, x.q, x.k, x.v, x.k_idx, x.w_q_idx, x.kv_role, N, p, cfg.n_sinks, cfg.window)
+    g = rtp.from_device_bf16(out).reshape(B, cfg.n_q_heads, cfg.head_dim)
+    cnt = step.sel_count.view(B, R).cpu().numpy()
+    sel = step.sel_idx.view(B, R, N).cpu().numpy()
+    identical, sizes = [], []
+    for b in range(B):
+        for ci in range(R):
+            r = ci // G
+            scale = P.score_scale(x, b, ci, r, N)
+            same, _ = P.check_set(sel[b, ci, :cnt[b, ci]], ora["info"][(b, ci)], p, ora["scores"][(b, ci)],
+                                  P.FP32_SCORE_SLACK * scale)
+            h = cfg.retrieval_kv[r] * G + ci % G
+            if same:
+                P.check_outputs(g[b, h][None], ora["out"][b, h][None], f"retrieval row ({b},{h})")
+            identical.append(same)
+            sizes.append(int(cnt[b, ci]))
+    loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
+    P.check_outputs(g[:, loc], ora["out"][:, loc], "local rows")
+    print(f"\n{name} p={p}: |S| min {min(sizes)} median {int(np.median(sizes))} mean {np.mean(sizes):.0f} "
+          f"max {max(sizes)}; sets identical {sum(identical)}/{len(identical)}")
+    assert sum(identical) >= 0.9 * len(identical)
+
+
+def test_decode_step_is_deterministic():
+    P.require_gpu()
+    torch = _torch()
+    x, d, step, out = _decode_step("decode_b8_32k", 0.95)
+    a = [t.clone() for t in (step.scores, step.row_max, step.sel_count, step.sel_idx, out)]
+    out2 = step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+    torch.cuda.synchronize()
+    b = [step.scores, step.row_max, step.sel_count, step.sel_idx, out2]
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
