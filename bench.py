@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the head-wise sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over synthetic inputs:
+  * a decode step of one layer at 128K context, batch 4, 32 q / 8 KV heads, d128:
+    indexer scores -> top-p sets (p = 0.95) -> sparse attention of the 2 retrieval
+    KV heads (+ their 8 q heads) and sink+window attention of the 6 local KV heads;
+  * a causal 32K-token prefill of one sequence in 4K chunks (retrieval heads dense,
+    local heads 4 sinks + 4096 window, indexer keys projected in the chunk).
+
+Inputs are resident in HBM before the timed region.  Decode rotates over several
+copies of the layer's caches so consecutive steps do not hit in the 256 MB
+Infinity Cache.  Prints one JSON line (see the fields below).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=3, help="decode cache copies rotated across steps")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the p = 0.9 / 0.99 decode timings")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run only one part (for profiling); the JSON line is still printed")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- decode
+class DecodeBench:
+    def __init__(self, copies: int):
+        import torch
+        from head_wise_sparse_amd import rtp
+        from head_wise_sparse_amd import workloads as W
+        self.torch, self.rtp = torch, rtp
+        self.cfg = cfg = W.CONFIGS["decode_b4_128k"]
+        t = time.time()
+        self.x = x = W.make_decode_inputs(cfg)
+        log(f"decode inputs drawn in {time.time() - t:.1f}s")
+        self.L = rtp.Layer(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx,
+                           cfg.kv_role.tolist(), cfg.n_sinks, cfg.window)
+        dev = rtp.to_device_bf16
+        base = dict(q_pre=dev(x.q_pre), q=dev(x.q), k=dev(x.k), v=dev(x.v), k_idx=dev(x.k_idx),
+                    w_q_idx=dev(x.w_q_idx))
+        self.sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(copies - 1)]
+        self.steps = {}
+        self.graphs = {}
+        torch.cuda.synchronize()
+
+    def _step_obj(self, p: float):
+        if p not in self.steps:
+            self.steps[p] = self.rtp.DecodeStep(self.L, self.cfg.n_ctx, p)
+        return self.steps[p]
+
+    def _launch(self, p: float, i: int, which=None):
+        """Enqueue the decode step (or one of its calls) on the current stream."""
+        rtp, L, n = self.rtp, self.L, self.cfg.n_ctx
+        st = self._step_obj(p)
+        s = self.sets[i % len(self.sets)]
+        if which is None:
+            return st.run(s["q_pre"], s["q"], s["k"], s["v"], s["k_idx"], s["w_q_idx"])
+        if which == "indexer_score":
+            rtp.rtp_indexer_score(L, n, s["q_pre"], s["w_q_idx"], L.head_dim * 16, s["k_idx"], 1.0, st.scores,
+                                  st.row_max, st.row_sum, st.ws[rtp.CALL_INDEXER_SCORE])
+        elif which == "topp_select":
+            rtp.rtp_topp_select(L, n, st.scores, st.row_max, st.row_sum, p, st.sel_idx, st.sel_count,
+                                st.ws[rtp.CALL_TOPP_SELECT])
+        elif which == "sparse_decode":
+            rtp.rtp_sparse_decode_attn(L, n, s["q"], s["k"], s["v"], st.sel_idx, st.sel_count, st.sm_scale,
+                                       st.out, st.ws[rtp.CALL_SPARSE_DECODE])
+        elif which == "window_sink":
+            rtp.rtp_window_sink_attn(L, n, s["q"], s["k"], s["v"], st.sm_scale, st.out,
+                                     st.ws[rtp.CALL_WINDOW_SINK])
+
+    def graph(self, p: float, i: int, which=None):
+        """A HIP graph (captured through torch) of the step or of one call, on cache copy i."""
+        key = (p, i % len(self.sets), which)
+        if key not in self.graphs:
+            torch = self.torch
+            self._launch(p, i, which)                 # eager run first: allocations happen outside capture
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._launch(p, i, which)
+            torch.cuda.synchronize()
+            self.graphs[key] = g
+        return self.graphs[key]
+
+    def step(self, p: float, i: int):
+        self.graph(p, i).replay()
+
+    def call_times(self, p: float, reps: int = 20):
+        """Average duration (ms) of each of the four calls: each call is captured in its own
+        graph and replayed `reps` times between HIP events on the launch stream."""
+        torch = self.torch
+        names = ["indexer_score", "topp_select", "sparse_decode", "window_sink"]
+        out = {}
+        for k in names:
+            gs = [self.graph(p, i, k) for i in range(len(self.sets))]
+            for g in gs:
+                g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(reps):
+                gs[i % len(gs)].replay()
+            b.record()
+            torch.cuda.synchronize()
+            out[k] = a.elapsed_time(b) / reps
+        return out
+
+    def algorithmic_bytes(self, p: float):
+        """Bytes the method must move for one decode step (not the dense work it avoids)."""
+        cfg, st = self.cfg, self.steps[p]
+        B, N, D, G = cfg.batch, cfg.n_ctx, cfg.head_dim, cfg.group
+        R = cfg.n_kv_r * G
+        cnt = st.sel_count.view(B, R).cpu().numpy()
+        sel = st.sel_idx.view(B, R, -1).cpu().numpy()
+        union = 0
+        per_head = int(cnt.sum())
+        for b in range(B):
+            for r in range(cfg.n_kv_r):
+                u = np.unique(np.concatenate([sel[b, r * G + t, :cnt[b, r * G + t]] for t in range(G)]))
+                union += u.size
+        s_end = min(cfg.n_sinks, N)
+        w_start = max(N - cfg.window, s_end)
+        n_local = s_end + (N - w_start)
+        n_loc_kv = cfg.n_kv_heads - cfg.n_kv_r
+        kidx = 32 * N * B * cfg.n_kv_r
+        local = 4 * D * n_local * B * n_loc_kv
+        gathered = 4 * D * union
+        qo = 2 * 2 * D * B * cfg.n_q_heads
+        return {"kidx": kidx, "local_kv": local, "gathered_kv_union": gathered, "q_out": qo,
+                "total": kidx + local + gathered + qo, "union_tokens": union, "per_head_tokens": per_head,
+                "sel_min": int(cnt.min()), "sel_median": int(np.median(cnt)), "sel_mean": float(cnt.mean()),
+                "sel_max": int(cnt.max())}
+
+
+# ----------------------------------------------------------------------------- prefill
+class PrefillBench:
+    def __init__(self):
+        import torch
+        from head_wise_sparse_amd import rtp
+        from head_wise_sparse_amd import workloads as W
+        self.torch, self.rtp = torch, rtp
+        self.cfg = cfg = W.CONFIGS["prefill_32k"]
+        t = time.time()
+        self.pi = W.PrefillInputs(cfg)
+        k, v, kp = self.pi.full_kv()
+        qs = [self.pi.q_chunk(c) for c in range(cfg.n_chunks)]
+        log(f"prefill inputs drawn in {time.time() - t:.1f}s")
+        dev = rtp.to_device_bf16
+        self.L = rtp.Layer(1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.kv_role.tolist(),
+                           cfg.n_sinks, cfg.window)
+        self.k, self.v = dev(k), dev(v)
+        self.k_pre = [dev(kp[c * cfg.chunk:(c + 1) * cfg.chunk]) for c in range(cfg.n_chunks)]
+        self.q = [dev(q) for q in qs]
+        self.w = dev(self.pi.w_k_idx)
+        self.k_idx = torch.zeros(cfg.n_kv_r * cfg.seq_len * 16, dtype=torch.bfloat16, device="cuda")
+        self.out = [torch.empty(cfg.chunk * cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+                    for _ in range(cfg.n_chunks)]
+        self.ws = rtp.workspace(self.L, cfg.chunk, rtp.CALL_PREFILL)
+        self.sm = 1.0 / math.sqrt(cfg.head_dim)
+        torch.cuda.synchronize()
+
+    def run(self):
+        cfg, rtp = self.cfg, self.rtp
+        for c in range(cfg.n_chunks):
+            c0, c1 = self.pi.chunk_bounds(c)
+            rtp.rtp_prefill_attn(self.L, c0, c1 - c0, self.q[c], self.k, self.v, self.k_pre[c], self.w,
+                                 cfg.head_dim * 16, self.k_idx, self.sm, self.out[c], self.ws)
+
+    def flops(self):
+        """Algorithmic FLOPs: 4*D per attended (row, key) pair, exact mask pair counts, plus the projection."""
+        cfg = self.cfg
+        T, D, G = cfg.seq_len, cfg.head_dim, cfg.group
+        n_ret_q = cfg.n_kv_r * G
+        n_loc_q = (cfg.n_kv_heads - cfg.n_kv_r) * G
+        dense_pairs = T * (T + 1) // 2
+        i = np.arange(T, dtype=np.int64)
+        s = np.minimum(cfg.n_sinks, i + 1)
+        wlo = np.maximum(s, i - cfg.window + 1)           # window part not already counted as sinks
+        band_pairs = int((s + (i + 1 - wlo)).sum())
+        attn = 4 * D * (dense_pairs * n_ret_q + band_pairs * n_loc_q)
+        proj = 2 * T * D * 16 * cfg.n_kv_r
+        return {"dense_pairs_per_head": dense_pairs, "band_pairs_per_head": band_pairs, "attn": attn,
+                "kidx_proj": proj, "total": attn + proj}
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(dec: DecodeBench):
+    """The fp64 oracle, single-threaded, on one batch entry of the 128K decode step
+    (all 32 heads), scaled by the batch size to a whole step."""
+    from threadpoolctl import threadpool_limits
+    from oracle import rtp_oracle as O
+    x, cfg = dec.x, dec.cfg
+    with threadpool_limits(limits=1):
+        reps, t0 = 0, time.time()
+        while True:
+            O.decode_step(x.q_pre, x.q, x.k, x.v, x.k_idx, x.w_q_idx, x.kv_role, cfg.n_ctx, cfg.top_p, cfg.n_sinks,
+                          cfg.window, batch_rows=[reps % cfg.batch])
+            reps += 1
+            if time.time() - t0 > 10.0 or reps >= 8:
+                break
+        per_row = (time.time() - t0) / reps
+    return {"value": per_row * cfg.batch * 1e6, "unit": "us/step/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} batch entr{'y' if reps == 1 else 'ies'} of the 128K decode step (all 32 heads, "
+                      f"p=0.95), fp64 numpy on 1 thread, scaled by batch {cfg.batch}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from head_wise_sparse_amd import rtp
+    torch.cuda.set_device(0)
+    log(f"device {torch.cuda.get_device_name(0)}, {rtp.rtp_version()}")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    do_dec = args.only in (None, "decode")
+    do_pre = args.only in (None, "prefill") and not args.no_prefill
+    dec = DecodeBench(args.copies) if do_dec else None
+    pre = None
+    if do_pre:
+        pre = PrefillBench()
+        try:
+            pre.run()
+            torch.cuda.synchronize()
+        except rtp.RtpError as e:
+            log(f"prefill unavailable: {e}")
+            pre = None
+
+    p0 = 0.95
+    for i in range(args.warmup):
+        if dec:
+            dec.step(p0, i)
+        if pre:
+            pre.run()
+    torch.cuda.synchronize()
+
+    t_dec = t_pre = 0.0
+    e_all0, e_all1 = ev(), ev()
+    torch.cuda.synchronize()
+    e_all0.record()
+    wall0 = time.time()
+    for i in range(args.steps):
+        if dec:
+            a, b = ev(), ev()
+            a.record()
+            dec.step(p0, i)
+            b.record()
+        if pre:
+            c, d = ev(), ev()
+            c.record()
+            pre.run()
+            d.record()
+        torch.cuda.synchronize()
+        if dec:
+            t_dec += a.elapsed_time(b)
+        if pre:
+            t_pre += c.elapsed_time(d)
+    e_all1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    ms_step = e_all0.elapsed_time(e_all1) / args.steps
+    dec_ms = t_dec / args.steps if dec else None
+    pre_ms = t_pre / args.steps if pre else None
+
+    res = {"metric": "sparse decode us/step/layer + HBM GB/s @128K; prefill attn ms + MFMA util",
+           "value": round(dec_ms * 1e3, 3) if dec_ms is not None else None, "unit": "us/step/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; needles planted in the indexer keys; no datasets or trained weights)",
+           "config": {"workload": "decode 128K x batch 4, 32q/8kv heads d128, 2 retrieval KV heads p=0.95, "
+                                  "6 local KV heads (4 sinks + 4096 window); + prefill 32K in 4K chunks",
+                      "decode": "decode_b4_128k", "prefill": "prefill_32k"}}
+    rooflines = {}
+    if dec:
+        ab = dec.algorithmic_bytes(p0)
+        calls = dec.call_times(p0)
+        gbs = ab["total"] / (dec_ms * 1e-3) / 1e9
+        res["decode"] = {"us_per_step": round(dec_ms * 1e3, 2), "hbm_GBps": round(gbs, 1),
+                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": ab,
+                         "call_us": {k: round(v * 1e3, 2) for k, v in calls.items()}}
+        sp_bytes = ab["gathered_kv_union"] + 2 * 2 * dec.cfg.head_dim * dec.cfg.batch * dec.cfg.n_kv_r * dec.cfg.group
+        sp_gbs = sp_bytes / (calls["sparse_decode"] * 1e-3) / 1e9
+        rooflines["sparse_decode"] = {"bound": "hbm", "achieved": round(sp_gbs, 1), "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": round(sp_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                      "kernel": "rtp_sparse_decode_attn (k_range_starts + k_decode_partial + "
+                                                "k_decode_merge)", "us": round(calls["sparse_decode"] * 1e3, 2)}
+        if not args.no_sweep:
+            sweep = {}
+            for p in (0.9, 0.99):
+                for i in range(2):
+                    dec.step(p, i)
+                torch.cuda.synchronize()
+                a, b = ev(), ev()
+                a.record()
+                for i in range(10):
+                    dec.step(p, i)
+                b.record()
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) / 10 * 1e3
+                abp = dec.algorithmic_bytes(p)
+                sweep[str(p)] = {"us_per_step": round(us, 2),
+                                 "hbm_GBps": round(abp["total"] / (us * 1e-6) / 1e9, 1),
+                                 "sel_mean": round(abp["sel_mean"], 1), "union_tokens": abp["union_tokens"]}
+            res["decode"]["p_sweep"] = sweep
+    if pre:
+        fl = pre.flops()
+        tflops = fl["total"] / (pre_ms * 1e-3) / 1e12
+        res["prefill"] = {"ms": round(pre_ms, 3), "tflops": round(tflops, 1),
+                          "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "flops": fl}
+        rooflines["prefill_attn"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                     "traffic": None, "kernel": "rtp_prefill_attn (k_kidx_proj + k_prefill_attn)",
+                                     "ms_per_chunk": round(pre_ms / pre.cfg.n_chunks, 4)}
+    # the dominant kernel of the step is the one that takes the most time
+    if rooflines:
+        dom = "prefill_attn" if "prefill_attn" in rooflines else "sparse_decode"
+        res["roofline"] = rooflines[dom]
+        res["rooflines"] = rooflines
+    if dec and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(dec)
+    res["wall_s_timed"] = round(wall, 3)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

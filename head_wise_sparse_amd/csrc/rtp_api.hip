@@ -95,12 +95,16 @@ SelLayout sel_layout(const Layer& L, int64_t n_ctx) {
   off = round_up(off + rows * 3 * kBins * sizeof(uint64_t), 256);
   s.hist_cnt = off;
   off = round_up(off + rows * 3 * kBins * sizeof(uint32_t), 256);
+  s.coarse_mass = off;
+  off = round_up(off + rows * 3 * 64 * sizeof(uint64_t), 256);
+  s.coarse_cnt = off;
+  off = round_up(off + rows * 3 * 64 * sizeof(uint32_t), 256);
   s.state = off;
   off = round_up(off + rows * sizeof(SelRowState), 256);
+  s.tile_ctr = off;
+  off = round_up(off + rows * sizeof(uint32_t), 256);
   s.lookback = off;
   off = round_up(off + rows * size_t(s.nblk) * sizeof(uint64_t), 256);
-  s.tile_ctr = off;
-  off = round_up(off + 256, 256);
   s.total = off;
   return s;
 }

@@ -9,7 +9,7 @@
 // Both are split-K flash decoding.  A block owns one GQA group (batch b, KV head g)
 // and one slice of that group's token list; it reads each cached K/V row of the
 // slice from HBM once and applies it to all G query heads of the group.  For the
-// sparse path the slice is a token-index range [j0, j0+2048): the block unions the
+// sparse path the slice is a token-index range [j0, j0+1024): the block unions the
 // G heads' selected sets inside the range (per-head membership bytes in LDS, then
 // an ordered compaction into an LDS token list with a G-bit head mask per token),
 // so a row chosen by several heads of the group is loaded once.  For the window
@@ -75,7 +75,7 @@ struct DecArgs {
 };
 
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kDecThreads, 2) void k_decode_partial(DecArgs a) {
+__global__ __launch_bounds__(kDecThreads, 4) void k_decode_partial(DecArgs a) {
   constexpr int LPT = D / 8;            // lanes per cached row
   constexpr int TPW = 64 / LPT;         // rows per wave step
   constexpr int NLG = (kDecThreads / 64) * TPW;
@@ -113,17 +113,34 @@ __global__ __launch_bounds__(kDecThreads, 2) void k_decode_partial(DecArgs a) {
     for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
     __syncthreads();
     uint8_t* hm = reinterpret_cast<uint8_t*>(s_hm);
+    // A head's selected indices are distinct, so at most RANGE of them fall in the
+    // range: SP per thread.  All loads are issued before any membership byte is set.
+    constexpr int SP = RANGE / kDecThreads;
+    int lo[G], hi[G];
 #pragma unroll
     for (int t = 0; t < G; ++t) {
-      const int row = grp * G + t;
-      const int lo = a.starts[int64_t(row) * (a.nsplit + 1) + split];
-      const int hi = a.starts[int64_t(row) * (a.nsplit + 1) + split + 1];
-      const int32_t* sr = a.sel_idx + int64_t(row) * a.n_cap;
-      for (int k = lo + tid; k < hi; k += kDecThreads) {
-        const int p = sr[k] - j0;
-        if (p >= 0 && p < RANGE) hm[t * RANGE + p] = 1;
+      const int64_t so = int64_t(grp * G + t) * (a.nsplit + 1) + split;
+      lo[t] = a.starts[so];
+      hi[t] = a.starts[so + 1];
+    }
+    int pos[G][SP];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int32_t* sr = a.sel_idx + int64_t(grp * G + t) * a.n_cap;
+#pragma unroll
+      for (int u = 0; u < SP; ++u) {
+        // unconditional load (index 0 stands in for out-of-range slots) so that the
+        // compiler keeps every load in flight instead of waiting inside a branch
+        const int k = lo[t] + u * kDecThreads + tid;
+        const int v = sr[k < hi[t] ? k : 0];
+        pos[t][u] = (k < hi[t]) ? v - j0 : -1;
       }
     }
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int u = 0; u < SP; ++u)
+        if (pos[t][u] >= 0 && pos[t][u] < RANGE) hm[t * RANGE + pos[t][u]] = 1;
     __syncthreads();
     // ordered union of the G membership arrays: thread tid owns positions tid*8 .. tid*8+7
     constexpr int PER = RANGE / kDecThreads;
@@ -223,23 +240,37 @@ __global__ __launch_bounds__(kDecThreads, 2) void k_decode_partial(DecArgs a) {
     }
   };
 
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-  for (int base = 0; base < U; base += 2 * NLG) {
-    const int e0 = base + lg, e1 = base + NLG + lg;
-    uint32_t mk0 = 0, mk1 = 0;
-    uint4 k0 = z4, v0 = z4, k1 = z4, v1 = z4;
-    if (e0 < U) {
-      const int64_t j = token_of(e0, mk0);
-      k0 = *reinterpret_cast<const uint4*>(kb + j * D);
-      v0 = *reinterpret_cast<const uint4*>(vb + j * D);
+  // Software pipeline: kDecUnroll rows per lane group per stage, two register stages.
+  // The loads of the next stage are issued before the current one is consumed, so
+  // every wave keeps K/V loads in flight.  Loads are unconditional (list position
+  // clamped to U-1; out-of-range rows get an empty head mask) so that none of them
+  // waits inside a branch.
+  constexpr int STEP = kDecUnroll * NLG;
+  auto load_stage = [&](int base, uint4 (&kk)[kDecUnroll], uint4 (&vv)[kDecUnroll], uint32_t (&mk)[kDecUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int e = base + u * NLG + lg;
+      uint32_t msk;
+      const int64_t j = token_of(e < U ? e : U - 1, msk);
+      mk[u] = e < U ? msk : 0u;
+      kk[u] = *reinterpret_cast<const uint4*>(kb + j * D);
+      vv[u] = *reinterpret_cast<const uint4*>(vb + j * D);
     }
-    if (e1 < U) {
-      const int64_t j = token_of(e1, mk1);
-      k1 = *reinterpret_cast<const uint4*>(kb + j * D);
-      v1 = *reinterpret_cast<const uint4*>(vb + j * D);
+  };
+  if (U > 0) {
+    uint4 ka[kDecUnroll], va[kDecUnroll], kb2[kDecUnroll], vb2[kDecUnroll];
+    uint32_t ma[kDecUnroll], mb[kDecUnroll];
+    load_stage(0, ka, va, ma);
+    for (int base = 0; base < U; base += 2 * STEP) {
+      const bool more_b = base + STEP < U;
+      if (more_b) load_stage(base + STEP, kb2, vb2, mb);
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) consume(ka[u], va[u], ma[u]);
+      if (!more_b) break;
+      if (base + 2 * STEP < U) load_stage(base + 2 * STEP, ka, va, ma);
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) consume(kb2[u], vb2[u], mb[u]);
     }
-    consume(k0, v0, mk0);
-    consume(k1, v1, mk1);
   }
 
   // ---- merge the lane groups of each wave, then the waves
@@ -310,25 +341,49 @@ __global__ __launch_bounds__(256) void k_range_starts(const int32_t* __restrict_
 }
 
 // Combine the per-slice partials of one (batch, head) row into the bf16 output.
+// 256 threads per row: SG = 256/D split groups, each thread sums the splits of its group
+// for one output dimension (independent loads, unrolled), then the groups are combined.
 template <int D>
-__global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ part, int nsplit, int G, int Hq,
-                                                    HeadMap map, uint16_t* __restrict__ out) {
-  const int row = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(256) void k_decode_merge(const float* __restrict__ part, int nsplit, int G, int Hq,
+                                                      HeadMap map, uint16_t* __restrict__ out) {
+  constexpr int SG = 256 / D;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int d = tid % D, sg = tid / D;
   const int grp = row / G, t = row % G;
   const int b = grp / map.n, rr = grp % map.n;
   const int h = map.kv[rr] * G + t;
   const float* pr = part + int64_t(row) * nsplit * (D + 2);
+  __shared__ float s_red[4];
+  __shared__ float s_a[SG][D], s_l[SG][D];
+  // reference max over the splits
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
+  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, pr[int64_t(s) * (D + 2) + D]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   float A = 0.0f, Lsum = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = pr[s * (D + 2) + D];
-    if (ms == -INFINITY) continue;
-    const float f = fast_exp2(ms - M);
-    A = fmaf(pr[s * (D + 2) + d], f, A);
-    Lsum = fmaf(pr[s * (D + 2) + D + 1], f, Lsum);
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = sg; s < nsplit; s += SG) {
+      const float* ps = pr + int64_t(s) * (D + 2);
+      const float ms = ps[D];
+      const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
+      A = fmaf(ps[d], f, A);
+      Lsum = fmaf(ps[D + 1], f, Lsum);
+    }
   }
-  out[(int64_t(b) * Hq + h) * D + d] = f32_to_bf16(Lsum > 0.0f ? A / Lsum : 0.0f);
+  s_a[sg][d] = A;
+  s_l[sg][d] = Lsum;
+  __syncthreads();
+  if (sg == 0) {
+#pragma unroll
+    for (int i = 1; i < SG; ++i) {
+      A += s_a[i][d];
+      Lsum += s_l[i][d];
+    }
+    out[(int64_t(b) * Hq + h) * D + d] = f32_to_bf16(Lsum > 0.0f ? A / Lsum : 0.0f);
+  }
 }
 
 template <int D, int G, bool SPARSE>
@@ -349,9 +404,9 @@ rtp_status dispatch_partial(const Layer& L, dim3 grid, hipStream_t s, const DecA
 rtp_status launch_merge(const Layer& L, int rows, int nsplit, const HeadMap& map, const float* part,
                         uint16_t* out, hipStream_t s) {
   if (L.D == 128)
-    hipLaunchKernelGGL(k_decode_merge<128>, dim3(rows), dim3(128), 0, s, part, nsplit, L.G, L.Hq, map, out);
+    hipLaunchKernelGGL(k_decode_merge<128>, dim3(rows), dim3(256), 0, s, part, nsplit, L.G, L.Hq, map, out);
   else
-    hipLaunchKernelGGL(k_decode_merge<64>, dim3(rows), dim3(64), 0, s, part, nsplit, L.G, L.Hq, map, out);
+    hipLaunchKernelGGL(k_decode_merge<64>, dim3(rows), dim3(256), 0, s, part, nsplit, L.G, L.Hq, map, out);
   return check_launch("k_decode_merge");
 }
 

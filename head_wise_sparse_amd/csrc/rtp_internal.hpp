@@ -53,29 +53,61 @@ size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
 
 // Top-p selection.
 constexpr int kSelThreads = 256;
-constexpr int kSelItems = 8;
+constexpr int kSelItems = 16;
 constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per block
 constexpr int kBins = 2048;                                     // 11-bit digits (last level 10 bits)
-struct SelRowState {             // one per score row, lives in the workspace
-  uint64_t target;               // mass the set must reach (fixed point)
-  uint64_t above;                // mass of tokens strictly above the current prefix
+struct SelLevelState {           // what is known after resolving one level's digit
   uint32_t prefix;               // key bits resolved so far
-  uint32_t cnt_above;            // tokens strictly above the current prefix
-  uint32_t done[3];              // blocks finished per histogram level
-  uint32_t take_ties;            // tokens to take among those tied at the threshold
-  uint32_t pad[6];
+  uint32_t cnt_above;            // tokens strictly above the prefix
+  uint64_t above;                // their mass (fixed point)
+  uint64_t target;               // mass the set must reach (fixed point)
 };
-static_assert(sizeof(SelRowState) == 64, "row state is one 64-byte line");
+struct SelRowState {             // one per score row, lives in the workspace
+  float ref_max;                 // the row max every fixed-point weight is taken against
+  uint32_t pad;
+  SelLevelState lvl[2];          // after level 0, after level 1 (written by different launches)
+};
+static_assert(sizeof(SelRowState) == 56, "row state layout");
 struct SelLayout {
-  size_t hist_mass, hist_cnt, state, lookback, tile_ctr, total;
+  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, tile_ctr, lookback, total;
   int nblk;
 };
 SelLayout sel_layout(const Layer& L, int64_t n_ctx);
+struct SelRows {                 // device views of the selection workspace
+  uint64_t* mass;                // [rows][3][kBins]
+  uint32_t* cnt;                 // [rows][3][kBins]
+  uint64_t* cmass;               // [rows][3][64]   coarse summaries (32 fine bins each)
+  uint32_t* ccnt;                // [rows][3][64]
+  SelRowState* state;            // [rows]
+  uint64_t* lookback;            // [rows][nblk]
+  uint32_t* tile_ctr;            // [rows]
+};
+struct SelArgs {
+  const float* scores;           // [rows][n_cap]
+  const float* row_max_in;       // [rows] (standalone selection) or null
+  const float2* score_part;      // [rows][score_nblk] (fused step: max/sum partials) or null
+  int score_nblk;
+  float* row_max_out;            // fused step: row statistics written by the first pass
+  float* row_sum_out;
+  float top_p;
+  int n_ctx;
+  int64_t n_cap;
+  int nblk;                      // selection tiles per row
+  int32_t* sel_idx;
+  int32_t* sel_count;
+  int32_t* starts;               // fused step: [rows][nsplit + 1] decode range starts, or null
+  int nsplit;
+  SelRows R;
+};
+SelRows sel_rows(void* ws, const SelLayout& lay);
+rtp_status launch_sel_zero(void* ws, size_t bytes, hipStream_t s);
+rtp_status launch_select_chain(const SelArgs& a, int rows, hipStream_t s);
 
 // Decode attention (sparse and window share the layout).
 constexpr int kDecThreads = 256;
-constexpr int kDecRange = 2048;          // token-index range per block (sparse path)
-constexpr int kWinRange = 256;           // list positions per block (window path)
+constexpr int kDecRange = 1024;          // token-index range per block (sparse path)
+constexpr int kWinRange = 128;           // list positions per block (window path)
+constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows][nsplit+1] after partials
 

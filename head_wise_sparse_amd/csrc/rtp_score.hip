@@ -28,23 +28,66 @@ __global__ __launch_bounds__(kScoreThreads) void k_indexer_score(
   const int b = grp / map.n, r = grp % map.n;
   const int g = map.kv[r];
 
-  __shared__ float s_q[G][D];
+  // LDS: raw bf16 q_pre rows and projection matrices of the group (padded so that every
+  // lane of a direct-to-LDS load has a slot), the fp32 q_idx vectors, reduction scratch
+  constexpr int QV = G * D / 8;                           // 16-byte pieces of q_pre
+  constexpr int WV = G * D * kIdxDim / 8;                 // 16-byte pieces of the G matrices
+  constexpr int QV_PAD = QV < 64 ? 64 : QV;
+  constexpr int WPT = (WV + kScoreThreads - 1) / kScoreThreads;
+  __shared__ uint4 s_qraw[QV_PAD];
+  __shared__ uint4 s_w[WPT * kScoreThreads];
   __shared__ float s_qidx[G][kIdxDim];
   __shared__ float s_red[kScoreThreads / 64][G];
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  typedef __attribute__((address_space(1))) const void* glb_ptr_t;
+  const int wave = tid / 64, lane = tid % 64;
+
+  // ---- every global load of the block is issued up front.  q_pre and W_q_idx go
+  // straight to LDS (global_load_lds_dwordx4: no registers, lane i writes 16 bytes at
+  // the wave's LDS base + 16*i); indices are clamped in range so every lane loads.
+  if (wave * 64 < QV_PAD) {
+    const int pidx = min(wave * 64 + lane, QV - 1);
+    const uint16_t* src = q_pre + (int64_t(b) * Hq + g * G + pidx / (D / 8)) * D + (pidx % (D / 8)) * 8;
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(s_qraw + wave * 64), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int pidx = min(i * kScoreThreads + tid, WV - 1);
+    const int t = pidx / (D * kIdxDim / 8), off = pidx % (D * kIdxDim / 8);
+    const uint16_t* src = w_q + int64_t(r * G + t) * w_stride + off * 8;
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(s_w + i * kScoreThreads + wave * 64), 16, 0, 0);
+  }
+  // this tile's keys: thread tid takes tokens base + it*256 + tid (coalesced 32-byte rows)
+  const int64_t base = int64_t(blk) * kScoreTile;
+  const uint4* kp = reinterpret_cast<const uint4*>(k_idx + int64_t(grp) * n_cap * kIdxDim);
+  uint4 kr[kScoreItems][2];
+#pragma unroll
+  for (int it = 0; it < kScoreItems; ++it) {
+    int64_t j = base + it * kScoreThreads + tid;
+    j = j < n_ctx ? j : n_ctx - 1;
+    kr[it][0] = kp[2 * j];
+    kr[it][1] = kp[2 * j + 1];
+  }
+  // wait for the LDS-direct loads only: vmcnt retires in issue order, so leaving the
+  // 2*kScoreItems key loads outstanding is vmcnt(2*kScoreItems)
+  static_assert(2 * kScoreItems < 64, "vmcnt field");
+  constexpr int NK = 2 * kScoreItems;
+  __builtin_amdgcn_s_waitcnt((NK & 0xF) | ((NK >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_s_barrier();   // a bare barrier: __syncthreads' fence would wait for the key loads too
 
   // ---- q_idx = q_pre . W_q_idx for the G heads of this group (fp32, not rounded)
-  for (int i = tid; i < G * D; i += kScoreThreads) {
-    const int t = i / D, d = i % D;
-    s_q[t][d] = bf16_to_f32(q_pre[(int64_t(b) * Hq + g * G + t) * D + d]);
-  }
-  __syncthreads();
   {
     constexpr int P = kScoreThreads / (G * kIdxDim);     // threads per output
     const int o = tid / P, pi = tid % P;
     const int t = o / kIdxDim, c = o % kIdxDim;
-    const uint16_t* w = w_q + int64_t(r * G + t) * w_stride;
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(s_w) + t * D * kIdxDim;
+    const uint16_t* qr = reinterpret_cast<const uint16_t*>(s_qraw) + t * D;
     float acc = 0.0f;
-    for (int d = pi; d < D; d += P) acc = fmaf(s_q[t][d], bf16_to_f32(w[d * kIdxDim + c]), acc);
+#pragma unroll
+    for (int i = 0; i < D / P; ++i) {
+      const int d = pi + i * P;
+      acc = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(w[d * kIdxDim + c]), acc);
+    }
 #pragma unroll
     for (int off = P / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (pi == 0) s_qidx[t][c] = acc * idx_scale;
@@ -56,18 +99,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_indexer_score(
 #pragma unroll
     for (int c = 0; c < kIdxDim; ++c) qi[t][c] = s_qidx[t][c];
 
-  // ---- score the tile: each thread takes tokens base + it*256 + tid (coalesced 32-byte rows)
-  const int64_t base = int64_t(blk) * kScoreTile;
-  const uint4* kp = reinterpret_cast<const uint4*>(k_idx + int64_t(grp) * n_cap * kIdxDim);
-  uint4 kr[kScoreItems][2];
-#pragma unroll
-  for (int it = 0; it < kScoreItems; ++it) {
-    const int64_t j = base + it * kScoreThreads + tid;
-    if (j < n_ctx) {
-      kr[it][0] = kp[2 * j];
-      kr[it][1] = kp[2 * j + 1];
-    }
-  }
+  // ---- score the tile (keys were loaded before the q_idx prologue)
   float sc[kScoreItems][G];
 #pragma unroll
   for (int it = 0; it < kScoreItems; ++it) {
@@ -91,7 +123,6 @@ __global__ __launch_bounds__(kScoreThreads) void k_indexer_score(
   }
 
   // ---- per-block max and sum of exp for each of the G rows
-  const int wave = tid / 64, lane = tid % 64;
   float mt[G];
 #pragma unroll
   for (int t = 0; t < G; ++t) {
@@ -166,9 +197,11 @@ extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ct
   if (L.n_ret == 0) return ok();
   if (!q_pre || !w_q_idx || !k_idx || !scores || !row_max || !row_sum)
     return fail(RTP_EINVAL, "rtp_indexer_score: NULL tensor pointer");
-  if (w_head_stride < 0) return fail(RTP_EINVAL, "w_head_stride must be >= 0");
+  if (w_head_stride < 0 || w_head_stride % 8 != 0)
+    return fail(RTP_EINVAL, "w_head_stride must be a non-negative multiple of 8 (got %lld)",
+                (long long)w_head_stride);
   if (!std::isfinite(idx_scale)) return fail(RTP_EINVAL, "idx_scale must be finite");
-  if (!aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(q_pre, 16) || !aligned(w_q_idx, 2))
+  if (!aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(q_pre, 16) || !aligned(w_q_idx, 16))
     return fail(RTP_EINVAL, "rtp_indexer_score: tensors must be 16-byte aligned");
   const size_t need = score_ws_bytes(L, n_ctx);
   if (!ws || ws_bytes < need || !aligned(ws, 256))

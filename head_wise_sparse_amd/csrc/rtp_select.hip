@@ -4,19 +4,26 @@
 //
 // For one score row, rank tokens by score (higher first, equal scores by lower
 // index) and keep the shortest prefix of the ranking whose softmax mass reaches p.
-// The prefix is exactly {key(s_j) > t} plus the first r tokens (by index) with
-// key(s_j) == t, where key() is the order-preserving uint32 image of the fp32
-// score, t the threshold key and r a tie count.  The search runs in O(N):
+// That prefix is exactly {key(s_j) > t} plus the first r tokens (by index) with
+// key(s_j) == t, where key() is the order-preserving uint32 image of the fp32 score,
+// t the threshold key and r a tie count.  The search is O(N) and takes four launches:
 //
-//   level 0..2  radix histograms on key bits [31:21], [20:10], [9:0].  Each bin
-//               carries the token count and the softmax mass in 2^-42 fixed point
-//               (u64, so the sums are exact and independent of summation order).
-//               Tokens outside the prefix resolved so far are skipped.  The last
-//               block of each level (atomic ticket) scans the row's histogram from
-//               the top and resolves the next digit.
-//   compaction  every tile counts its "above" and "tied" tokens, gets the counts of
-//               all earlier tiles through a decoupled look-back chain, and writes
-//               its selected indices in increasing order.
+//   hist<0>   histogram of key bits [31:21] over the whole row.  Each bin carries the
+//             token count and the softmax mass exp(s - max) in 2^-42 fixed point (u64:
+//             exact sums, independent of order, bit-reproducible).  Bins are built in
+//             LDS per block and added to the row's histogram with global atomics, with a
+//             64-bin coarse summary (32 fine bins each) beside it.
+//   hist<1,2> the same on key bits [20:10] and [9:0], only for tokens whose higher
+//             bits equal the digits resolved so far.  Before that, one wave of every
+//             block resolves the previous level's digit from the coarse summary, then
+//             from the 32 fine bins under the chosen coarse bin (two small reads): the
+//             digit is where the mass accumulated from the top first reaches what is
+//             still needed.  The kernel boundary is the only synchronisation.
+//   compact   resolves the last digit (t is now the full key), the tie count r in
+//             closed form (tied tokens carry equal weight), and writes the selected
+//             indices in increasing order: each tile counts its above / tied tokens and
+//             learns the counts of all earlier tiles through a decoupled look-back
+//             (relaxed atomics on 64-bit status words that carry the counts themselves).
 #include <cmath>
 
 #include "rtp_internal.hpp"
@@ -28,12 +35,11 @@ namespace {
 
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
+constexpr int kCoarse = 64;          // coarse bins of levels 0/1 (32 at level 2)
+constexpr int kFinePer = 32;         // fine bins under one coarse bin
 
-__device__ __forceinline__ uint64_t ld_acq(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_rel(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_rlx(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_rlx(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -42,222 +48,249 @@ __device__ __forceinline__ uint32_t ld_rlx(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-struct SelPtrs {
-  uint64_t* mass;        // [rows][3][kBins]
-  uint32_t* cnt;         // [rows][3][kBins]
-  SelRowState* state;    // [rows]
-  uint64_t* lookback;    // [rows][nblk]
-  uint32_t* tile_ctr;    // [1]
-};
+template <typename T>
+__device__ __forceinline__ T wave_suffix_incl(T v, int lane) {      // sum over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_down(v, o, 64);
+    if (lane + o < 64) v += y;
+  }
+  return v;
+}
 
-__device__ __forceinline__ int level_shift(int level) { return level == 0 ? 21 : (level == 1 ? 10 : 0); }
 __device__ __forceinline__ int level_bins(int level) { return level == 2 ? 1024 : 2048; }
 
-// Zero every histogram, row state, look-back word and the tile counter.
+struct Resolved {            // result of resolving one level's digit
+  uint32_t prefix;           // digits resolved so far
+  uint64_t above;            // mass strictly above the prefix
+  uint32_t cnt_above;        // tokens strictly above the prefix
+  uint64_t target;           // mass the set must reach
+  uint32_t tied;             // count in the resolved bin (meaningful at level 2)
+};
+
+// Resolve the digit of `level` from the finished histogram of that level.  Called by
+// one full wave; every lane returns the same result.  `in` carries the state after
+// the previous level (ignored for level 0, where the target is ceil(p * Z)).
+__device__ Resolved resolve_level(const SelRows& R, int row, int level, const Resolved& in, float top_p,
+                                  int lane) {
+  const int nc = level == 2 ? 32 : kCoarse;
+  const uint64_t* cm = R.cmass + (int64_t(row) * 3 + level) * kCoarse;
+  const uint32_t* cc = R.ccnt + (int64_t(row) * 3 + level) * kCoarse;
+  const uint64_t m_l = lane < nc ? ld_rlx(cm + lane) : 0ull;
+  const uint32_t c_l = lane < nc ? ld_rlx(cc + lane) : 0u;
+  Resolved o = in;
+  if (level == 0) {
+    const uint64_t z = wave_sum<uint64_t>(m_l);
+    const double tgt = ceil(double(top_p) * double(z));
+    uint64_t t = tgt < 1.0 ? 1ull : (uint64_t)tgt;
+    o.target = t > z ? z : t;
+    o.above = 0;
+    o.cnt_above = 0;
+    o.prefix = 0;
+  }
+  uint64_t need = o.target - o.above;
+  // coarse: S(c) = mass of coarse bins >= c; the owner satisfies S(c+1) < need <= S(c)
+  const uint64_t S = wave_suffix_incl<uint64_t>(m_l, lane);
+  const uint32_t SC = wave_suffix_incl<uint32_t>(c_l, lane);
+  const uint64_t own = __ballot(lane < nc && S >= need && S - m_l < need);
+  const int cs = own ? __ffsll((unsigned long long)own) - 1 : 0;
+  const uint64_t above_c = __shfl(S - m_l, cs, 64);
+  const uint32_t cnt_above_c = __shfl(SC - c_l, cs, 64);
+  need -= above_c;
+  // fine bins under the chosen coarse bin
+  const uint64_t* fm = R.mass + (int64_t(row) * 3 + level) * kBins + cs * kFinePer;
+  const uint32_t* fc = R.cnt + (int64_t(row) * 3 + level) * kBins + cs * kFinePer;
+  const uint64_t fm_l = lane < kFinePer ? ld_rlx(fm + lane) : 0ull;
+  const uint32_t fc_l = lane < kFinePer ? ld_rlx(fc + lane) : 0u;
+  const uint64_t FS = wave_suffix_incl<uint64_t>(fm_l, lane);
+  const uint32_t FSC = wave_suffix_incl<uint32_t>(fc_l, lane);
+  const uint64_t fown = __ballot(lane < kFinePer && FS >= need && FS - fm_l < need);
+  const int fs = fown ? __ffsll((unsigned long long)fown) - 1 : 0;
+  const uint32_t digit = uint32_t(cs * kFinePer + fs);
+  o.above += above_c + __shfl(FS - fm_l, fs, 64);
+  o.cnt_above += cnt_above_c + __shfl(FSC - fc_l, fs, 64);
+  o.tied = __shfl(fc_l, fs, 64);
+  o.prefix = level == 0 ? digit : ((o.prefix << (level == 1 ? 11 : 10)) | digit);
+  return o;
+}
+
+// Zero the selection workspace (histograms, summaries, states, counters, look-back).
 __global__ __launch_bounds__(256) void k_sel_zero(uint4* __restrict__ p, size_t n16) {
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256) p[i] = z;
 }
 
-// Suffix scan of one histogram level by a whole block; resolves the digit where the
-// cumulative mass from the top first reaches what is still needed.
-__device__ void scan_level(const SelPtrs& P, int row, int level, float top_p, float row_m,
-                           int32_t* __restrict__ sel_count) {
-  const int tid = threadIdx.x;
-  const int nb = level_bins(level);
-  const int per = nb / kSelThreads;                    // 8 or 4 bins per thread
-  const uint64_t* hm = P.mass + (int64_t(row) * 3 + level) * kBins;
-  const uint32_t* hc = P.cnt + (int64_t(row) * 3 + level) * kBins;
-  SelRowState* st = P.state + row;
-
-  __shared__ uint64_t s_m[kSelThreads];
-  __shared__ uint32_t s_c[kSelThreads];
-  __shared__ uint64_t s_need, s_target, s_above;
-  __shared__ uint32_t s_prefix, s_cnt_above;
-
-  uint64_t bm[8];
-  uint32_t bc[8];
-  uint64_t tm = 0;
-  uint32_t tc = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bm[i] = (i < per) ? ld_rlx(hm + tid * per + i) : 0ull;
-    bc[i] = (i < per) ? ld_rlx(hc + tid * per + i) : 0u;
-    tm += bm[i];
-    tc += bc[i];
-  }
-  s_m[tid] = tm;
-  s_c[tid] = tc;
+// Row max for level 0: from row_max (standalone call) or from the scoring kernel's
+// per-block (max, sum) partials (fused decode step; block 0 also writes the row stats).
+__device__ float row_reference_max(const SelArgs& a, int row, int tid, float* s_red) {
+  if (!a.score_part) return a.row_max_in[row];
+  const float2* p = a.score_part + int64_t(row) * a.score_nblk;
+  float m = -INFINITY;
+  for (int i = tid; i < a.score_nblk; i += kSelThreads) m = fmaxf(m, p[i].x);
+  m = wave_max(m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
   __syncthreads();
-  if (tid == 0) {
-    uint64_t need;
-    if (level == 0) {
-      uint64_t z = 0;
-      for (int i = 0; i < kSelThreads; ++i) z += s_m[i];
-      double tgt = ceil(double(top_p) * double(z));
-      uint64_t t = tgt < 1.0 ? 1ull : (uint64_t)tgt;
-      if (t > z) t = z;
-      st->target = t;
-      s_target = t;
-      s_above = 0;
-      s_cnt_above = 0;
-      s_prefix = 0;
-      need = t;
-    } else {
-      s_target = st->target;
-      s_above = st->above;
-      s_cnt_above = st->cnt_above;
-      s_prefix = st->prefix;
-      need = s_target - s_above;
-    }
-    s_need = need;
-    // exclusive suffix sums over threads (thread i gets the sum of threads > i)
-    uint64_t am = 0;
-    uint32_t ac = 0;
-    for (int i = kSelThreads - 1; i >= 0; --i) {
-      const uint64_t m = s_m[i];
-      const uint32_t c = s_c[i];
-      s_m[i] = am;
-      s_c[i] = ac;
-      am += m;
-      ac += c;
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  if (blockIdx.x == 0 && a.row_max_out) {
+    float z = 0.0f;
+    for (int i = tid; i < a.score_nblk; i += kSelThreads) z += p[i].y * __expf(p[i].x - m);
+    z = wave_sum(z);
+    __syncthreads();
+    if ((tid & 63) == 0) s_red[tid >> 6] = z;
+    __syncthreads();
+    if (tid == 0) {
+      a.row_max_out[row] = m;
+      a.row_sum_out[row] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
     }
   }
-  __syncthreads();
-  const uint64_t need = s_need;
-  uint64_t suf = s_m[tid];
-  uint32_t sufc = s_c[tid];
-  // The owning thread is the one whose bins straddle `need`: suf < need <= suf + tm.
-  if (suf < need && need <= suf + tm) {
-    int d = 0;            // stays 0 only if the histogram were inconsistent
-    bool found = false;
-    uint32_t tied = bc[0];
-#pragma unroll
-    for (int k = 7; k >= 0; --k) {
-      if (k < per && !found) {
-        if (suf + bm[k] >= need) {
-          found = true;
-          d = k;
-          tied = bc[k];
-        } else {
-          suf += bm[k];
-          sufc += bc[k];
-        }
-      }
-    }
-    const uint32_t digit = uint32_t(tid * per + d);
-    const uint32_t prefix = (level == 0) ? digit : ((s_prefix << (level == 1 ? 11 : 10)) | digit);
-    const uint64_t above = s_above + suf;
-    const uint32_t cnt_above = s_cnt_above + sufc;
-    st->prefix = prefix;
-    st->above = above;
-    st->cnt_above = cnt_above;
-    if (level == 2) {
-      // prefix is now the full threshold key; tied tokens share one weight
-      const uint64_t w = fixed_weight(key_score(prefix), row_m);
-      const uint64_t rem = s_target - above;
-      uint64_t r = (w == 0) ? tied : (rem + w - 1) / w;
-      if (r < 1) r = 1;
-      if (r > tied) r = tied;
-      st->take_ties = uint32_t(r);
-      sel_count[row] = int32_t(cnt_above + uint32_t(r));
-    }
-  }
+  return m;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_sel_hist(const float* __restrict__ scores,
-                                                          const float* __restrict__ row_max, SelPtrs P,
-                                                          int level, int n_ctx, int64_t n_cap, int nblk,
-                                                          float top_p, int32_t* __restrict__ sel_count) {
-  const int tid = threadIdx.x;
+template <int LEVEL>
+__global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
+  constexpr int NB = LEVEL == 2 ? 1024 : 2048;
+  constexpr int SHIFT = LEVEL == 0 ? 21 : (LEVEL == 1 ? 10 : 0);
+  constexpr int PSHIFT = LEVEL == 1 ? 21 : 10;                     // prefix bits start (levels 1, 2)
+  const int tid = threadIdx.x, lane = tid & 63;
   const int blk = blockIdx.x, row = blockIdx.y;
-  __shared__ uint64_t h_m[kBins];
-  __shared__ uint32_t h_c[kBins];
-  __shared__ int s_last;
-  const int nb = level_bins(level);
-  for (int i = tid; i < nb; i += kSelThreads) {
-    h_m[i] = 0;
-    h_c[i] = 0;
-  }
-  const float m = row_max[row];
-  const uint32_t prefix = level == 0 ? 0u : P.state[row].prefix;
-  const int shift = level_shift(level);
-  const int pshift = level == 0 ? 32 : (level == 1 ? 21 : 10);
-  const uint32_t dmask = uint32_t(nb - 1);
-  __syncthreads();
+  __shared__ uint64_t h_m[NB];
+  __shared__ uint32_t h_c[NB];
+  __shared__ float s_red[4];
+  __shared__ uint32_t s_prefix;
 
-  const float* sp = scores + int64_t(row) * n_cap;
+  // scores of the tile: unconditional loads (index clamped), validity kept aside
+  const float* sp = a.scores + int64_t(row) * a.n_cap;
   const int64_t base = int64_t(blk) * kSelTile;
   float sv[kSelItems];
 #pragma unroll
   for (int it = 0; it < kSelItems; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
-    sv[it] = (j < n_ctx) ? sp[j] : 0.0f;
+    sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
   }
-#pragma unroll
-  for (int it = 0; it < kSelItems; ++it) {
-    const int64_t j = base + it * kSelThreads + tid;
-    if (j < n_ctx) {
-      const uint32_t key = score_key(sv[it]);
-      const bool match = (level == 0) || ((key >> pshift) == prefix);
-      if (match) {
-        const uint32_t d = (key >> shift) & dmask;
-        atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m));
-        atomicAdd(&h_c[d], 1u);
+  for (int i = tid; i < NB; i += kSelThreads) {
+    h_m[i] = 0;
+    h_c[i] = 0;
+  }
+  float m;
+  if constexpr (LEVEL == 0) {
+    m = row_reference_max(a, row, tid, s_red);
+    if (blk == 0 && tid == 0) a.R.state[row].ref_max = m;
+  } else {
+    m = a.R.state[row].ref_max;                      // written by the level-0 launch
+  }
+  if (LEVEL > 0 && tid < 64) {
+    Resolved in{};
+    if (LEVEL == 2) {
+      const SelLevelState& ls = a.R.state[row].lvl[0];
+      in.prefix = ls.prefix;
+      in.above = ls.above;
+      in.cnt_above = ls.cnt_above;
+      in.target = ls.target;
+    }
+    const Resolved o = resolve_level(a.R, row, LEVEL - 1, in, a.top_p, lane);
+    if (lane == 0) {
+      s_prefix = o.prefix;
+      if (blk == 0) {          // one block publishes; this launch's blocks read only lvl[LEVEL-2]
+        SelLevelState& ls = a.R.state[row].lvl[LEVEL - 1];
+        ls.prefix = o.prefix;
+        ls.above = o.above;
+        ls.cnt_above = o.cnt_above;
+        ls.target = o.target;
       }
     }
   }
   __syncthreads();
-  uint64_t* gm = P.mass + (int64_t(row) * 3 + level) * kBins;
-  uint32_t* gc = P.cnt + (int64_t(row) * 3 + level) * kBins;
-  for (int i = tid; i < nb; i += kSelThreads) {
+  const uint32_t prefix = LEVEL > 0 ? s_prefix : 0u;
+#pragma unroll
+  for (int it = 0; it < kSelItems; ++it) {
+    const int64_t j = base + it * kSelThreads + tid;
+    const uint32_t key = score_key(sv[it]);
+    const bool match = (j < a.n_ctx) && (LEVEL == 0 || (key >> PSHIFT) == prefix);
+    if (match) {
+      const uint32_t d = (key >> SHIFT) & uint32_t(NB - 1);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m));
+      atomicAdd(&h_c[d], 1u);
+    }
+  }
+  __syncthreads();
+  uint64_t* gm = a.R.mass + (int64_t(row) * 3 + LEVEL) * kBins;
+  uint32_t* gc = a.R.cnt + (int64_t(row) * 3 + LEVEL) * kBins;
+  for (int i = tid; i < NB; i += kSelThreads) {
     if (h_c[i]) {
       atomicAdd(reinterpret_cast<unsigned long long*>(gm + i), (unsigned long long)h_m[i]);
       atomicAdd(gc + i, h_c[i]);
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&P.state[row].done[level], 1u);
-    s_last = (old == uint32_t(nblk - 1));
-  }
-  __syncthreads();
-  if (s_last) {
-    __threadfence();
-    scan_level(P, row, level, top_p, m, sel_count);
+  // coarse summary: thread c < NB/32 sums its 32 fine bins
+  if (tid < NB / kFinePer) {
+    uint64_t sm = 0;
+    uint32_t sc = 0;
+#pragma unroll 8
+    for (int i = 0; i < kFinePer; ++i) {
+      sm += h_m[tid * kFinePer + i];
+      sc += h_c[tid * kFinePer + i];
+    }
+    if (sc) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.R.cmass + (int64_t(row) * 3 + LEVEL) * kCoarse + tid),
+                (unsigned long long)sm);
+      atomicAdd(a.R.ccnt + (int64_t(row) * 3 + LEVEL) * kCoarse + tid, sc);
+    }
   }
 }
 
-// Ordered compaction of {key > t} U {first r tokens with key == t}.
-__global__ __launch_bounds__(kSelThreads) void k_sel_compact(const float* __restrict__ scores, SelPtrs P,
-                                                             int n_ctx, int64_t n_cap, int nblk,
-                                                             int32_t* __restrict__ sel_idx) {
+// Resolve the last digit, then write {key > t} U {first r with key == t} in order.
+__global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  __shared__ uint32_t s_id;
-  __shared__ uint32_t s_wa[kSelItems][kSelThreads / 64], s_we[kSelItems][kSelThreads / 64];
+  const int row = blockIdx.y;
+  constexpr int NW = kSelThreads / 64;
+  __shared__ uint32_t s_tile, s_t, s_r;
+  __shared__ uint32_t s_wa[kSelItems][NW], s_we[kSelItems][NW];
   __shared__ uint32_t s_pa, s_pe;
-  if (tid == 0) s_id = atomicAdd(P.tile_ctr, 1u);
+  if (tid == 0) s_tile = atomicAdd(a.R.tile_ctr + row, 1u);     // dynamic tile id: predecessors started
   __syncthreads();
-  const uint32_t id = s_id;
-  const int row = int(id / uint32_t(nblk)), tile = int(id % uint32_t(nblk));
-  const uint32_t t = P.state[row].prefix;
-  const uint32_t r = P.state[row].take_ties;
-
-  const float* sp = scores + int64_t(row) * n_cap;
+  const int tile = int(s_tile);
+  const float* sp = a.scores + int64_t(row) * a.n_cap;
   const int64_t base = int64_t(tile) * kSelTile;
-  bool fa[kSelItems], fe[kSelItems];
+  float sv[kSelItems];
 #pragma unroll
   for (int it = 0; it < kSelItems; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
-    const float s = (j < n_ctx) ? sp[j] : 0.0f;
-    const uint32_t key = score_key(s);
-    fa[it] = (j < n_ctx) && key > t;
-    fe[it] = (j < n_ctx) && key == t;
+    sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
   }
+  if (wave == 0) {
+    const SelLevelState& ls = a.R.state[row].lvl[1];
+    Resolved in{};
+    in.prefix = ls.prefix;
+    in.above = ls.above;
+    in.cnt_above = ls.cnt_above;
+    in.target = ls.target;
+    const Resolved o = resolve_level(a.R, row, 2, in, a.top_p, lane);
+    if (lane == 0) {
+      // tied tokens share one weight: take just enough of them to reach the target
+      s_t = o.prefix;
+      const uint64_t w = fixed_weight(key_score(o.prefix), a.R.state[row].ref_max);
+      const uint64_t rem = o.target - o.above;
+      uint64_t r = (w == 0) ? o.tied : (rem + w - 1) / w;
+      if (r < 1) r = 1;
+      if (r > o.tied) r = o.tied;
+      s_r = uint32_t(r);
+      if (tile == 0) {
+        const uint32_t cnt = o.cnt_above + uint32_t(r);
+        a.sel_count[row] = int32_t(cnt);
+        if (a.starts) a.starts[int64_t(row) * (a.nsplit + 1) + a.nsplit] = int32_t(cnt);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t t = s_t, r = s_r;
+  bool fa[kSelItems], fe[kSelItems];
   uint64_t ba[kSelItems], be[kSelItems];
 #pragma unroll
   for (int it = 0; it < kSelItems; ++it) {
+    const int64_t j = base + it * kSelThreads + tid;
+    const uint32_t key = score_key(sv[it]);
+    fa[it] = (j < a.n_ctx) && key > t;
+    fe[it] = (j < a.n_ctx) && key == t;
     ba[it] = __ballot(fa[it]);
     be[it] = __ballot(fe[it]);
     if (lane == 0) {
@@ -266,43 +299,58 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(const float* __rest
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t a = 0, e = 0;
+  // decoupled look-back, one wave wide
+  if (wave == 0) {
+    uint32_t a_ = 0, e_ = 0;
     for (int it = 0; it < kSelItems; ++it)
-      for (int w = 0; w < kSelThreads / 64; ++w) {
-        a += s_wa[it][w];
-        e += s_we[it][w];
+      for (int w = 0; w < NW; ++w) {
+        a_ += s_wa[it][w];
+        e_ += s_we[it][w];
       }
-    uint64_t* lb = P.lookback + int64_t(row) * nblk;
+    uint64_t* lb = a.R.lookback + int64_t(row) * a.nblk;
     uint64_t pa = 0, pe = 0;
     if (tile == 0) {
-      st_rel(lb, kFlagIncl | (uint64_t(a) << 31) | e);
+      if (lane == 0) st_rlx(lb, kFlagIncl | (uint64_t(a_) << 31) | e_);
     } else {
-      st_rel(lb + tile, kFlagAgg | (uint64_t(a) << 31) | e);
-      int k = tile - 1;
+      if (lane == 0) st_rlx(lb + tile, kFlagAgg | (uint64_t(a_) << 31) | e_);
+      int k = tile - 1;                       // lanes inspect tiles k, k-1, ..., k-63
       while (true) {
-        const uint64_t v = ld_acq(lb + k);
+        const int idx = k - lane;
+        const uint64_t v = (idx >= 0) ? ld_rlx(lb + idx) : kFlagIncl;
         const uint64_t f = v >> 62;
-        if (f == 0) {
+        const uint64_t incl = __ballot(f == 2);
+        const uint64_t none = __ballot(f == 0);
+        const int first = incl ? __ffsll((unsigned long long)incl) - 1 : 64;
+        const uint64_t upto = (first >= 63) ? ~0ull : ((2ull << first) - 1ull);
+        if (none & upto) {                    // a needed predecessor has not published yet
           __builtin_amdgcn_s_sleep(1);
           continue;
         }
-        pa += (v >> 31) & 0x7FFFFFFFull;
-        pe += v & 0x7FFFFFFFull;
-        if (f == 2) break;
-        --k;
+        const bool use = lane <= first;
+        pa += wave_sum<uint64_t>(use ? ((v >> 31) & 0x7FFFFFFFull) : 0ull);
+        pe += wave_sum<uint64_t>(use ? (v & 0x7FFFFFFFull) : 0ull);
+        if (first < 64) break;
+        k -= 64;
       }
-      st_rel(lb + tile, kFlagIncl | ((pa + a) << 31) | (pe + e));
+      if (lane == 0) st_rlx(lb + tile, kFlagIncl | ((pa + a_) << 31) | (pe + e_));
     }
-    s_pa = uint32_t(pa);
-    s_pe = uint32_t(pe);
+    if (lane == 0) {
+      s_pa = uint32_t(pa);
+      s_pe = uint32_t(pe);
+    }
   }
   __syncthreads();
   uint32_t ca = s_pa, ce = s_pe;              // counts of every earlier token
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int32_t* out = sel_idx + int64_t(row) * n_cap;
+  int32_t* out = a.sel_idx + int64_t(row) * a.n_cap;
+  constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
 #pragma unroll
   for (int it = 0; it < kSelItems; ++it) {
+    if (a.starts && it % IT_PER_RANGE == 0 && tid == 0) {
+      // first token of a decode range: the number of selected tokens before it
+      const int64_t q = (base + it * kSelThreads) / kDecRange;
+      if (q < a.nsplit) a.starts[int64_t(row) * (a.nsplit + 1) + q] = int32_t(ca + (ce < r ? ce : r));
+    }
     uint32_t wa = 0, we = 0;
     for (int w = 0; w < wave; ++w) {
       wa += s_wa[it][w];
@@ -311,11 +359,8 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(const float* __rest
     const uint32_t a_before = ca + wa + __popcll(ba[it] & lt);
     const uint32_t e_before = ce + we + __popcll(be[it] & lt);
     const bool take = fa[it] || (fe[it] && e_before < r);
-    if (take) {
-      const uint32_t pos = a_before + (e_before < r ? e_before : r);
-      out[pos] = int32_t(base + it * kSelThreads + tid);
-    }
-    for (int w = 0; w < kSelThreads / 64; ++w) {
+    if (take) out[a_before + (e_before < r ? e_before : r)] = int32_t(base + it * kSelThreads + tid);
+    for (int w = 0; w < NW; ++w) {
       ca += s_wa[it][w];
       ce += s_we[it][w];
     }
@@ -324,14 +369,56 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(const float* __rest
 
 // top_p >= 1: every token, in order.
 __global__ __launch_bounds__(256) void k_sel_all(int n_ctx, int64_t n_cap, int32_t* __restrict__ sel_idx,
-                                                 int32_t* __restrict__ sel_count) {
+                                                 int32_t* __restrict__ sel_count, int32_t* __restrict__ starts,
+                                                 int nsplit) {
   const int row = blockIdx.y;
   const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (j < n_ctx) sel_idx[int64_t(row) * n_cap + j] = int32_t(j);
   if (j == 0) sel_count[row] = n_ctx;
+  if (starts && j <= nsplit) starts[int64_t(row) * (nsplit + 1) + j] = int32_t(j == nsplit ? n_ctx : j * kDecRange);
 }
 
 }  // namespace
+
+namespace rtp {
+
+SelRows sel_rows(void* ws, const SelLayout& lay) {
+  char* w = static_cast<char*>(ws);
+  return SelRows{reinterpret_cast<uint64_t*>(w + lay.hist_mass), reinterpret_cast<uint32_t*>(w + lay.hist_cnt),
+                 reinterpret_cast<uint64_t*>(w + lay.coarse_mass), reinterpret_cast<uint32_t*>(w + lay.coarse_cnt),
+                 reinterpret_cast<SelRowState*>(w + lay.state), reinterpret_cast<uint64_t*>(w + lay.lookback),
+                 reinterpret_cast<uint32_t*>(w + lay.tile_ctr)};
+}
+
+rtp_status launch_sel_zero(void* ws, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const unsigned zb = unsigned(std::min<size_t>((n16 + 255) / 256, 2048));
+  hipLaunchKernelGGL(k_sel_zero, dim3(zb), dim3(256), 0, s, reinterpret_cast<uint4*>(ws), n16);
+  return check_launch("k_sel_zero");
+}
+
+rtp_status launch_select_chain(const SelArgs& a0, int rows, hipStream_t s) {
+  SelArgs a = a0;
+  rtp_status st;
+  if (a.top_p >= 1.0f) {
+    hipLaunchKernelGGL(k_sel_all, dim3(unsigned((a.n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, a.n_ctx,
+                       a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
+    return check_launch("k_sel_all");
+  }
+  const dim3 grid(a.nblk, rows);
+  hipLaunchKernelGGL(k_sel_hist<0>, grid, dim3(kSelThreads), 0, s, a);
+  if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
+  a.score_part = nullptr;                    // later levels read the reference max from the row state
+  a.row_max_in = nullptr;
+  hipLaunchKernelGGL(k_sel_hist<1>, grid, dim3(kSelThreads), 0, s, a);
+  if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
+  hipLaunchKernelGGL(k_sel_hist<2>, grid, dim3(kSelThreads), 0, s, a);
+  if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
+  hipLaunchKernelGGL(k_sel_compact, grid, dim3(kSelThreads), 0, s, a);
+  return check_launch("k_sel_compact");
+}
+
+}  // namespace rtp
 
 extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx, const float* scores,
                                       const float* row_max, const float* row_sum, float top_p, int32_t* sel_idx,
@@ -349,30 +436,22 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
     return fail(RTP_EINVAL, "rtp_topp_select: tensors must be 16-byte aligned");
   const int rows = L.B * L.n_ret * L.G;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (top_p >= 1.0f) {
-    hipLaunchKernelGGL(k_sel_all, dim3(unsigned((n_ctx + 255) / 256), rows), dim3(256), 0, s, int(n_ctx), L.n_cap,
-                       sel_idx, sel_count);
-    return check_launch("k_sel_all");
-  }
   const SelLayout lay = sel_layout(L, n_ctx);
-  if (!ws || ws_bytes < lay.total || !aligned(ws, 256))
+  if (top_p < 1.0f && (!ws || ws_bytes < lay.total || !aligned(ws, 256)))
     return fail(RTP_EWORKSPACE, "rtp_topp_select: workspace needs %zu bytes, 256-aligned (got %zu)", lay.total,
                 ws_bytes);
-  char* w = static_cast<char*>(ws);
-  SelPtrs P{reinterpret_cast<uint64_t*>(w + lay.hist_mass), reinterpret_cast<uint32_t*>(w + lay.hist_cnt),
-            reinterpret_cast<SelRowState*>(w + lay.state), reinterpret_cast<uint64_t*>(w + lay.lookback),
-            reinterpret_cast<uint32_t*>(w + lay.tile_ctr)};
-  const size_t n16 = lay.total / 16;
-  const unsigned zb = unsigned(std::min<size_t>((n16 + 255) / 256, 2048));
-  hipLaunchKernelGGL(k_sel_zero, dim3(zb), dim3(256), 0, s, reinterpret_cast<uint4*>(ws), n16);
-  if ((st = check_launch("k_sel_zero")) != RTP_OK) return st;
-  const dim3 grid(lay.nblk, rows);
-  for (int level = 0; level < 3; ++level) {
-    hipLaunchKernelGGL(k_sel_hist, grid, dim3(kSelThreads), 0, s, scores, row_max, P, level, int(n_ctx), L.n_cap,
-                       lay.nblk, top_p, sel_count);
-    if ((st = check_launch("k_sel_hist")) != RTP_OK) return st;
+  SelArgs a{};
+  a.scores = scores;
+  a.row_max_in = row_max;
+  a.top_p = top_p;
+  a.n_ctx = int(n_ctx);
+  a.n_cap = L.n_cap;
+  a.nblk = lay.nblk;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  if (top_p < 1.0f) {
+    a.R = sel_rows(ws, lay);
+    if ((st = launch_sel_zero(ws, lay.total, s)) != RTP_OK) return st;
   }
-  hipLaunchKernelGGL(k_sel_compact, dim3(unsigned(lay.nblk) * unsigned(rows)), dim3(kSelThreads), 0, s, scores, P,
-                     int(n_ctx), L.n_cap, lay.nblk, sel_idx);
-  return check_launch("k_sel_compact");
+  return launch_select_chain(a, rows, s);
 }

@@ -344,3 +344,28 @@ def test_decode_step_is_deterministic():
     b = [step.scores, step.row_max, step.sel_count, step.sel_idx, out2]
     for u, v in zip(a, b):
         assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph (through torch) reproduces the eager result on
+    every replay, with eager work and synchronisations between replays."""
+    P.require_gpu()
+    torch = _torch()
+    x, d, step, out = _decode_step("decode_b8_32k", 0.95, batch=2, n_ctx=9000)
+    step.sel_idx.fill_(-1)
+    step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (step.sel_count, step.sel_idx, out)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+    for rep in range(4):
+        step.sel_idx.fill_(-1)
+        step.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for u, v in zip(ref, (step.sel_count, step.sel_idx, step.out)):
+            assert torch.equal(u.view(torch.uint8), v.view(torch.uint8)), f"replay {rep}"
+        step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)      # eager work between replays
+        torch.cuda.synchronize()
