@@ -15,13 +15,11 @@
 //  - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K tile from LDS, Q^T held in registers
 //    for the whole loop); the accumulator layout of S^T is exactly the B operand of
 //    O^T = V^T P^T, so P never goes through LDS.
-//  - V^T is staged in LDS: each thread loads 4 keys x 8 dims, transposes them in
-//    registers and writes 8-byte runs; keys are stored in the order the P^T operand
-//    holds them, so every MFMA operand read is one 16-byte ds_read.
 //  - online softmax in the exp2 domain with a lazy reference max (rescale only when
 //    a row max grows by more than 2^8); masks are applied only on boundary tiles.
-//  - K/V tiles are double-buffered in LDS and the next tile's global loads are in
-//    flight while the current tile is computed.
+//  - K/V tiles are double-buffered in LDS; the next tile is copied HBM -> LDS directly
+//    (no registers) while the current tile is computed, and V^T operands are read with
+//    the transposing LDS read (ds_read_b64_tr_b16), so V needs no explicit transpose.
 #include <cmath>
 
 #include "rtp_internal.hpp"
@@ -34,14 +32,45 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int PD = 128;               // head dim
-constexpr int BM = 128;               // query rows per block
+#ifndef RTP_PREFILL_RB
+#define RTP_PREFILL_RB 1
+#endif
+constexpr int RB = RTP_PREFILL_RB;    // 32-row column blocks per wave
+constexpr int BM = 128;               // query rows per block (waves x 32*RB rows)
 constexpr int BN = 64;                // keys per tile
-constexpr int KP = PD + 8;            // K tile row pitch (bf16 elements): 272 bytes
-constexpr int VP = BN + 8;            // V^T tile row pitch (bf16 elements): 144 bytes
-constexpr int kPreThreads = 256;
+// LDS tiles are 64 rows x 128 bf16 (256-byte rows, 16 chunks of 16 bytes), unpadded
+// (direct-to-LDS loads fill 1 KB contiguous runs), with the chunk index XOR-swizzled per
+// row, differently for K and V:
+//  - K is read as MFMA A operands: 16 consecutive rows, one chunk each -> c ^ (r & 15)
+//    puts them in 16 different chunk slots;
+//  - V is read with the transposing read: per wave, rows 4h .. 4h+3 (h = 0, 1) x 4 chunks
+//    -> c ^ 4*(r & 3) spreads each row's 4 chunks over a different quarter of the row.
+constexpr int KP = PD;
+__device__ __forceinline__ int swz_k(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }
+__device__ __forceinline__ int swz_v(int r, int c) { return r * 128 + ((c ^ ((r & 3) << 2)) << 3); }
+
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i writes at the
+// wave-uniform LDS byte address `lds` + 16*i.  Issued from inline asm so that the
+// compiler's wait insertion does not treat it as an LDS store that every later LDS read
+// must wait for (the compiler cannot tell that the two double-buffer halves are
+// disjoint).  The instruction has no destination register; completion is awaited
+// explicitly (vmcnt) before the barrier that publishes the tile.
+__device__ __forceinline__ void g2lds_16(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }   // vmcnt(0)
+
+constexpr int kPreThreads = 64 * (BM / (32 * RB));   // waves x 64 lanes
 
 struct PrefArgs {
   const uint16_t* q;        // [C][Hq][D]
@@ -61,14 +90,14 @@ struct PrefArgs {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// position of key kl (multiple of 4, inside a 64-key tile) in the V^T tile row: within
-// each 16-key group, keys 4h..4h+3 and 8+4h..8+4h+3 sit in slots 8h .. 8h+7
-__device__ __forceinline__ int vt_pos(int kl) {
-  const int q4 = (kl & 15) >> 2;
-  return (kl & ~15) + 8 * (q4 & 1) + 4 * (q4 >> 1);
-}
 
-__global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* glb_ptr_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t* lds_s4;
+
+__global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(PrefArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hf = lane >> 5;
 
@@ -107,171 +136,194 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
   auto tile_of = [&](int n) { return n < n_sink_t ? n : kt_start + (n - n_sink_t); };
 
   __shared__ uint16_t s_k[2][BN * KP];
-  __shared__ uint16_t s_vt[2][PD * VP];
+  __shared__ uint16_t s_v[2][BN * KP];
 
   const uint16_t* kbase = a.k + int64_t(kvh) * a.n_cap * PD;
   const uint16_t* vbase = a.v + int64_t(kvh) * a.n_cap * PD;
 
-  // ---- Q^T operand: lane holds q row (wave*32 + l32), dims 16*ds + 8*hf .. +8
-  const int64_t my_row = R0 + wave * 32 + l32;                 // absolute row of this lane's column
-  const int64_t qrow_c = min<int64_t>(my_row - a.c0, a.C - 1); // chunk-relative, clamped
-  bf16x8_t qop[PD / 16];
+  // ---- Q^T operands: a wave owns 64 rows as two 32-row column blocks; lane holds row
+  // R0 + wave*64 + rb*32 + l32, dims 16*ds + 8*hf .. +8
+  int64_t my_row[RB];
+  bf16x8_t qop[RB][PD / 16];
 #pragma unroll
-  for (int ds = 0; ds < PD / 16; ++ds)
-    qop[ds] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + (qrow_c * a.Hq + qh) * PD + 16 * ds + 8 * hf));
+  for (int rb = 0; rb < RB; ++rb) {
+    my_row[rb] = R0 + wave * (32 * RB) + rb * 32 + l32;
+    const int64_t qrow_c = min<int64_t>(my_row[rb] - a.c0, a.C - 1);   // chunk-relative, clamped
+#pragma unroll
+    for (int ds = 0; ds < PD / 16; ++ds)
+      qop[rb][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + (qrow_c * a.Hq + qh) * PD + 16 * ds + 8 * hf));
+  }
 
-  // ---- tile staging: global -> registers -> LDS
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt) {
+  // ---- tile staging: the next tile's K and V rows go from HBM straight to the other LDS
+  // buffer while the current tile is computed.  Wave w's i-th copy fills physical chunks
+  // (i*NWV + w)*64 .. +63; each lane fetches the global chunk that belongs at its slot.
+  constexpr int KCH = BN * PD / 8;                            // 16-byte chunks per tile
+  constexpr int KLD = KCH / kPreThreads;                      // copies per thread per tile (K and V each)
+  constexpr int NWV = kPreThreads / 64;
+  auto load_tile = [&](int kt, int buf) {
     const int64_t k0 = int64_t(kt) * BN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + kPreThreads * i;
-      const int key = u >> 4, d8 = u & 15;
-      const int64_t kr = min<int64_t>(k0 + key, a.n_cap - 1);
-      kreg[i] = *reinterpret_cast<const uint4*>(kbase + kr * PD + d8 * 8);
-    }
-    const int kg = tid >> 4, d8 = tid & 15;                    // keys 4kg..4kg+3, dims 8*d8..+8
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t kr = min<int64_t>(k0 + 4 * kg + j, a.n_cap - 1);
-      vreg[j] = *reinterpret_cast<const uint4*>(vbase + kr * PD + d8 * 8);
+    for (int i = 0; i < KLD; ++i) {
+      const int base = (i * NWV + wave) * 64;
+      const int p = base + lane;
+      const int row = p >> 4, ck = (p & 15) ^ (row & 15), cv = (p & 15) ^ ((row & 3) << 2);
+      const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
+      g2lds_16(kbase + kr * PD + ck * 8, lds_addr(&s_k[buf][base * 8]));
+      g2lds_16(vbase + kr * PD + cv * 8, lds_addr(&s_v[buf][base * 8]));
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + kPreThreads * i;
-      const int key = u >> 4, d8 = u & 15;
-      *reinterpret_cast<uint4*>(&s_k[buf][key * KP + d8 * 8]) = kreg[i];
-    }
-    const int kg = tid >> 4, d8 = tid & 15;
-    const int pos = vt_pos(4 * kg);
-    auto word = [&](int j, int e2) -> uint32_t {
-      return e2 == 0 ? vreg[j].x : (e2 == 1 ? vreg[j].y : (e2 == 2 ? vreg[j].z : vreg[j].w));
-    };
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {          // dims 8*d8 + 2*e2 (low halves) and +1 (high halves)
-      const uint32_t w0 = word(0, e2), w1 = word(1, e2), w2 = word(2, e2), w3 = word(3, e2);
-      uint2 lo, hi;
-      lo.x = (w0 & 0xFFFFu) | (w1 << 16);
-      lo.y = (w2 & 0xFFFFu) | (w3 << 16);
-      hi.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
-      hi.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(&s_vt[buf][(d8 * 8 + 2 * e2) * VP + pos]) = lo;
-      *reinterpret_cast<uint2*>(&s_vt[buf][(d8 * 8 + 2 * e2 + 1) * VP + pos]) = hi;
-    }
+  // V^T operand addresses.  ds_read_b64_tr_b16: within each 16-lane group, lane r names a
+  // row of 4 bf16 and lane 4j+i receives element i of the rows named by lanes j, j+4, j+8,
+  // j+12.  Lane r names V[key0 + r/4][d0 + 4*(r%4)], so lane l receives dims d0 + l%16 of
+  // keys key0 .. key0+3: a slice of the V^T operand.  For the (32-dim block db, 16-key step
+  // ks) operand, lane l's 8 elements are the keys 16*ks + 8*(e/4) + 4*(l/32) + e%4 (the key
+  // order of the P^T operand); read t covers e = 4t .. 4t+3.
+  const int tr_r = lane & 15, tr_dsub = (lane >> 4) & 1;
+  auto vt_operand = [&](int buf, int db, int ks) -> bf16x8_t {
+    short4_t h0, h1;
+    const int d = 32 * db + 16 * tr_dsub + 4 * (tr_r & 3);
+    const int key0 = 16 * ks + 4 * hf + (tr_r >> 2);
+    h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&s_v[buf][swz_v(key0, d >> 3) + (d & 7)]));
+    h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&s_v[buf][swz_v(key0 + 8, d >> 3) + (d & 7)]));
+    short8_t r8;
+    r8[0] = h0[0]; r8[1] = h0[1]; r8[2] = h0[2]; r8[3] = h0[3];
+    r8[4] = h1[0]; r8[5] = h1[1]; r8[6] = h1[2]; r8[7] = h1[3];
+    return __builtin_bit_cast(bf16x8_t, r8);
   };
 
-  f32x16 oacc[PD / 32];
+  f32x16 oacc[RB][PD / 32];
 #pragma unroll
-  for (int db = 0; db < PD / 32; ++db)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+    for (int db = 0; db < PD / 32; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[rb][db][v] = 0.0f;
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+  }
 
-  load_tile(tile_of(0));
-  store_tile(0);
+  load_tile(tile_of(0), 0);
+  wait_vm0();
   __syncthreads();
-
   for (int n = 0; n < n_tiles; ++n) {
     const int buf = n & 1;
     const int kt = tile_of(n);
     const int64_t k0 = int64_t(kt) * BN;
-    if (n + 1 < n_tiles) load_tile(tile_of(n + 1));
+    if (n + 1 < n_tiles) load_tile(tile_of(n + 1), buf ^ 1);
 
-    // S^T = K Q^T : two 32-key blocks
-    f32x16 sacc[2];
+    // S^T = K Q^T for both row blocks; each K operand read from LDS serves both
+    f32x16 sacc[RB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.0f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[rb][kb][v] = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ds = 0; ds < PD / 16; ++ds) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][(kb * 32 + l32) * KP + 16 * ds + 8 * hf]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[ds], sacc[kb], 0, 0, 0);
+        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][swz_k(kb * 32 + l32, 2 * ds + hf)]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[rb][ds], sacc[rb][kb], 0, 0, 0);
       }
-    }
 
-    // mask (boundary tiles only): key = k0 + kb*32 + 8*(v/4) + 4*hf + v%4, row = my_row
+    // masks apply only where some (row, key) pair of the tile is invisible
     bool full;
     if (retr) {
       full = (k0 + BN - 1 <= R0);
     } else {
       full = (k0 + BN - 1 <= R0) && (k0 >= Rl - a.window + 1 || k0 + BN - 1 < a.n_sinks);
     }
-    float tmax = -INFINITY;
+    uint32_t pk[RB][2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      // row max on the raw scores (the scale is positive), masked entries -inf
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = sacc[kb][v] * a.scale_log2;
-        if (!full) {
-          const int64_t key = k0 + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-          bool vis = key <= my_row;
-          if (!retr) vis = vis && (key < a.n_sinks || key > my_row - a.window);
-          x = vis ? x : -INFINITY;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = sacc[rb][kb][v];
+          if (!full) {
+            const int64_t key = k0 + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+            bool vis = key <= my_row[rb];
+            if (!retr) vis = vis && (key < a.n_sinks || key > my_row[rb] - a.window);
+            x = vis ? x : -INFINITY;
+            sacc[rb][kb][v] = x;
+          }
+          tmax = fmaxf(tmax, x);
         }
-        sacc[kb][v] = x;
-        tmax = fmaxf(tmax, x);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;   // both halves hold the same row
+      // lazy reference max (log2 domain): move it only when the row max grows past 2^8
+      const bool grow = tmax > m_run[rb] + 8.0f;
+      if (__ballot(grow)) {
+        const float m_new = grow ? tmax : m_run[rb];
+        const float alpha = (m_run[rb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < PD / 32; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[rb][db][v] *= alpha;
+        m_run[rb] = m_new;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));             // both halves hold the same row
-    // lazy reference max: move it only when the row max grows past 2^8 of headroom
-    const bool grow = tmax > m_run + 8.0f;
-    if (__ballot(grow)) {
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      const bool live = m_run[rb] != -INFINITY;
+      const float nm = -m_run[rb];
+      float psum = 0.0f;
 #pragma unroll
-      for (int db = 0; db < PD / 32; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-      m_run = m_new;
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v], a.scale_log2, nm)) : 0.0f;
+          const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v + 1], a.scale_log2, nm)) : 0.0f;
+          pk[rb][kb][v >> 1] = pack_bf16x2(p0, p1);
+          // row sum of the bf16 probabilities the PV product uses (one dot2 per pair)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[rb][kb][v >> 1]),
+                                                 __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+        }
+      l_run[rb] += psum;
     }
-    const bool live = m_run != -INFINITY;
-    uint32_t pk[2][8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = live ? __builtin_amdgcn_exp2f(sacc[kb][v] - m_run) : 0.0f;
-        const float p1 = live ? __builtin_amdgcn_exp2f(sacc[kb][v + 1] - m_run) : 0.0f;
-        psum += p0 + p1;
-        pk[kb][v >> 1] = pack_bf16x2(p0, p1);
-      }
-    l_run += psum;
 
-    // O^T += V^T P^T : four 32-dim blocks x four 16-key steps
+    // O^T += V^T P^T: each V^T operand read from LDS serves both row blocks
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb = ks >> 1, half = ks & 1;
-      const uint4 pb = make_uint4(pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2], pk[kb][4 * half + 3]);
 #pragma unroll
       for (int db = 0; db < PD / 32; ++db) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(&s_vt[buf][(db * 32 + l32) * VP + 16 * ks + 8 * hf]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(pb), oacc[db], 0, 0, 0);
+        const bf16x8_t vv = vt_operand(buf, db, ks);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint4 pb = make_uint4(pk[rb][kb][4 * half], pk[rb][kb][4 * half + 1], pk[rb][kb][4 * half + 2],
+                                      pk[rb][kb][4 * half + 3]);
+          oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(pb), oacc[rb][db], 0, 0, 0);
+        }
       }
     }
-
-    if (n + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+    wait_vm0();                 // this wave's copies of the next tile have landed
+    __syncthreads();            // ... and everyone's; the current buffer is free again
   }
 
-  // ---- normalise and store: lane holds row my_row, dims db*32 + 8*(v/4) + 4*hf + (v%4)
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (my_row < Rend) {
-    uint16_t* op = a.out + ((my_row - a.c0) * a.Hq + qh) * PD;
+  // ---- normalise and store: lane holds row my_row[rb], dims db*32 + 8*(v/4) + 4*hf + (v%4)
 #pragma unroll
-    for (int db = 0; db < PD / 32; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lt = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (my_row[rb] < Rend) {
+      uint16_t* op = a.out + ((my_row[rb] - a.c0) * a.Hq + qh) * PD;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * g4 + 4 * hf) = w;
-      }
+      for (int db = 0; db < PD / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint2 w;
+          w.x = pack_bf16x2(oacc[rb][db][4 * g4] * inv, oacc[rb][db][4 * g4 + 1] * inv);
+          w.y = pack_bf16x2(oacc[rb][db][4 * g4 + 2] * inv, oacc[rb][db][4 * g4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + db * 32 + 8 * g4 + 4 * hf) = w;
+        }
+    }
   }
 }
 
@@ -338,7 +390,8 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
   if (L.n_ret > 0 && (!k_pre || !w_k_idx || !k_idx_cache))
     return fail(RTP_EINVAL, "rtp_prefill_attn: NULL indexer pointer");
   if (w_head_stride < 0) return fail(RTP_EINVAL, "w_head_stride must be >= 0");
-  if (!std::isfinite(sm_scale)) return fail(RTP_EINVAL, "rtp_prefill_attn: sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(RTP_EINVAL, "rtp_prefill_attn: sm_scale must be finite and > 0");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       (k_pre && !aligned(k_pre, 16)) || (k_idx_cache && !aligned(k_idx_cache, 2)))
     return fail(RTP_EINVAL, "rtp_prefill_attn: tensors must be 16-byte aligned");
