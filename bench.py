@@ -30,6 +30,30 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per call from rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, summed over the call's kernels), with the scale each counter showed for a
+# plain 1 GiB device copy: FETCH_SIZE read half the bytes moved, WRITE_SIZE all of them.
+# `src` is the sha256 prefix of the kernel source the counters were taken on; once it
+# changes the figure no longer describes the kernel and `traffic` is reported as null.
+COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
+MEASURED_KIB = {
+    "prefill_attn": {"src": ("rtp_prefill.hip", "0841fa6519701399"),
+                     "fetch": 1074.0 + 204736.5, "write": 256.0 + 32768.6},
+    "sparse_decode": {"src": ("rtp_decode.hip", "890b671f5d4fa52d"),
+                      "fetch": 2083.3 + 172603.8 + 946.0, "write": 54.6 + 2176.3 + 16.0},
+}
+
+
+def measured_traffic(name):
+    """HBM bytes per call of `name` as the counters measured it, or None if its source changed."""
+    import hashlib
+    m = MEASURED_KIB[name]
+    path = os.path.join(ROOT, "head_wise_sparse_amd", "csrc", m["src"][0])
+    with open(path, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != m["src"][1]:
+            return None
+    return int((m["fetch"] * COPY_SCALE["fetch"] + m["write"] * COPY_SCALE["write"]) * 1024)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -42,7 +66,22 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the p = 0.9 / 0.99 decode timings")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run only one part (for profiling); the JSON line is still printed")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device 3 times (scale reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read for it is the
+    scale that turns those counters into bytes for the kernels measured alongside."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
 def log(msg):
@@ -236,6 +275,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from head_wise_sparse_amd import rtp
     torch.cuda.set_device(0)
@@ -310,7 +352,8 @@ def main():
         sp_bytes = ab["gathered_kv_union"] + 2 * 2 * dec.cfg.head_dim * dec.cfg.batch * dec.cfg.n_kv_r * dec.cfg.group
         sp_gbs = sp_bytes / (calls["sparse_decode"] * 1e-3) / 1e9
         rooflines["sparse_decode"] = {"bound": "hbm", "achieved": round(sp_gbs, 1), "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": round(sp_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                      "unit": "GB/s", "frac": round(sp_gbs / HBM_PEAK_GBS, 4),
+                                      "traffic": measured_traffic("sparse_decode"), "algorithmic_bytes": sp_bytes,
                                       "kernel": "rtp_sparse_decode_attn (k_range_starts + k_decode_partial + "
                                                 "k_decode_merge)", "us": round(calls["sparse_decode"] * 1e3, 2)}
         if not args.no_sweep:
@@ -338,7 +381,8 @@ def main():
                           "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "flops": fl}
         rooflines["prefill_attn"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                                     "traffic": None, "kernel": "rtp_prefill_attn (k_kidx_proj + k_prefill_attn)",
+                                     "traffic": measured_traffic("prefill_attn"),
+                                     "kernel": "rtp_prefill_attn (k_kidx_proj + k_prefill_attn)",
                                      "ms_per_chunk": round(pre_ms / pre.cfg.n_chunks, 4)}
     # the dominant kernel of the step is the one that takes the most time
     if rooflines:
