@@ -88,7 +88,7 @@ size_t score_ws_bytes(const Layer& L, int64_t n_ctx) {
 
 SelLayout sel_layout(const Layer& L, int64_t n_ctx) {
   SelLayout s{};
-  size_t rows = size_t(L.B) * L.n_ret * L.G;
+  const size_t rows = size_t(L.B) * L.n_ret * L.G;
   s.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
   size_t off = 0;
   s.hist_mass = off;
@@ -101,8 +101,8 @@ SelLayout sel_layout(const Layer& L, int64_t n_ctx) {
   off = round_up(off + rows * 3 * 64 * sizeof(uint32_t), 256);
   s.state = off;
   off = round_up(off + rows * sizeof(SelRowState), 256);
-  s.tile_ctr = off;
-  off = round_up(off + rows * sizeof(uint32_t), 256);
+  s.ctr = off;
+  off = round_up(off + rows * 2 * sizeof(uint32_t), 256);
   s.lookback = off;
   off = round_up(off + rows * size_t(s.nblk) * sizeof(uint64_t), 256);
   s.total = off;

@@ -120,8 +120,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void k_decode_partial(DecArgs a) {
 #pragma unroll
     for (int t = 0; t < G; ++t) {
       const int64_t so = int64_t(grp * G + t) * (a.nsplit + 1) + split;
-      lo[t] = a.starts[so];
-      hi[t] = a.starts[so + 1];
+      // clamped: the range index may come from the caller
+      hi[t] = min(max(a.starts[so + 1], 0), a.n_ctx);
+      lo[t] = min(max(a.starts[so], 0), hi[t]);
     }
     int pos[G][SP];
 #pragma unroll
@@ -426,8 +427,9 @@ rtp_status check_common(const Layer& L, int64_t n_ctx, const uint16_t* q, const 
 
 extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q,
                                              const uint16_t* k_cache, const uint16_t* v_cache,
-                                             const int32_t* sel_idx, const int32_t* sel_count, float sm_scale,
-                                             uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+                                             const int32_t* sel_idx, const int32_t* sel_count,
+                                             const int32_t* sel_starts, float sm_scale, uint16_t* out, void* ws,
+                                             size_t ws_bytes, void* stream) {
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;
@@ -443,11 +445,15 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
   const int nsplit = int((n_ctx + kDecRange - 1) / kDecRange);
   const int rows = L.B * L.n_ret * L.G;
   float* part = static_cast<float*>(ws);
-  int32_t* starts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + dec_sparse_starts_offset(L, n_ctx));
-  const unsigned sb = unsigned(std::min<int64_t>((n_ctx + 256) / 256, 64));
-  hipLaunchKernelGGL(k_range_starts, dim3(sb, rows), dim3(256), 0, s, sel_idx, sel_count, starts, L.n_cap,
-                     int(n_ctx), nsplit);
-  if ((st = check_launch("k_range_starts")) != RTP_OK) return st;
+  const int32_t* starts = sel_starts;
+  if (!starts) {
+    int32_t* built = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + dec_sparse_starts_offset(L, n_ctx));
+    const unsigned sb = unsigned(std::min<int64_t>((n_ctx + 256) / 256, 64));
+    hipLaunchKernelGGL(k_range_starts, dim3(sb, rows), dim3(256), 0, s, sel_idx, sel_count, built, L.n_cap,
+                       int(n_ctx), nsplit);
+    if ((st = check_launch("k_range_starts")) != RTP_OK) return st;
+    starts = built;
+  }
   DecArgs a{};
   a.q = q;
   a.k = k_cache;

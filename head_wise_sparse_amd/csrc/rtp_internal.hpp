@@ -51,7 +51,7 @@ constexpr int kScoreItems = 8;                                  // tokens per th
 constexpr int kScoreTile = kScoreThreads * kScoreItems;         // tokens per block
 size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
 
-// Top-p selection.
+// Top-p selection (four launches; the workspace is zero before and after a call).
 constexpr int kSelThreads = 256;
 constexpr int kSelItems = 16;
 constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per block
@@ -69,7 +69,7 @@ struct SelRowState {             // one per score row, lives in the workspace
 };
 static_assert(sizeof(SelRowState) == 56, "row state layout");
 struct SelLayout {
-  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, tile_ctr, lookback, total;
+  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, lookback, total;
   int nblk;
 };
 SelLayout sel_layout(const Layer& L, int64_t n_ctx);
@@ -79,33 +79,27 @@ struct SelRows {                 // device views of the selection workspace
   uint64_t* cmass;               // [rows][3][64]   coarse summaries (32 fine bins each)
   uint32_t* ccnt;                // [rows][3][64]
   SelRowState* state;            // [rows]
+  uint32_t* ctr;                 // [rows][2]       compaction: dynamic tile ids, blocks done
   uint64_t* lookback;            // [rows][nblk]
-  uint32_t* tile_ctr;            // [rows]
 };
 struct SelArgs {
   const float* scores;           // [rows][n_cap]
-  const float* row_max_in;       // [rows] (standalone selection) or null
-  const float2* score_part;      // [rows][score_nblk] (fused step: max/sum partials) or null
-  int score_nblk;
-  float* row_max_out;            // fused step: row statistics written by the first pass
-  float* row_sum_out;
+  const float* row_max;          // [rows]
   float top_p;
   int n_ctx;
   int64_t n_cap;
   int nblk;                      // selection tiles per row
   int32_t* sel_idx;
   int32_t* sel_count;
-  int32_t* starts;               // fused step: [rows][nsplit + 1] decode range starts, or null
+  int32_t* starts;               // [rows][nsplit + 1] range index of the selected lists, or null
   int nsplit;
   SelRows R;
 };
 SelRows sel_rows(void* ws, const SelLayout& lay);
-rtp_status launch_sel_zero(void* ws, size_t bytes, hipStream_t s);
-rtp_status launch_select_chain(const SelArgs& a, int rows, hipStream_t s);
 
 // Decode attention (sparse and window share the layout).
 constexpr int kDecThreads = 256;
-constexpr int kDecRange = 1024;          // token-index range per block (sparse path)
+constexpr int kDecRange = RTP_SEL_RANGE; // token-index range per block (sparse path)
 constexpr int kWinRange = 128;           // list positions per block (window path)
 constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);

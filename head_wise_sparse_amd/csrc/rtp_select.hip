@@ -24,6 +24,12 @@
 //             indices in increasing order: each tile counts its above / tied tokens and
 //             learns the counts of all earlier tiles through a decoupled look-back
 //             (relaxed atomics on 64-bit status words that carry the counts themselves).
+//             It also writes the range index of every list when asked for.
+// The workspace is all zero when a call starts and when it ends: each launch clears
+// what earlier launches left and nobody reads any more (hist<2> the level-0
+// histogram, compact the level-1 histogram), and the last compaction block of a row
+// to finish clears the rest of that row (level-2 histogram, look-back words, row state
+// and counters).
 #include <cmath>
 
 #include "rtp_internal.hpp"
@@ -114,36 +120,19 @@ __device__ Resolved resolve_level(const SelRows& R, int row, int level, const Re
   return o;
 }
 
-// Zero the selection workspace (histograms, summaries, states, counters, look-back).
-__global__ __launch_bounds__(256) void k_sel_zero(uint4* __restrict__ p, size_t n16) {
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256) p[i] = z;
-}
-
-// Row max for level 0: from row_max (standalone call) or from the scoring kernel's
-// per-block (max, sum) partials (fused decode step; block 0 also writes the row stats).
-__device__ float row_reference_max(const SelArgs& a, int row, int tid, float* s_red) {
-  if (!a.score_part) return a.row_max_in[row];
-  const float2* p = a.score_part + int64_t(row) * a.score_nblk;
-  float m = -INFINITY;
-  for (int i = tid; i < a.score_nblk; i += kSelThreads) m = fmaxf(m, p[i].x);
-  m = wave_max(m);
-  if ((tid & 63) == 0) s_red[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  if (blockIdx.x == 0 && a.row_max_out) {
-    float z = 0.0f;
-    for (int i = tid; i < a.score_nblk; i += kSelThreads) z += p[i].y * __expf(p[i].x - m);
-    z = wave_sum(z);
-    __syncthreads();
-    if ((tid & 63) == 0) s_red[tid >> 6] = z;
-    __syncthreads();
-    if (tid == 0) {
-      a.row_max_out[row] = m;
-      a.row_sum_out[row] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    }
+// Clear one level's histogram of a row (plain stores: the next launch sees them).
+// Block `blk` of `nblk` clears its share.
+__device__ __forceinline__ void clear_level(const SelRows& R, int row, int level, int blk, int nblk) {
+  uint64_t* gm = R.mass + (int64_t(row) * 3 + level) * kBins;
+  uint32_t* gc = R.cnt + (int64_t(row) * 3 + level) * kBins;
+  for (int i = blk * kSelThreads + int(threadIdx.x); i < kBins; i += nblk * kSelThreads) {
+    gm[i] = 0;
+    gc[i] = 0;
   }
-  return m;
+  if (blk == nblk - 1 && threadIdx.x < kCoarse) {
+    R.cmass[(int64_t(row) * 3 + level) * kCoarse + threadIdx.x] = 0;
+    R.ccnt[(int64_t(row) * 3 + level) * kCoarse + threadIdx.x] = 0;
+  }
 }
 
 template <int LEVEL>
@@ -155,7 +144,6 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   const int blk = blockIdx.x, row = blockIdx.y;
   __shared__ uint64_t h_m[NB];
   __shared__ uint32_t h_c[NB];
-  __shared__ float s_red[4];
   __shared__ uint32_t s_prefix;
 
   // scores of the tile: unconditional loads (index clamped), validity kept aside
@@ -173,11 +161,12 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   }
   float m;
   if constexpr (LEVEL == 0) {
-    m = row_reference_max(a, row, tid, s_red);
+    m = a.row_max[row];
     if (blk == 0 && tid == 0) a.R.state[row].ref_max = m;
   } else {
     m = a.R.state[row].ref_max;                      // written by the level-0 launch
   }
+  if constexpr (LEVEL == 2) clear_level(a.R, row, 0, blk, a.nblk);   // read last by hist<1>
   if (LEVEL > 0 && tid < 64) {
     Resolved in{};
     if (LEVEL == 2) {
@@ -221,14 +210,16 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
       atomicAdd(gc + i, h_c[i]);
     }
   }
-  // coarse summary: thread c < NB/32 sums its 32 fine bins
+  // coarse summary: thread c < NB/32 sums its 32 fine bins, starting at a different
+  // one per thread so that the lanes of a wave read different LDS banks
   if (tid < NB / kFinePer) {
     uint64_t sm = 0;
     uint32_t sc = 0;
 #pragma unroll 8
     for (int i = 0; i < kFinePer; ++i) {
-      sm += h_m[tid * kFinePer + i];
-      sc += h_c[tid * kFinePer + i];
+      const int f = tid * kFinePer + ((i + tid) & (kFinePer - 1));
+      sm += h_m[f];
+      sc += h_c[f];
     }
     if (sc) {
       atomicAdd(reinterpret_cast<unsigned long long*>(a.R.cmass + (int64_t(row) * 3 + LEVEL) * kCoarse + tid),
@@ -245,8 +236,9 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   constexpr int NW = kSelThreads / 64;
   __shared__ uint32_t s_tile, s_t, s_r;
   __shared__ uint32_t s_wa[kSelItems][NW], s_we[kSelItems][NW];
-  __shared__ uint32_t s_pa, s_pe;
-  if (tid == 0) s_tile = atomicAdd(a.R.tile_ctr + row, 1u);     // dynamic tile id: predecessors started
+  __shared__ uint32_t s_pa, s_pe, s_last;
+  uint32_t* ctr = a.R.ctr + 2 * int64_t(row);
+  if (tid == 0) s_tile = atomicAdd(ctr, 1u);          // dynamic tile id: predecessors started
   __syncthreads();
   const int tile = int(s_tile);
   const float* sp = a.scores + int64_t(row) * a.n_cap;
@@ -282,6 +274,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     }
   }
   __syncthreads();
+  clear_level(a.R, row, 1, tile, a.nblk);             // read last by hist<2>
   const uint32_t t = s_t, r = s_r;
   bool fa[kSelItems], fe[kSelItems];
   uint64_t ba[kSelItems], be[kSelItems];
@@ -365,6 +358,21 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
       ce += s_we[it][w];
     }
   }
+  // the last block of the row to finish clears what this launch read: every other
+  // block has finished its look-back and its reads of the level-2 histogram and state
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(ctr + 1, 1u) == uint32_t(a.nblk - 1));
+  __syncthreads();
+  if (s_last) {
+    for (int i = tid; i < a.nblk; i += kSelThreads) a.R.lookback[int64_t(row) * a.nblk + i] = 0;
+    uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
+    if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
+    clear_level(a.R, row, 2, 0, 1);
+    if (tid == 0) {
+      ctr[0] = 0;
+      ctr[1] = 0;
+    }
+  }
 }
 
 // top_p >= 1: every token, in order.
@@ -386,43 +394,16 @@ SelRows sel_rows(void* ws, const SelLayout& lay) {
   char* w = static_cast<char*>(ws);
   return SelRows{reinterpret_cast<uint64_t*>(w + lay.hist_mass), reinterpret_cast<uint32_t*>(w + lay.hist_cnt),
                  reinterpret_cast<uint64_t*>(w + lay.coarse_mass), reinterpret_cast<uint32_t*>(w + lay.coarse_cnt),
-                 reinterpret_cast<SelRowState*>(w + lay.state), reinterpret_cast<uint64_t*>(w + lay.lookback),
-                 reinterpret_cast<uint32_t*>(w + lay.tile_ctr)};
-}
-
-rtp_status launch_sel_zero(void* ws, size_t bytes, hipStream_t s) {
-  const size_t n16 = bytes / 16;
-  const unsigned zb = unsigned(std::min<size_t>((n16 + 255) / 256, 2048));
-  hipLaunchKernelGGL(k_sel_zero, dim3(zb), dim3(256), 0, s, reinterpret_cast<uint4*>(ws), n16);
-  return check_launch("k_sel_zero");
-}
-
-rtp_status launch_select_chain(const SelArgs& a0, int rows, hipStream_t s) {
-  SelArgs a = a0;
-  rtp_status st;
-  if (a.top_p >= 1.0f) {
-    hipLaunchKernelGGL(k_sel_all, dim3(unsigned((a.n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, a.n_ctx,
-                       a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
-    return check_launch("k_sel_all");
-  }
-  const dim3 grid(a.nblk, rows);
-  hipLaunchKernelGGL(k_sel_hist<0>, grid, dim3(kSelThreads), 0, s, a);
-  if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
-  a.score_part = nullptr;                    // later levels read the reference max from the row state
-  a.row_max_in = nullptr;
-  hipLaunchKernelGGL(k_sel_hist<1>, grid, dim3(kSelThreads), 0, s, a);
-  if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
-  hipLaunchKernelGGL(k_sel_hist<2>, grid, dim3(kSelThreads), 0, s, a);
-  if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
-  hipLaunchKernelGGL(k_sel_compact, grid, dim3(kSelThreads), 0, s, a);
-  return check_launch("k_sel_compact");
+                 reinterpret_cast<SelRowState*>(w + lay.state), reinterpret_cast<uint32_t*>(w + lay.ctr),
+                 reinterpret_cast<uint64_t*>(w + lay.lookback)};
 }
 
 }  // namespace rtp
 
 extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx, const float* scores,
                                       const float* row_max, const float* row_sum, float top_p, int32_t* sel_idx,
-                                      int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+                                      int32_t* sel_count, int32_t* sel_starts, void* ws, size_t ws_bytes,
+                                      void* stream) {
   (void)row_sum;
   Layer L;
   rtp_status st = check_desc(desc, &L);
@@ -440,18 +421,31 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   if (top_p < 1.0f && (!ws || ws_bytes < lay.total || !aligned(ws, 256)))
     return fail(RTP_EWORKSPACE, "rtp_topp_select: workspace needs %zu bytes, 256-aligned (got %zu)", lay.total,
                 ws_bytes);
+  const int nsplit = int((n_ctx + kDecRange - 1) / kDecRange);
+  if (top_p >= 1.0f) {
+    hipLaunchKernelGGL(k_sel_all, dim3(unsigned((n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, int(n_ctx),
+                       L.n_cap, sel_idx, sel_count, sel_starts, nsplit);
+    return check_launch("k_sel_all");
+  }
   SelArgs a{};
   a.scores = scores;
-  a.row_max_in = row_max;
+  a.row_max = row_max;
   a.top_p = top_p;
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
   a.nblk = lay.nblk;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
-  if (top_p < 1.0f) {
-    a.R = sel_rows(ws, lay);
-    if ((st = launch_sel_zero(ws, lay.total, s)) != RTP_OK) return st;
-  }
-  return launch_select_chain(a, rows, s);
+  a.starts = sel_starts;
+  a.nsplit = nsplit;
+  a.R = sel_rows(ws, lay);
+  const dim3 grid(a.nblk, rows);
+  hipLaunchKernelGGL(k_sel_hist<0>, grid, dim3(kSelThreads), 0, s, a);
+  if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
+  hipLaunchKernelGGL(k_sel_hist<1>, grid, dim3(kSelThreads), 0, s, a);
+  if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
+  hipLaunchKernelGGL(k_sel_hist<2>, grid, dim3(kSelThreads), 0, s, a);
+  if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
+  hipLaunchKernelGGL(k_sel_compact, grid, dim3(kSelThreads), 0, s, a);
+  return check_launch("k_sel_compact");
 }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libr
 
 RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EDEVICE = range(5)
 CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK, CALL_PREFILL = range(5)
+SEL_RANGE = 1024          # RTP_SEL_RANGE: token range of one entry of a selected-set range index
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
             "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_status_string", "rtp_last_error", "rtp_version"]
@@ -55,9 +56,9 @@ def load() -> C.CDLL:
         "rtp_workspace_bytes": (C.c_size_t, [D, C.c_int64, C.c_int]),
         "rtp_indexer_score": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, _P,
                                         C.c_size_t, _P]),
-        "rtp_topp_select": (C.c_int, [D, C.c_int64, _P, _P, _P, C.c_float, _P, _P, _P, C.c_size_t, _P]),
-        "rtp_sparse_decode_attn": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, _P, C.c_float, _P, _P, C.c_size_t,
-                                             _P]),
+        "rtp_topp_select": (C.c_int, [D, C.c_int64, _P, _P, _P, C.c_float, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_sparse_decode_attn": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, _P, _P, C.c_float, _P, _P,
+                                             C.c_size_t, _P]),
         "rtp_window_sink_attn": (C.c_int, [D, C.c_int64, _P, _P, _P, C.c_float, _P, _P, C.c_size_t, _P]),
         "rtp_prefill_attn": (C.c_int, [D, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, C.c_int64, _P, C.c_float,
                                        _P, _P, C.c_size_t, _P]),
@@ -149,7 +150,7 @@ def workspace(layer: Layer, n_ctx: int, which: int, device="cuda"):
     """A workspace tensor of the size the call needs (256-byte aligned by torch's allocator)."""
     import torch
     n = max(256, rtp_workspace_bytes(layer, n_ctx, which))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)      # workspaces start zero-filled
 
 
 def rtp_indexer_score(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_stride: int, k_idx, idx_scale: float,
@@ -160,19 +161,20 @@ def rtp_indexer_score(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_stride: i
                                     p, n, _stream(stream)))
 
 
-def rtp_topp_select(layer: Layer, n_ctx: int, scores, row_max, row_sum, top_p: float, sel_idx, sel_count, ws,
-                    stream=None):
+def rtp_topp_select(layer: Layer, n_ctx: int, scores, row_max, row_sum, top_p: float, sel_idx, sel_count,
+                    sel_starts, ws, stream=None):
     p, n = _ws(ws)
     _check(load().rtp_topp_select(layer.desc, int(n_ctx), _ptr(scores), _ptr(row_max), _ptr(row_sum),
-                                  float(top_p), _ptr(sel_idx), _ptr(sel_count), p, n, _stream(stream)))
+                                  float(top_p), _ptr(sel_idx), _ptr(sel_count), _ptr(sel_starts), p, n,
+                                  _stream(stream)))
 
 
-def rtp_sparse_decode_attn(layer: Layer, n_ctx: int, q, k_cache, v_cache, sel_idx, sel_count, sm_scale: float,
-                           out, ws, stream=None):
+def rtp_sparse_decode_attn(layer: Layer, n_ctx: int, q, k_cache, v_cache, sel_idx, sel_count, sel_starts,
+                           sm_scale: float, out, ws, stream=None):
     p, n = _ws(ws)
     _check(load().rtp_sparse_decode_attn(layer.desc, int(n_ctx), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                         _ptr(sel_idx), _ptr(sel_count), float(sm_scale), _ptr(out), p, n,
-                                         _stream(stream)))
+                                         _ptr(sel_idx), _ptr(sel_count), _ptr(sel_starts), float(sm_scale),
+                                         _ptr(out), p, n, _stream(stream)))
 
 
 def rtp_window_sink_attn(layer: Layer, n_ctx: int, q, k_cache, v_cache, sm_scale: float, out, ws, stream=None):
@@ -208,8 +210,9 @@ def from_device_bf16(t) -> np.ndarray:
 
 class DecodeStep:
     """One decode step of one layer through the four decode calls, with every output
-    and workspace allocated once.  ``run`` enqueues: indexer scores -> top-p sets ->
-    sparse attention (retrieval heads) and sink+window attention (local heads)."""
+    and workspace allocated once.  ``run`` enqueues, on one stream: indexer scores ->
+    top-p sets (with their range index) -> sparse attention of the retrieval heads ->
+    sink+window attention of the local heads (the two write disjoint rows of ``out``)."""
 
     def __init__(self, layer: Layer, n_ctx: int, top_p: float, sm_scale: Optional[float] = None,
                  idx_scale: float = 1.0, device="cuda"):
@@ -218,11 +221,13 @@ class DecodeStep:
         self.sm_scale = (1.0 / layer.head_dim ** 0.5) if sm_scale is None else float(sm_scale)
         self.idx_scale = float(idx_scale)
         B, R, cap = layer.batch, layer.n_q_r, layer.n_cap
+        nsplit = (self.n_ctx + SEL_RANGE - 1) // SEL_RANGE
         self.scores = torch.empty(B * R * cap, dtype=torch.float32, device=device)
         self.row_max = torch.empty(B * R, dtype=torch.float32, device=device)
         self.row_sum = torch.empty(B * R, dtype=torch.float32, device=device)
         self.sel_idx = torch.empty(B * R * cap, dtype=torch.int32, device=device)
         self.sel_count = torch.empty(B * R, dtype=torch.int32, device=device)
+        self.sel_starts = torch.empty(B * R * (nsplit + 1), dtype=torch.int32, device=device)
         self.out = torch.zeros(B * layer.n_q_heads * layer.head_dim, dtype=torch.bfloat16, device=device)
         self.ws = {w: workspace(layer, n_ctx, w, device) for w in
                    (CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK)}
@@ -234,8 +239,8 @@ class DecodeStep:
         rtp_indexer_score(L, n, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, self.scores, self.row_max,
                           self.row_sum, self.ws[CALL_INDEXER_SCORE], stream)
         rtp_topp_select(L, n, self.scores, self.row_max, self.row_sum, self.top_p, self.sel_idx, self.sel_count,
-                        self.ws[CALL_TOPP_SELECT], stream)
-        rtp_sparse_decode_attn(L, n, q, k_cache, v_cache, self.sel_idx, self.sel_count, self.sm_scale, self.out,
-                               self.ws[CALL_SPARSE_DECODE], stream)
+                        self.sel_starts, self.ws[CALL_TOPP_SELECT], stream)
+        rtp_sparse_decode_attn(L, n, q, k_cache, v_cache, self.sel_idx, self.sel_count, self.sel_starts,
+                               self.sm_scale, self.out, self.ws[CALL_SPARSE_DECODE], stream)
         rtp_window_sink_attn(L, n, q, k_cache, v_cache, self.sm_scale, self.out, self.ws[CALL_WINDOW_SINK], stream)
         return self.out

@@ -23,8 +23,12 @@
  *    IEEE bfloat16 raw bits (uint16_t); results are rounded to nearest even.
  *  - Ownership: the library allocates nothing.  Scratch space comes from the
  *    caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned); size it with
- *    rtp_workspace_bytes().  A workspace may be reused by later calls on the same
- *    stream; calls that run concurrently need distinct workspaces.
+ *    rtp_workspace_bytes().  A workspace must be ZERO-FILLED before its first use:
+ *    some calls keep counters and histograms in it that their kernels reset
+ *    themselves, so every call that completes leaves the workspace zero-filled
+ *    again.  A workspace may be reused by later calls on the same stream (of any
+ *    call kind and size); calls that run concurrently need distinct workspaces.
+ *    After a device fault, zero-fill it again before reuse.
  *  - Errors: every argument is validated on the host before anything is
  *    enqueued.  On error nothing is launched and no output is touched; the
  *    status is returned and rtp_last_error() (thread-local) explains it.
@@ -69,6 +73,9 @@ typedef struct rtp_layer_desc {
   int32_t n_sinks;        /* local heads: sink tokens at the start of the sequence (>= 0) */
   int32_t window;         /* local heads: sliding window, counting the query token (>= 1) */
 } rtp_layer_desc;
+
+/* Token-index range of one entry of a selected-set range index (sel_starts). */
+#define RTP_SEL_RANGE 1024
 
 /* Which call rtp_workspace_bytes() sizes. */
 typedef enum rtp_call {
@@ -124,10 +131,18 @@ rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ctx,
  *   sel_idx  int32 [B][Hq_r][n_cap]: the first sel_count entries of each row hold
  *            the selected token indices in increasing order; the rest is untouched
  *   sel_count int32 [B][Hq_r]
+ *   sel_starts int32 [B][Hq_r][ceil(n_ctx / RTP_SEL_RANGE) + 1] or NULL: a range
+ *            index of each selected list, entry q = number of selected tokens with
+ *            index < q * RTP_SEL_RANGE (the last entry = sel_count).  Optional; when
+ *            given, rtp_sparse_decode_attn can take it instead of rebuilding it.
+ * The row_max values are the reference of every weight exp(s - row_max): pass the
+ * row maxima rtp_indexer_score wrote (a smaller value saturates weights at 1).
+ * The workspace holds the radix histograms, row states, counters and look-back
+ * words of the search; see the zero-fill rule above.
  */
 rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
                            const float* scores, const float* row_max, const float* row_sum,
-                           float top_p, int32_t* sel_idx, int32_t* sel_count,
+                           float top_p, int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -139,6 +154,8 @@ rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
  *   q        bf16 [B][Hq][D]  post-RoPE queries
  *   k_cache, v_cache bf16 [B][Hkv][n_cap][D]
  *   sel_idx, sel_count  as written by rtp_topp_select (indices < n_ctx, increasing)
+ *   sel_starts  the range index rtp_topp_select wrote for the same sets, or NULL
+ *            (then it is rebuilt from sel_idx in the workspace)
  *   out      bf16 [B][Hq][D]; only retrieval heads' rows are written.  A row
  *            with sel_count == 0 is written as zeros.
  * Rows of one GQA group are processed together: a cached row selected by several
@@ -146,8 +163,8 @@ rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
  */
 rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t n_ctx,
                                   const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
-                                  const int32_t* sel_idx, const int32_t* sel_count, float sm_scale,
-                                  uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+                                  const int32_t* sel_idx, const int32_t* sel_count, const int32_t* sel_starts,
+                                  float sm_scale, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * rtp_window_sink_attn -- decode attention of the local heads over

@@ -98,14 +98,14 @@ def test_call_validation():
     assert _call_score(L, ptr=FAKE + 2) == rtp.RTP_EINVAL                      # misaligned
     assert _call_score(L, ptr=None) == rtp.RTP_EINVAL                          # NULL tensors
     for p in (0.0, -0.5, math.nan):
-        assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, p, FAKE, FAKE, FAKE, 1 << 30, None) \
+        assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, p, FAKE, FAKE, None, FAKE, 1 << 30, None) \
             == rtp.RTP_EINVAL
-    assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, FAKE, 64, None) \
+    assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, None, FAKE, 64, None) \
         == rtp.RTP_EWORKSPACE
-    assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, 1 << 30,
+    assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, None, FAKE, None, 0.1, FAKE, FAKE, 1 << 30,
                                       None) == rtp.RTP_EINVAL
-    assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, math.inf, FAKE, FAKE, 1 << 30,
-                                      None) == rtp.RTP_EINVAL
+    assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, math.inf, FAKE, FAKE,
+                                      1 << 30, None) == rtp.RTP_EINVAL
     assert lib.rtp_window_sink_attn(L.desc, 1000, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 8, None) \
         == rtp.RTP_EWORKSPACE
     L1 = _layer(batch=1, n_cap=32768)

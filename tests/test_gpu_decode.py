@@ -114,15 +114,24 @@ def _run_select(L, n_ctx, scores32: np.ndarray, p: float, n_cap=None):
                          .sum(axis=1).astype(np.float32)).cuda()
     sel = torch.full((rows * cap,), -7, dtype=torch.int32, device="cuda")
     cnt = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
-    rtp.rtp_topp_select(L, n_ctx, st, m, z, p, sel, cnt, rtp.workspace(L, n_ctx, rtp.CALL_TOPP_SELECT))
+    nsplit = (n_ctx + rtp.SEL_RANGE - 1) // rtp.SEL_RANGE
+    starts = torch.full((rows * (nsplit + 1),), -3, dtype=torch.int32, device="cuda")
+    ws = rtp.workspace(L, n_ctx, rtp.CALL_TOPP_SELECT)
+    rtp.rtp_topp_select(L, n_ctx, st, m, z, p, sel, cnt, starts, ws)
     torch.cuda.synchronize()
+    assert not ws.any().item(), "the selection workspace must be left zero-filled"
     seln, cntn = sel.view(rows, cap).cpu().numpy(), cnt.cpu().numpy()
+    stn = starts.view(rows, nsplit + 1).cpu().numpy()
     out = []
     for r in range(rows):
         c = int(cntn[r])
         assert 1 <= c <= n_ctx
         assert np.all(seln[r, c:] == -7), "entries past sel_count must be untouched"
         out.append(seln[r, :c])
+        # range index: entry q counts the selected tokens below q * SEL_RANGE
+        want = np.searchsorted(seln[r, :c], np.arange(nsplit + 1) * rtp.SEL_RANGE)
+        want[nsplit] = c
+        assert np.array_equal(stn[r], want), f"row {r}: range index differs"
     return out
 
 
@@ -217,7 +226,7 @@ def test_sparse_decode_on_oracle_sets(name, over):
     L = P.layer_for(cfg)
     sel, cnt = _sel_tensors(ora["sel"], B, R, N)
     out = torch.zeros(B * cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
-    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, 1 / math.sqrt(cfg.head_dim), out,
+    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, None, 1 / math.sqrt(cfg.head_dim), out,
                                rtp.workspace(L, N, rtp.CALL_SPARSE_DECODE))
     torch.cuda.synchronize()
     g = rtp.from_device_bf16(out).reshape(B, cfg.n_q_heads, cfg.head_dim)
@@ -243,9 +252,19 @@ def test_sparse_decode_special_sets():
     L = P.layer_for(cfg)
     sel, cnt = _sel_tensors(sets, 1, 8, N)
     out = torch.zeros(cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
-    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, 1 / math.sqrt(128), out,
+    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, None, 1 / math.sqrt(128), out,
+                               rtp.workspace(L, N, rtp.CALL_SPARSE_DECODE))
+    # the same sets with a caller-built range index give the same bits
+    nsplit = (N + rtp.SEL_RANGE - 1) // rtp.SEL_RANGE
+    st = np.zeros((8, nsplit + 1), np.int32)
+    for (b, ci), s_ in sets.items():
+        st[ci] = np.searchsorted(s_, np.arange(nsplit + 1) * rtp.SEL_RANGE)
+        st[ci, nsplit] = len(s_)
+    out2 = torch.zeros_like(out)
+    rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, torch.from_numpy(st).cuda(), 1 / math.sqrt(128), out2,
                                rtp.workspace(L, N, rtp.CALL_SPARSE_DECODE))
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     g = rtp.from_device_bf16(out).reshape(cfg.n_q_heads, 128)
     for (b, ci), s in sets.items():
         h = cfg.retrieval_kv[ci // G] * G + ci % G
@@ -338,10 +357,10 @@ def test_decode_step_is_deterministic():
     P.require_gpu()
     torch = _torch()
     x, d, step, out = _decode_step("decode_b8_32k", 0.95)
-    a = [t.clone() for t in (step.scores, step.row_max, step.sel_count, step.sel_idx, out)]
+    a = [t.clone() for t in (step.scores, step.row_max, step.sel_count, step.sel_idx, step.sel_starts, out)]
     out2 = step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
     torch.cuda.synchronize()
-    b = [step.scores, step.row_max, step.sel_count, step.sel_idx, out2]
+    b = [step.scores, step.row_max, step.sel_count, step.sel_idx, step.sel_starts, out2]
     for u, v in zip(a, b):
         assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
 
