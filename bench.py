@@ -109,17 +109,20 @@ class DecodeBench:
         self.graphs = {}
         torch.cuda.synchronize()
 
-    def _step_obj(self, p: float):
-        if p not in self.steps:
-            self.steps[p] = self.rtp.DecodeStep(self.L, self.cfg.n_ctx, p)
-        return self.steps[p]
+    def _step_obj(self, p: float, fused: bool = True):
+        if (p, fused) not in self.steps:
+            self.steps[(p, fused)] = self.rtp.DecodeStep(self.L, self.cfg.n_ctx, p, fused=fused)
+        return self.steps[(p, fused)]
 
     def _launch(self, p: float, i: int, which=None):
-        """Enqueue the decode step (or one of its calls) on the current stream."""
+        """Enqueue the decode step (fused call; which="separate": the four calls), or one
+        of the four calls, on the current stream."""
         rtp, L, n = self.rtp, self.L, self.cfg.n_ctx
-        st = self._step_obj(p)
         s = self.sets[i % len(self.sets)]
         if which is None:
+            return self._step_obj(p).run(s["q_pre"], s["q"], s["k"], s["v"], s["k_idx"], s["w_q_idx"])
+        st = self._step_obj(p, fused=False)
+        if which == "separate":
             return st.run(s["q_pre"], s["q"], s["k"], s["v"], s["k_idx"], s["w_q_idx"])
         if which == "indexer_score":
             rtp.rtp_indexer_score(L, n, s["q_pre"], s["w_q_idx"], L.head_dim * 16, s["k_idx"], 1.0, st.scores,
@@ -173,7 +176,7 @@ class DecodeBench:
 
     def algorithmic_bytes(self, p: float):
         """Bytes the method must move for one decode step (not the dense work it avoids)."""
-        cfg, st = self.cfg, self.steps[p]
+        cfg, st = self.cfg, self.steps[(p, True)]
         B, N, D, G = cfg.batch, cfg.n_ctx, cfg.head_dim, cfg.group
         R = cfg.n_kv_r * G
         cnt = st.sel_count.view(B, R).cpu().numpy()
@@ -298,6 +301,9 @@ def main():
             pre = None
 
     p0 = 0.95
+    if dec:                                  # capture the graph of every cache copy before timing
+        for i in range(len(dec.sets)):
+            dec.graph(p0, i)
     for i in range(args.warmup):
         if dec:
             dec.step(p0, i)
@@ -354,21 +360,26 @@ def main():
                                       "unit": "GB/s", "frac": round(sp_gbs / HBM_PEAK_GBS, 4),
                                       "traffic": measured_traffic("sparse_decode"), "algorithmic_bytes": sp_bytes,
                                       "kernel": "rtp_sparse_decode_attn (k_decode_partial + k_decode_merge)", "us": round(calls["sparse_decode"] * 1e3, 2)}
-        # the same step without a graph (every call launched from Python), for reference
-        for i in range(2):
+        # for reference: the four separate calls in one graph, and the fused call without a graph
+        for i in range(len(dec.sets)):
+            dec.graph(p0, i, "separate").replay()
             dec._launch(p0, i)
         torch.cuda.synchronize()
-        a, b = ev(), ev()
+        a, b, c, d = ev(), ev(), ev(), ev()
         a.record()
         for i in range(10):
-            dec._launch(p0, i)
+            dec.graph(p0, i, "separate").replay()
         b.record()
+        for i in range(10):
+            dec._launch(p0, i)
+        c.record()
         torch.cuda.synchronize()
-        res["decode"]["eager_us_per_step"] = round(a.elapsed_time(b) / 10 * 1e3, 2)
+        res["decode"]["separate_calls_us_per_step"] = round(a.elapsed_time(b) / 10 * 1e3, 2)
+        res["decode"]["eager_us_per_step"] = round(b.elapsed_time(c) / 10 * 1e3, 2)
         if not args.no_sweep:
             sweep = {}
             for p in (0.9, 0.99):
-                for i in range(2):
+                for i in range(len(dec.sets)):
                     dec.step(p, i)
                 torch.cuda.synchronize()
                 a, b = ev(), ev()

@@ -1,0 +1,362 @@
+// Device bodies of the split-K decode attention and of the split merge (shared by
+// the decode calls and the fused decode step).  See rtp_decode.hip for the design.
+#pragma once
+
+#include <cmath>
+
+#include "rtp_internal.hpp"
+
+using namespace rtp;
+using namespace rtp_dev;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;           // log2 headroom before the reference max moves
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPT consecutive lanes of a lane group (LPT = 8 or 16, inside one DPP row).
+template <int LPT>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror
+  if (LPT == 16) v += dpp<0x140>(v);   // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct DecArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* sel_idx;     // sparse only
+  const int32_t* starts;      // sparse only: [rows][nsplit + 1]
+  float* part;                // [rows][nsplit][D + 2]
+  int n_ctx;
+  int64_t n_cap;
+  int Hq, Hkv;
+  int nsplit;
+  float scale_log2;           // sm_scale * log2(e)
+  int s_end, w_start, list_len;   // window only
+  HeadMap map;
+};
+
+// One block of split-K decode: slice `split` of group `grp` (= b * n_heads_of_kind + rank).
+template <int D, int G, bool SPARSE>
+__device__ __forceinline__ void decode_block(const DecArgs& a, int split, int grp) {
+  constexpr int LPT = D / 8;            // lanes per cached row
+  constexpr int TPW = 64 / LPT;         // rows per wave step
+  constexpr int NLG = (kDecThreads / 64) * TPW;
+  constexpr int RANGE = SPARSE ? kDecRange : kWinRange;
+  constexpr int NW = kDecThreads / 64;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lg = wave * TPW + lane / LPT;
+  const int li = lane % LPT;
+  const int b = grp / a.map.n, rr = grp % a.map.n, g = a.map.kv[rr];
+  const uint16_t* kb = a.k + (int64_t(b) * a.Hkv + g) * a.n_cap * D + li * 8;
+  const uint16_t* vb = a.v + (int64_t(b) * a.Hkv + g) * a.n_cap * D + li * 8;
+
+  __shared__ uint16_t s_list[SPARSE ? RANGE : 1];
+  __shared__ uint8_t s_lmask[SPARSE ? RANGE : 1];
+  __shared__ uint32_t s_hm[SPARSE ? G * RANGE / 4 : 1];
+  __shared__ int s_wcnt[NW];
+  __shared__ float s_wm[NW][G], s_wl[NW][G];
+  __shared__ float s_wacc[NW][G][D];
+
+  uint32_t qw[G][4];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    const uint4 qv = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.Hq + g * G + t) * D + li * 8);
+    qw[t][0] = qv.x;
+    qw[t][1] = qv.y;
+    qw[t][2] = qv.z;
+    qw[t][3] = qv.w;
+  }
+
+  int U, j0 = 0, p0 = 0;
+  if constexpr (SPARSE) {
+    j0 = split * RANGE;
+    for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
+    __syncthreads();
+    uint8_t* hm = reinterpret_cast<uint8_t*>(s_hm);
+    // A head's selected indices are distinct, so at most RANGE of them fall in the
+    // range: SP per thread.  All loads are issued before any membership byte is set.
+    constexpr int SP = RANGE / kDecThreads;
+    int lo[G], hi[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int64_t so = int64_t(grp * G + t) * (a.nsplit + 1) + split;
+      // clamped: the range index may come from the caller
+      hi[t] = min(max(a.starts[so + 1], 0), a.n_ctx);
+      lo[t] = min(max(a.starts[so], 0), hi[t]);
+    }
+    int pos[G][SP];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int32_t* sr = a.sel_idx + int64_t(grp * G + t) * a.n_cap;
+#pragma unroll
+      for (int u = 0; u < SP; ++u) {
+        // unconditional load (index 0 stands in for out-of-range slots) so that the
+        // compiler keeps every load in flight instead of waiting inside a branch
+        const int k = lo[t] + u * kDecThreads + tid;
+        const int v = sr[k < hi[t] ? k : 0];
+        pos[t][u] = (k < hi[t]) ? v - j0 : -1;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int u = 0; u < SP; ++u)
+        if (pos[t][u] >= 0 && pos[t][u] < RANGE) hm[t * RANGE + pos[t][u]] = 1;
+    __syncthreads();
+    // ordered union of the G membership arrays: thread tid owns positions tid*8 .. tid*8+7
+    constexpr int PER = RANGE / kDecThreads;
+    uint8_t mk[PER];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int p = tid * PER + e;
+      uint32_t m = 0;
+#pragma unroll
+      for (int t = 0; t < G; ++t) m |= uint32_t(hm[t * RANGE + p]) << t;
+      mk[e] = uint8_t(m);
+      c += (m != 0);
+    }
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wcnt[wave] = incl;
+    __syncthreads();
+    int off = incl - c;
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) off += s_wcnt[w];
+      total += s_wcnt[w];
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (mk[e]) {
+        s_list[off] = uint16_t(tid * PER + e);
+        s_lmask[off] = mk[e];
+        ++off;
+      }
+    }
+    U = total;
+    __syncthreads();
+  } else {
+    p0 = split * RANGE;
+    U = min(RANGE, a.list_len - p0);
+  }
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[t][i] = 0.0f;
+  }
+
+  auto token_of = [&](int e, uint32_t& mask) -> int64_t {
+    if constexpr (SPARSE) {
+      mask = s_lmask[e];
+      return int64_t(j0) + s_list[e];
+    } else {
+      mask = (1u << G) - 1u;
+      const int p = p0 + e;
+      return p < a.s_end ? int64_t(p) : int64_t(a.w_start) + (p - a.s_end);
+    }
+  };
+
+  auto consume = [&](const uint4& kv4, const uint4& vv4, uint32_t mask) {
+    const uint32_t kw[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+    float x[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d = dot2(qw[t][i], kw[i], d);
+      x[t] = group_sum<LPT>(d) * a.scale_log2;
+    }
+    const uint32_t vw[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+    float vf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vf[2 * i] = bf16_lo(vw[i]);
+      vf[2 * i + 1] = bf16_hi(vw[i]);
+    }
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      if (mask & (1u << t)) {
+        if (x[t] > m[t] + kLazy) {
+          const float al = fast_exp2(m[t] - x[t]);
+          l[t] *= al;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[t][i] *= al;
+          m[t] = x[t];
+        }
+        const float p = fast_exp2(x[t] - m[t]);
+        l[t] += p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[t][i] = fmaf(p, vf[i], acc[t][i]);
+      }
+    }
+  };
+
+  // Software pipeline: kDecUnroll rows per lane group per stage, two register stages.
+  // The loads of the next stage are issued before the current one is consumed, so
+  // every wave keeps K/V loads in flight.  Loads are unconditional (list position
+  // clamped to U-1; out-of-range rows get an empty head mask) so that none of them
+  // waits inside a branch.
+  constexpr int STEP = kDecUnroll * NLG;
+  auto load_stage = [&](int base, uint4 (&kk)[kDecUnroll], uint4 (&vv)[kDecUnroll], uint32_t (&mk)[kDecUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int e = base + u * NLG + lg;
+      uint32_t msk;
+      const int64_t j = token_of(e < U ? e : U - 1, msk);
+      mk[u] = e < U ? msk : 0u;
+      kk[u] = *reinterpret_cast<const uint4*>(kb + j * D);
+      vv[u] = *reinterpret_cast<const uint4*>(vb + j * D);
+    }
+  };
+  if (U > 0) {
+    uint4 ka[kDecUnroll], va[kDecUnroll], kb2[kDecUnroll], vb2[kDecUnroll];
+    uint32_t ma[kDecUnroll], mb[kDecUnroll];
+    load_stage(0, ka, va, ma);
+    for (int base = 0; base < U; base += 2 * STEP) {
+      const bool more_b = base + STEP < U;
+      if (more_b) load_stage(base + STEP, kb2, vb2, mb);
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) consume(ka[u], va[u], ma[u]);
+      if (!more_b) break;
+      if (base + 2 * STEP < U) load_stage(base + 2 * STEP, ka, va, ma);
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) consume(kb2[u], vb2[u], mb[u]);
+    }
+  }
+
+  // ---- merge the lane groups of each wave, then the waves
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    float mw = m[t];
+#pragma unroll
+    for (int o = LPT; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
+    const float f = (m[t] == -INFINITY) ? 0.0f : fast_exp2(m[t] - mw);
+    float lw = l[t] * f;
+#pragma unroll
+    for (int o = LPT; o < 64; o <<= 1) lw += __shfl_xor(lw, o, 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float y = acc[t][i] * f;
+#pragma unroll
+      for (int o = LPT; o < 64; o <<= 1) y += __shfl_xor(y, o, 64);
+      acc[t][i] = y;
+    }
+    if (lane < LPT) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s_wacc[wave][t][li * 8 + i] = acc[t][i];
+      if (lane == 0) {
+        s_wm[wave][t] = mw;
+        s_wl[wave][t] = lw;
+      }
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < G * D; o += kDecThreads) {
+    const int t = o / D, d = o % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_wm[w][t]);
+    float A = 0.0f, Lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = (s_wm[w][t] == -INFINITY) ? 0.0f : fast_exp2(s_wm[w][t] - M);
+      A += s_wacc[w][t][d] * f;
+      Lsum += s_wl[w][t] * f;
+    }
+    float* pr = a.part + ((int64_t(grp) * G + t) * a.nsplit + split) * (D + 2);
+    pr[d] = A;
+    if (d == 0) {
+      pr[D] = M;
+      pr[D + 1] = Lsum;
+    }
+  }
+}
+
+// Combine the per-slice partials of one (batch, head) row into the bf16 output.
+// 256 threads per row: SG = 256/D split groups, each thread sums the splits of its group
+// for one output dimension (independent loads, unrolled), then the groups are combined.
+struct MergeArgs {
+  const float* part;           // [rows][nsplit][D + 2]
+  int nsplit;
+  int G, Hq;
+  HeadMap map;
+  uint16_t* out;               // [B][Hq][D]
+};
+
+template <int D>
+__device__ __forceinline__ void merge_row(const MergeArgs& ma, int row) {
+  const float* __restrict__ part = ma.part;
+  const int nsplit = ma.nsplit, G = ma.G, Hq = ma.Hq;
+  const HeadMap& map = ma.map;
+  uint16_t* __restrict__ out = ma.out;
+  constexpr int SG = 256 / D;
+  const int tid = threadIdx.x;
+  const int d = tid % D, sg = tid / D;
+  const int grp = row / G, t = row % G;
+  const int b = grp / map.n, rr = grp % map.n;
+  const int h = map.kv[rr] * G + t;
+  const float* pr = part + int64_t(row) * nsplit * (D + 2);
+  __shared__ float s_red[4];
+  __shared__ float s_a[SG][D], s_l[SG][D];
+  // reference max over the splits
+  float M = -INFINITY;
+  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, pr[int64_t(s) * (D + 2) + D]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float A = 0.0f, Lsum = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = sg; s < nsplit; s += SG) {
+      const float* ps = pr + int64_t(s) * (D + 2);
+      const float ms = ps[D];
+      const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
+      A = fmaf(ps[d], f, A);
+      Lsum = fmaf(ps[D + 1], f, Lsum);
+    }
+  }
+  s_a[sg][d] = A;
+  s_l[sg][d] = Lsum;
+  __syncthreads();
+  if (sg == 0) {
+#pragma unroll
+    for (int i = 1; i < SG; ++i) {
+      A += s_a[i][d];
+      Lsum += s_l[i][d];
+    }
+    out[(int64_t(b) * Hq + h) * D + d] = f32_to_bf16(Lsum > 0.0f ? A / Lsum : 0.0f);
+  }
+}
+
+}  // namespace

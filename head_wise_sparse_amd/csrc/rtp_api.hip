@@ -86,10 +86,10 @@ size_t score_ws_bytes(const Layer& L, int64_t n_ctx) {
   return round_up(size_t(L.B) * L.n_ret * L.G * nblk * 2 * sizeof(float), 256);
 }
 
-SelLayout sel_layout(const Layer& L, int64_t n_ctx) {
+SelLayout sel_layout(const Layer& L) {
   SelLayout s{};
   const size_t rows = size_t(L.B) * L.n_ret * L.G;
-  s.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
+  s.nblk_max = int((L.n_cap + kSelTile - 1) / kSelTile);
   size_t off = 0;
   s.hist_mass = off;
   off = round_up(off + rows * 3 * kBins * sizeof(uint64_t), 256);
@@ -104,7 +104,7 @@ SelLayout sel_layout(const Layer& L, int64_t n_ctx) {
   s.ctr = off;
   off = round_up(off + rows * 2 * sizeof(uint32_t), 256);
   s.lookback = off;
-  off = round_up(off + rows * size_t(s.nblk) * sizeof(uint64_t), 256);
+  off = round_up(off + rows * size_t(s.nblk_max) * sizeof(uint64_t), 256);
   s.total = off;
   return s;
 }
@@ -141,10 +141,11 @@ extern "C" size_t rtp_workspace_bytes(const rtp_layer_desc* desc, int64_t n_ctx,
   if (check_desc(desc, &L) != RTP_OK || n_ctx < 1) return 0;
   switch (which) {
     case RTP_CALL_INDEXER_SCORE: return score_ws_bytes(L, n_ctx);
-    case RTP_CALL_TOPP_SELECT: return sel_layout(L, n_ctx).total;
+    case RTP_CALL_TOPP_SELECT: return sel_layout(L).total;
     case RTP_CALL_SPARSE_DECODE: return dec_ws_bytes(L, n_ctx, true);
     case RTP_CALL_WINDOW_SINK: return dec_ws_bytes(L, n_ctx, false);
     case RTP_CALL_PREFILL: return prefill_ws_bytes(L, n_ctx);
+    case RTP_CALL_DECODE_STEP: return step_ws_bytes(L, n_ctx);
     default: return 0;
   }
 }

@@ -68,11 +68,11 @@ struct SelRowState {             // one per score row, lives in the workspace
   SelLevelState lvl[2];          // after level 0, after level 1 (written by different launches)
 };
 static_assert(sizeof(SelRowState) == 56, "row state layout");
-struct SelLayout {
+struct SelLayout {                // depends on the layer only (n_cap), not on n_ctx: the
   size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, lookback, total;
-  int nblk;
+  int nblk_max;                   // zero-filled region stays in place while n_ctx grows
 };
-SelLayout sel_layout(const Layer& L, int64_t n_ctx);
+SelLayout sel_layout(const Layer& L);
 struct SelRows {                 // device views of the selection workspace
   uint64_t* mass;                // [rows][3][kBins]
   uint32_t* cnt;                 // [rows][3][kBins]
@@ -84,11 +84,16 @@ struct SelRows {                 // device views of the selection workspace
 };
 struct SelArgs {
   const float* scores;           // [rows][n_cap]
-  const float* row_max;          // [rows]
+  const float* row_max;          // [rows], or null: then from score_part
+  const float2* score_part;      // [rows][score_nblk] per-block (max, sum of exp) of the scoring, or null
+  int score_nblk;
+  float* row_max_out;            // with score_part: row statistics written by the first pass
+  float* row_sum_out;
   float top_p;
   int n_ctx;
   int64_t n_cap;
-  int nblk;                      // selection tiles per row
+  int nblk;                      // selection tiles per row (from n_ctx)
+  int lb_stride;                 // look-back words per row (from n_cap)
   int32_t* sel_idx;
   int32_t* sel_count;
   int32_t* starts;               // [rows][nsplit + 1] range index of the selected lists, or null
@@ -96,6 +101,8 @@ struct SelArgs {
   SelRows R;
 };
 SelRows sel_rows(void* ws, const SelLayout& lay);
+// Enqueue the selection launches for `rows` score rows (top_p < 1 uses the workspace).
+rtp_status launch_select(const SelArgs& a, int rows, hipStream_t s);
 
 // Decode attention (sparse and window share the layout).
 constexpr int kDecThreads = 256;
@@ -107,6 +114,9 @@ size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows
 
 // Prefill.
 size_t prefill_ws_bytes(const Layer& L, int64_t C);
+
+// Fused decode step (selection region first, then scoring / sparse / window regions).
+size_t step_ws_bytes(const Layer& L, int64_t n_ctx);
 
 }  // namespace rtp
 

@@ -15,172 +15,24 @@
 using namespace rtp;
 using namespace rtp_dev;
 
+#include "score_dev.hpp"
+
 namespace {
 
 template <int G, int D>
-__global__ __launch_bounds__(kScoreThreads) void k_indexer_score(
-    const uint16_t* __restrict__ q_pre, const uint16_t* __restrict__ w_q, int64_t w_stride,
-    const uint16_t* __restrict__ k_idx, float idx_scale, float* __restrict__ scores,
-    float2* __restrict__ part, int n_ctx, int64_t n_cap, int Hq, HeadMap map, int nblk) {
-  const int tid = threadIdx.x;
-  const int blk = blockIdx.x;
-  const int grp = blockIdx.y;              // b * n_ret + r
-  const int b = grp / map.n, r = grp % map.n;
-  const int g = map.kv[r];
-
-  // LDS: raw bf16 q_pre rows and projection matrices of the group (padded so that every
-  // lane of a direct-to-LDS load has a slot), the fp32 q_idx vectors, reduction scratch
-  constexpr int QV = G * D / 8;                           // 16-byte pieces of q_pre
-  constexpr int WV = G * D * kIdxDim / 8;                 // 16-byte pieces of the G matrices
-  constexpr int QV_PAD = QV < 64 ? 64 : QV;
-  constexpr int WPT = (WV + kScoreThreads - 1) / kScoreThreads;
-  __shared__ uint4 s_qraw[QV_PAD];
-  __shared__ uint4 s_w[WPT * kScoreThreads];
-  __shared__ float s_qidx[G][kIdxDim];
-  __shared__ float s_red[kScoreThreads / 64][G];
-  typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  typedef __attribute__((address_space(1))) const void* glb_ptr_t;
-  const int wave = tid / 64, lane = tid % 64;
-
-  // ---- every global load of the block is issued up front.  q_pre and W_q_idx go
-  // straight to LDS (global_load_lds_dwordx4: no registers, lane i writes 16 bytes at
-  // the wave's LDS base + 16*i); indices are clamped in range so every lane loads.
-  if (wave * 64 < QV_PAD) {
-    const int pidx = min(wave * 64 + lane, QV - 1);
-    const uint16_t* src = q_pre + (int64_t(b) * Hq + g * G + pidx / (D / 8)) * D + (pidx % (D / 8)) * 8;
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(s_qraw + wave * 64), 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int pidx = min(i * kScoreThreads + tid, WV - 1);
-    const int t = pidx / (D * kIdxDim / 8), off = pidx % (D * kIdxDim / 8);
-    const uint16_t* src = w_q + int64_t(r * G + t) * w_stride + off * 8;
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(s_w + i * kScoreThreads + wave * 64), 16, 0, 0);
-  }
-  // this tile's keys: thread tid takes tokens base + it*256 + tid (coalesced 32-byte rows)
-  const int64_t base = int64_t(blk) * kScoreTile;
-  const uint4* kp = reinterpret_cast<const uint4*>(k_idx + int64_t(grp) * n_cap * kIdxDim);
-  uint4 kr[kScoreItems][2];
-#pragma unroll
-  for (int it = 0; it < kScoreItems; ++it) {
-    int64_t j = base + it * kScoreThreads + tid;
-    j = j < n_ctx ? j : n_ctx - 1;
-    kr[it][0] = kp[2 * j];
-    kr[it][1] = kp[2 * j + 1];
-  }
-  // wait for the LDS-direct loads only: vmcnt retires in issue order, so leaving the
-  // 2*kScoreItems key loads outstanding is vmcnt(2*kScoreItems)
-  static_assert(2 * kScoreItems < 64, "vmcnt field");
-  constexpr int NK = 2 * kScoreItems;
-  __builtin_amdgcn_s_waitcnt((NK & 0xF) | ((NK >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  __builtin_amdgcn_s_barrier();   // a bare barrier: __syncthreads' fence would wait for the key loads too
-
-  // ---- q_idx = q_pre . W_q_idx for the G heads of this group (fp32, not rounded)
-  {
-    constexpr int P = kScoreThreads / (G * kIdxDim);     // threads per output
-    const int o = tid / P, pi = tid % P;
-    const int t = o / kIdxDim, c = o % kIdxDim;
-    const uint16_t* w = reinterpret_cast<const uint16_t*>(s_w) + t * D * kIdxDim;
-    const uint16_t* qr = reinterpret_cast<const uint16_t*>(s_qraw) + t * D;
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D / P; ++i) {
-      const int d = pi + i * P;
-      acc = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(w[d * kIdxDim + c]), acc);
-    }
-#pragma unroll
-    for (int off = P / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (pi == 0) s_qidx[t][c] = acc * idx_scale;
-  }
-  __syncthreads();
-  float qi[G][kIdxDim];
-#pragma unroll
-  for (int t = 0; t < G; ++t)
-#pragma unroll
-    for (int c = 0; c < kIdxDim; ++c) qi[t][c] = s_qidx[t][c];
-
-  // ---- score the tile (keys were loaded before the q_idx prologue)
-  float sc[kScoreItems][G];
-#pragma unroll
-  for (int it = 0; it < kScoreItems; ++it) {
-    const int64_t j = base + it * kScoreThreads + tid;
-    float kf[kIdxDim];
-    const uint32_t w8[8] = {kr[it][0].x, kr[it][0].y, kr[it][0].z, kr[it][0].w,
-                            kr[it][1].x, kr[it][1].y, kr[it][1].z, kr[it][1].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kf[2 * e] = bf16_lo(w8[e]);
-      kf[2 * e + 1] = bf16_hi(w8[e]);
-    }
-#pragma unroll
-    for (int t = 0; t < G; ++t) {
-      float s = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kIdxDim; ++c) s = fmaf(qi[t][c], kf[c], s);
-      sc[it][t] = (j < n_ctx) ? s : -INFINITY;
-      if (j < n_ctx) scores[(int64_t(grp) * G + t) * n_cap + j] = s;
-    }
-  }
-
-  // ---- per-block max and sum of exp for each of the G rows
-  float mt[G];
-#pragma unroll
-  for (int t = 0; t < G; ++t) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int it = 0; it < kScoreItems; ++it) m = fmaxf(m, sc[it][t]);
-    m = wave_max(m);
-    if (lane == 0) s_red[wave][t] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < G; ++t) {
-    float m = s_red[0][t];
-#pragma unroll
-    for (int w = 1; w < kScoreThreads / 64; ++w) m = fmaxf(m, s_red[w][t]);
-    mt[t] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < G; ++t) {
-    float z = 0.0f;
-#pragma unroll
-    for (int it = 0; it < kScoreItems; ++it) z += __expf(sc[it][t] - mt[t]);
-    z = wave_sum(z);
-    if (lane == 0) s_red[wave][t] = z;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float z = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kScoreThreads / 64; ++w) z += s_red[w][tid];
-    part[(int64_t(grp) * G + tid) * nblk + blk] = make_float2(mt[tid], z);
-  }
+__global__ __launch_bounds__(kScoreThreads) void k_indexer_score(ScoreArgs A) {
+  score_block<G, D>(A, blockIdx.x, blockIdx.y);
 }
 
 // One wave per score row: combine the per-block partials into (row_max, row_sum).
 __global__ __launch_bounds__(64) void k_score_finalize(const float2* __restrict__ part, int nblk,
                                                        float* __restrict__ row_max, float* __restrict__ row_sum) {
-  const int row = blockIdx.x, lane = threadIdx.x;
-  const float2* p = part + int64_t(row) * nblk;
-  float m = -INFINITY;
-  for (int i = lane; i < nblk; i += 64) m = fmaxf(m, p[i].x);
-  m = wave_max(m);
-  float z = 0.0f;
-  for (int i = lane; i < nblk; i += 64) z += p[i].y * __expf(p[i].x - m);
-  z = wave_sum(z);
-  if (lane == 0) {
-    row_max[row] = m;
-    row_sum[row] = z;
-  }
+  score_finalize_row(part, nblk, row_max, row_sum, blockIdx.x);
 }
 
 template <int G, int D>
-void launch_score(dim3 grid, hipStream_t st, const uint16_t* q_pre, const uint16_t* w_q, int64_t ws,
-                  const uint16_t* k_idx, float scale, float* scores, float2* part, int n_ctx, int64_t n_cap,
-                  int Hq, const HeadMap& map, int nblk) {
-  hipLaunchKernelGGL((k_indexer_score<G, D>), grid, dim3(kScoreThreads), 0, st, q_pre, w_q, ws, k_idx, scale,
-                     scores, part, n_ctx, n_cap, Hq, map, nblk);
+void launch_score(dim3 grid, hipStream_t st, const ScoreArgs& A) {
+  hipLaunchKernelGGL((k_indexer_score<G, D>), grid, dim3(kScoreThreads), 0, st, A);
 }
 
 }  // namespace
@@ -209,15 +61,13 @@ extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ct
                 ws_bytes);
 
   const int nblk = int((n_ctx + kScoreTile - 1) / kScoreTile);
-  const HeadMap map = ret_map(L);
   const dim3 grid(nblk, L.B * L.n_ret);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws);
-  const int n = int(n_ctx);
-#define RTP_SCORE_CASE(GG, DD)                                                                              \
-  if (L.G == GG && L.D == DD)                                                                               \
-    launch_score<GG, DD>(grid, s, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, n, L.n_cap, \
-                         L.Hq, map, nblk);
+  const ScoreArgs A{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, int(n_ctx), L.n_cap, L.Hq,
+                    ret_map(L), nblk};
+#define RTP_SCORE_CASE(GG, DD) \
+  if (L.G == GG && L.D == DD) launch_score<GG, DD>(grid, s, A);
   RTP_SCORE_CASE(1, 64) RTP_SCORE_CASE(2, 64) RTP_SCORE_CASE(4, 64) RTP_SCORE_CASE(8, 64)
   RTP_SCORE_CASE(1, 128) RTP_SCORE_CASE(2, 128) RTP_SCORE_CASE(4, 128) RTP_SCORE_CASE(8, 128)
 #undef RTP_SCORE_CASE

@@ -33,6 +33,7 @@
 #include <cmath>
 
 #include "rtp_internal.hpp"
+#include "score_dev.hpp"
 
 using namespace rtp;
 using namespace rtp_dev;
@@ -43,6 +44,7 @@ constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr int kCoarse = 64;          // coarse bins of levels 0/1 (32 at level 2)
 constexpr int kFinePer = 32;         // fine bins under one coarse bin
+constexpr int kSpinLimit = 1 << 20;  // bound of a look-back wait (never reached in a valid launch)
 
 __device__ __forceinline__ void st_rlx(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -135,6 +137,22 @@ __device__ __forceinline__ void clear_level(const SelRows& R, int row, int level
   }
 }
 
+// Row max (and, by the first block, the row statistics) from the scoring's per-block
+// (max, sum of exp) partials.
+__device__ float row_max_from_partials(const SelArgs& a, int row, int blk, int tid, float* s_red) {
+  const float2* p = a.score_part + int64_t(row) * a.score_nblk;
+  float m = -INFINITY;
+  for (int i = tid; i < a.score_nblk; i += kSelThreads) m = fmaxf(m, p[i].x);
+  m = wave_max(m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  // the row statistics, by the same one-wave reduction as rtp_indexer_score's
+  if (blk == 0 && a.row_max_out && tid < 64)
+    score_finalize_row(a.score_part, a.score_nblk, a.row_max_out, a.row_sum_out, row);
+  return m;
+}
+
 template <int LEVEL>
 __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   constexpr int NB = LEVEL == 2 ? 1024 : 2048;
@@ -145,6 +163,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   __shared__ uint64_t h_m[NB];
   __shared__ uint32_t h_c[NB];
   __shared__ uint32_t s_prefix;
+  __shared__ float s_red[kSelThreads / 64];
 
   // scores of the tile: unconditional loads (index clamped), validity kept aside
   const float* sp = a.scores + int64_t(row) * a.n_cap;
@@ -161,7 +180,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   }
   float m;
   if constexpr (LEVEL == 0) {
-    m = a.row_max[row];
+    m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red) : a.row_max[row];
     if (blk == 0 && tid == 0) a.R.state[row].ref_max = m;
   } else {
     m = a.R.state[row].ref_max;                      // written by the level-0 launch
@@ -234,13 +253,14 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int row = blockIdx.y;
   constexpr int NW = kSelThreads / 64;
-  __shared__ uint32_t s_tile, s_t, s_r;
+  __shared__ uint32_t s_t, s_r;
   __shared__ uint32_t s_wa[kSelItems][NW], s_we[kSelItems][NW];
   __shared__ uint32_t s_pa, s_pe, s_last;
   uint32_t* ctr = a.R.ctr + 2 * int64_t(row);
-  if (tid == 0) s_tile = atomicAdd(ctr, 1u);          // dynamic tile id: predecessors started
-  __syncthreads();
-  const int tile = int(s_tile);
+  // Static tile ids: a tile waits only for lower-numbered tiles of its row, which the
+  // dispatcher has issued before it (workgroups of a launch start in index order), so
+  // the look-back always ends; its spin count is bounded all the same.
+  const int tile = blockIdx.x;
   const float* sp = a.scores + int64_t(row) * a.n_cap;
   const int64_t base = int64_t(tile) * kSelTile;
   float sv[kSelItems];
@@ -300,13 +320,14 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
         a_ += s_wa[it][w];
         e_ += s_we[it][w];
       }
-    uint64_t* lb = a.R.lookback + int64_t(row) * a.nblk;
+    uint64_t* lb = a.R.lookback + int64_t(row) * a.lb_stride;
     uint64_t pa = 0, pe = 0;
     if (tile == 0) {
       if (lane == 0) st_rlx(lb, kFlagIncl | (uint64_t(a_) << 31) | e_);
     } else {
       if (lane == 0) st_rlx(lb + tile, kFlagAgg | (uint64_t(a_) << 31) | e_);
       int k = tile - 1;                       // lanes inspect tiles k, k-1, ..., k-63
+      int spins = 0;
       while (true) {
         const int idx = k - lane;
         const uint64_t v = (idx >= 0) ? ld_rlx(lb + idx) : kFlagIncl;
@@ -315,7 +336,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
         const uint64_t none = __ballot(f == 0);
         const int first = incl ? __ffsll((unsigned long long)incl) - 1 : 64;
         const uint64_t upto = (first >= 63) ? ~0ull : ((2ull << first) - 1ull);
-        if (none & upto) {                    // a needed predecessor has not published yet
+        if ((none & upto) && ++spins < kSpinLimit) {   // a needed predecessor has not published yet
           __builtin_amdgcn_s_sleep(1);
           continue;
         }
@@ -364,7 +385,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   if (tid == 0) s_last = (atomicAdd(ctr + 1, 1u) == uint32_t(a.nblk - 1));
   __syncthreads();
   if (s_last) {
-    for (int i = tid; i < a.nblk; i += kSelThreads) a.R.lookback[int64_t(row) * a.nblk + i] = 0;
+    for (int i = tid; i < a.nblk; i += kSelThreads) a.R.lookback[int64_t(row) * a.lb_stride + i] = 0;
     uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
     if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
     clear_level(a.R, row, 2, 0, 1);
@@ -417,7 +438,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
     return fail(RTP_EINVAL, "rtp_topp_select: tensors must be 16-byte aligned");
   const int rows = L.B * L.n_ret * L.G;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const SelLayout lay = sel_layout(L, n_ctx);
+  const SelLayout lay = sel_layout(L);
   if (top_p < 1.0f && (!ws || ws_bytes < lay.total || !aligned(ws, 256)))
     return fail(RTP_EWORKSPACE, "rtp_topp_select: workspace needs %zu bytes, 256-aligned (got %zu)", lay.total,
                 ws_bytes);
@@ -433,12 +454,26 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.top_p = top_p;
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
-  a.nblk = lay.nblk;
+  a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
+  a.lb_stride = lay.nblk_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.starts = sel_starts;
   a.nsplit = nsplit;
   a.R = sel_rows(ws, lay);
+  return launch_select(a, rows, s);
+}
+
+namespace rtp {
+
+rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
+  rtp_status st;
+  const SelArgs& a = a0;
+  if (a.top_p >= 1.0f) {
+    hipLaunchKernelGGL(k_sel_all, dim3(unsigned((a.n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, a.n_ctx,
+                       a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
+    return check_launch("k_sel_all");
+  }
   const dim3 grid(a.nblk, rows);
   hipLaunchKernelGGL(k_sel_hist<0>, grid, dim3(kSelThreads), 0, s, a);
   if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
@@ -449,3 +484,5 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   hipLaunchKernelGGL(k_sel_compact, grid, dim3(kSelThreads), 0, s, a);
   return check_launch("k_sel_compact");
 }
+
+}  // namespace rtp

@@ -1,0 +1,245 @@
+// rtp_decode_step: the whole decode step of one layer in one call -- indexer scores,
+// top-p sets, sparse attention of the retrieval heads and sink+window attention of
+// the local heads (abstract, observations (1)-(3); research-map summary, "Approach").
+//
+// It computes exactly what the four calls compute one after the other, with the
+// same kernel bodies, in seven launches instead of thirteen:
+//   1. scoring blocks and the local heads' split-K blocks in one grid: both stream
+//      HBM (indexer keys / sink+window K,V) and do not depend on each other;
+//   2. the first radix pass, which also reduces the scoring partials to the row
+//      statistics (no separate finalize launch);
+//   3-4. the two further radix passes;  5. compaction, which also writes the range
+//      index of every selected list;  6. the retrieval heads' split-K blocks;
+//   7. one merge launch for the split partials of both head kinds.
+#include <cmath>
+
+#include "score_dev.hpp"
+#include "decode_dev.hpp"
+
+namespace {
+
+static_assert(kScoreThreads == kDecThreads, "scoring and decode blocks share one launch");
+
+template <int G, int D>
+__global__ __launch_bounds__(kDecThreads, 4) void k_step_score_window(ScoreArgs sa, int n_score, int score_gx,
+                                                                      DecArgs wa, int win_gx) {
+  const int i = blockIdx.x;
+  if (i < n_score) {
+    score_block<G, D>(sa, i % score_gx, i / score_gx);
+  } else {
+    const int j = i - n_score;
+    decode_block<D, G, false>(wa, j % win_gx, j / win_gx);
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kDecThreads, 4) void k_step_sparse(DecArgs a) {
+  decode_block<D, G, true>(a, blockIdx.x, blockIdx.y);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_step_merge(MergeArgs ms, int rows_s, MergeArgs mw) {
+  const int i = blockIdx.x;
+  if (i < rows_s) merge_row<D>(ms, i);
+  else merge_row<D>(mw, i - rows_s);
+}
+
+__global__ __launch_bounds__(64) void k_step_finalize(const float2* __restrict__ part, int nblk,
+                                                      float* __restrict__ row_max, float* __restrict__ row_sum) {
+  score_finalize_row(part, nblk, row_max, row_sum, blockIdx.x);
+}
+
+struct StepLayout {
+  size_t sel, score, sparse, window, total;
+};
+
+// The selection region comes first and depends on the layer only, so the part of the
+// workspace that must stay zero between calls does not move while n_ctx grows.
+StepLayout step_layout(const Layer& L, int64_t n_ctx) {
+  StepLayout s{};
+  size_t off = 0;
+  s.sel = off;
+  off = round_up(off + (L.n_ret ? sel_layout(L).total : 0), 256);
+  s.score = off;
+  off = round_up(off + (L.n_ret ? score_ws_bytes(L, n_ctx) : 0), 256);
+  s.sparse = off;
+  off = round_up(off + (L.n_ret ? dec_ws_bytes(L, n_ctx, true) : 0), 256);
+  s.window = off;
+  off = round_up(off + (L.n_loc ? dec_ws_bytes(L, n_ctx, false) : 0), 256);
+  s.total = off;
+  return s;
+}
+
+template <int G, int D>
+void launch_score_window(unsigned nblocks, hipStream_t s, const ScoreArgs& sa, int n_score, int score_gx,
+                         const DecArgs& wa, int win_gx) {
+  hipLaunchKernelGGL((k_step_score_window<G, D>), dim3(nblocks), dim3(kDecThreads), 0, s, sa, n_score, score_gx,
+                     wa, win_gx);
+}
+
+rtp_status dispatch_score_window(const Layer& L, unsigned nblocks, hipStream_t s, const ScoreArgs& sa, int n_score,
+                                 int score_gx, const DecArgs& wa, int win_gx) {
+#define RTP_STEP_CASE(GG, DD)                                                 \
+  if (L.G == GG && L.D == DD) {                                               \
+    launch_score_window<GG, DD>(nblocks, s, sa, n_score, score_gx, wa, win_gx); \
+    return check_launch("k_step_score_window");                               \
+  }
+  RTP_STEP_CASE(1, 64) RTP_STEP_CASE(2, 64) RTP_STEP_CASE(4, 64) RTP_STEP_CASE(8, 64)
+  RTP_STEP_CASE(1, 128) RTP_STEP_CASE(2, 128) RTP_STEP_CASE(4, 128) RTP_STEP_CASE(8, 128)
+#undef RTP_STEP_CASE
+  return fail(RTP_EUNSUPPORTED, "rtp_decode_step: unsupported head_dim/group");
+}
+
+rtp_status dispatch_sparse(const Layer& L, dim3 grid, hipStream_t s, const DecArgs& a) {
+#define RTP_STEP_CASE(GG, DD)                                                          \
+  if (L.G == GG && L.D == DD) {                                                        \
+    hipLaunchKernelGGL((k_step_sparse<DD, GG>), grid, dim3(kDecThreads), 0, s, a);     \
+    return check_launch("k_step_sparse");                                              \
+  }
+  RTP_STEP_CASE(1, 64) RTP_STEP_CASE(2, 64) RTP_STEP_CASE(4, 64) RTP_STEP_CASE(8, 64)
+  RTP_STEP_CASE(1, 128) RTP_STEP_CASE(2, 128) RTP_STEP_CASE(4, 128) RTP_STEP_CASE(8, 128)
+#undef RTP_STEP_CASE
+  return fail(RTP_EUNSUPPORTED, "rtp_decode_step: unsupported head_dim/group");
+}
+
+constexpr float kLog2eStep = 1.4426950408889634f;
+
+}  // namespace
+
+namespace rtp {
+size_t step_ws_bytes(const Layer& L, int64_t n_ctx) { return step_layout(L, n_ctx).total; }
+}  // namespace rtp
+
+extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
+                                      const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
+                                      float idx_scale, const uint16_t* q, const uint16_t* k_cache,
+                                      const uint16_t* v_cache, float top_p, float sm_scale, float* scores,
+                                      float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
+                                      int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  Layer L;
+  rtp_status st = check_desc(desc, &L);
+  if (st != RTP_OK) return st;
+  if (n_ctx < 1 || n_ctx > L.n_cap)
+    return fail(RTP_EINVAL, "rtp_decode_step: n_ctx must be in [1, n_cap=%lld] (got %lld)", (long long)L.n_cap,
+                (long long)n_ctx);
+  if (!q || !k_cache || !v_cache || !out) return fail(RTP_EINVAL, "rtp_decode_step: NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 2))
+    return fail(RTP_EINVAL, "rtp_decode_step: q/k/v must be 16-byte aligned");
+  if (!std::isfinite(sm_scale)) return fail(RTP_EINVAL, "rtp_decode_step: sm_scale must be finite");
+  if (L.n_ret) {
+    if (!q_pre || !w_q_idx || !k_idx || !scores || !row_max || !row_sum || !sel_idx || !sel_count)
+      return fail(RTP_EINVAL, "rtp_decode_step: NULL tensor pointer");
+    if (w_head_stride < 0 || w_head_stride % 8 != 0)
+      return fail(RTP_EINVAL, "w_head_stride must be a non-negative multiple of 8 (got %lld)",
+                  (long long)w_head_stride);
+    if (!std::isfinite(idx_scale)) return fail(RTP_EINVAL, "idx_scale must be finite");
+    if (!(top_p > 0.0f)) return fail(RTP_EINVAL, "top_p must be > 0 (got %g)", double(top_p));
+    if (!aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(q_pre, 16) || !aligned(w_q_idx, 16) ||
+        !aligned(sel_idx, 16))
+      return fail(RTP_EINVAL, "rtp_decode_step: tensors must be 16-byte aligned");
+  }
+  const StepLayout lay = step_layout(L, n_ctx);
+  if (!ws || ws_bytes < lay.total || !aligned(ws, 256))
+    return fail(RTP_EWORKSPACE, "rtp_decode_step: workspace needs %zu bytes, 256-aligned (got %zu)", lay.total,
+                ws_bytes);
+  if (!L.n_ret && !L.n_loc) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const int n = int(n_ctx);
+
+  // ---- launch 1: scoring blocks + local heads' split-K blocks
+  ScoreArgs sa{};
+  int n_score = 0, score_gx = 1;
+  if (L.n_ret) {
+    score_gx = int((n_ctx + kScoreTile - 1) / kScoreTile);
+    n_score = score_gx * L.B * L.n_ret;
+    sa = ScoreArgs{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, reinterpret_cast<float2*>(w + lay.score),
+                   n, L.n_cap, L.Hq, ret_map(L), score_gx};
+  }
+  DecArgs wa{};
+  int win_gx = 1, n_win = 0;
+  if (L.n_loc) {
+    const int64_t s_end = std::min<int64_t>(L.n_sinks, n_ctx);
+    const int64_t w_start = std::max<int64_t>(n_ctx - L.window, s_end);
+    const int64_t len = s_end + (n_ctx - w_start);
+    win_gx = int((len + kWinRange - 1) / kWinRange);
+    n_win = win_gx * L.B * L.n_loc;
+    wa.q = q;
+    wa.k = k_cache;
+    wa.v = v_cache;
+    wa.part = reinterpret_cast<float*>(w + lay.window);
+    wa.n_ctx = n;
+    wa.n_cap = L.n_cap;
+    wa.Hq = L.Hq;
+    wa.Hkv = L.Hkv;
+    wa.nsplit = win_gx;
+    wa.scale_log2 = sm_scale * kLog2eStep;
+    wa.s_end = int(s_end);
+    wa.w_start = int(w_start);
+    wa.list_len = int(len);
+    wa.map = loc_map(L);
+  }
+  if ((st = dispatch_score_window(L, unsigned(n_score + n_win), s, sa, n_score, score_gx, wa, win_gx)) != RTP_OK)
+    return st;
+
+  // ---- launches 2-5: top-p sets (the first pass also writes the row statistics)
+  const int nsplit = int((n_ctx + kDecRange - 1) / kDecRange);
+  const int rows_s = L.B * L.n_ret * L.G;
+  int32_t* starts = sel_starts;
+  if (L.n_ret) {
+    if (!starts) starts = reinterpret_cast<int32_t*>(w + lay.sparse + dec_sparse_starts_offset(L, n_ctx));
+    const SelLayout sl = sel_layout(L);
+    SelArgs a{};
+    a.scores = scores;
+    a.row_max = nullptr;
+    a.score_part = sa.part;
+    a.score_nblk = score_gx;
+    a.row_max_out = row_max;
+    a.row_sum_out = row_sum;
+    a.top_p = top_p;
+    a.n_ctx = n;
+    a.n_cap = L.n_cap;
+    a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
+    a.lb_stride = sl.nblk_max;
+    a.sel_idx = sel_idx;
+    a.sel_count = sel_count;
+    a.starts = starts;
+    a.nsplit = nsplit;
+    a.R = sel_rows(w + lay.sel, sl);
+    if (top_p >= 1.0f) {           // no radix pass runs: reduce the partials here
+      hipLaunchKernelGGL(k_step_finalize, dim3(rows_s), dim3(64), 0, s, sa.part, score_gx, row_max, row_sum);
+      if ((st = check_launch("k_step_finalize")) != RTP_OK) return st;
+    }
+    if ((st = launch_select(a, rows_s, s)) != RTP_OK) return st;
+
+    // ---- launch 6: retrieval heads' split-K blocks over the union of each group's sets
+    DecArgs da{};
+    da.q = q;
+    da.k = k_cache;
+    da.v = v_cache;
+    da.sel_idx = sel_idx;
+    da.starts = starts;
+    da.part = reinterpret_cast<float*>(w + lay.sparse);
+    da.n_ctx = n;
+    da.n_cap = L.n_cap;
+    da.Hq = L.Hq;
+    da.Hkv = L.Hkv;
+    da.nsplit = nsplit;
+    da.scale_log2 = sm_scale * kLog2eStep;
+    da.map = ret_map(L);
+    if ((st = dispatch_sparse(L, dim3(nsplit, L.B * L.n_ret), s, da)) != RTP_OK) return st;
+  }
+
+  // ---- launch 7: merge the split partials of both head kinds
+  const int rows_w = L.B * L.n_loc * L.G;
+  const MergeArgs ms{reinterpret_cast<const float*>(w + lay.sparse), nsplit, L.G, L.Hq, ret_map(L), out};
+  const MergeArgs mw{reinterpret_cast<const float*>(w + lay.window), win_gx, L.G, L.Hq, loc_map(L), out};
+  const unsigned mrows = unsigned((L.n_ret ? rows_s : 0) + (L.n_loc ? rows_w : 0));
+  const int rs = L.n_ret ? rows_s : 0;
+  if (L.D == 128)
+    hipLaunchKernelGGL(k_step_merge<128>, dim3(mrows), dim3(256), 0, s, ms, rs, mw);
+  else
+    hipLaunchKernelGGL(k_step_merge<64>, dim3(mrows), dim3(256), 0, s, ms, rs, mw);
+  return check_launch("k_step_merge");
+}

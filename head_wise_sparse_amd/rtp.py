@@ -19,11 +19,12 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "librtp.so")
 
 RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EDEVICE = range(5)
-CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK, CALL_PREFILL = range(5)
+CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK, CALL_PREFILL, CALL_DECODE_STEP = range(6)
 SEL_RANGE = 1024          # RTP_SEL_RANGE: token range of one entry of a selected-set range index
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
-            "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_status_string", "rtp_last_error", "rtp_version"]
+            "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_status_string", "rtp_last_error",
+            "rtp_version"]
 
 
 class RtpError(RuntimeError):
@@ -62,6 +63,8 @@ def load() -> C.CDLL:
         "rtp_window_sink_attn": (C.c_int, [D, C.c_int64, _P, _P, _P, C.c_float, _P, _P, C.c_size_t, _P]),
         "rtp_prefill_attn": (C.c_int, [D, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, C.c_int64, _P, C.c_float,
                                        _P, _P, C.c_size_t, _P]),
+        "rtp_decode_step": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, C.c_float,
+                                      C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_status_string": (C.c_char_p, [C.c_int]),
         "rtp_last_error": (C.c_char_p, []),
         "rtp_version": (C.c_char_p, []),
@@ -191,6 +194,16 @@ def rtp_prefill_attn(layer: Layer, c0: int, C_rows: int, q, k_cache, v_cache, k_
                                    float(sm_scale), _ptr(out), p, n, _stream(stream)))
 
 
+def rtp_decode_step(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_stride: int, k_idx, idx_scale: float, q,
+                    k_cache, v_cache, top_p: float, sm_scale: float, scores, row_max, row_sum, sel_idx, sel_count,
+                    sel_starts, out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(load().rtp_decode_step(layer.desc, int(n_ctx), _ptr(q_pre), _ptr(w_q_idx), int(w_head_stride),
+                                  _ptr(k_idx), float(idx_scale), _ptr(q), _ptr(k_cache), _ptr(v_cache), float(top_p),
+                                  float(sm_scale), _ptr(scores), _ptr(row_max), _ptr(row_sum), _ptr(sel_idx),
+                                  _ptr(sel_count), _ptr(sel_starts), _ptr(out), p, n, _stream(stream)))
+
+
 def rtp_version() -> str:
     return load().rtp_version().decode()
 
@@ -209,19 +222,20 @@ def from_device_bf16(t) -> np.ndarray:
 
 
 class DecodeStep:
-    """One decode step of one layer through the four decode calls, with every output
-    and workspace allocated once.  ``run`` enqueues, on one stream: indexer scores ->
-    top-p sets (with their range index) -> sparse attention of the retrieval heads ->
-    sink+window attention of the local heads (the two write disjoint rows of ``out``)."""
+    """One decode step of one layer, with every output and workspace allocated once.
+    ``run`` enqueues, on one stream, either the fused call (``rtp_decode_step``, the
+    default) or the four separate calls: indexer scores -> top-p sets (with their range
+    index) -> sparse attention of the retrieval heads, and sink+window attention of the
+    local heads.  Both give the same bits."""
 
     def __init__(self, layer: Layer, n_ctx: int, top_p: float, sm_scale: Optional[float] = None,
-                 idx_scale: float = 1.0, device="cuda"):
+                 idx_scale: float = 1.0, device="cuda", fused: bool = True):
         import torch
-        self.layer, self.n_ctx, self.top_p = layer, int(n_ctx), float(top_p)
+        self.layer, self.n_ctx, self.top_p, self.fused = layer, int(n_ctx), float(top_p), bool(fused)
         self.sm_scale = (1.0 / layer.head_dim ** 0.5) if sm_scale is None else float(sm_scale)
         self.idx_scale = float(idx_scale)
         B, R, cap = layer.batch, layer.n_q_r, layer.n_cap
-        nsplit = (self.n_ctx + SEL_RANGE - 1) // SEL_RANGE
+        nsplit = (cap + SEL_RANGE - 1) // SEL_RANGE
         self.scores = torch.empty(B * R * cap, dtype=torch.float32, device=device)
         self.row_max = torch.empty(B * R, dtype=torch.float32, device=device)
         self.row_sum = torch.empty(B * R, dtype=torch.float32, device=device)
@@ -229,13 +243,22 @@ class DecodeStep:
         self.sel_count = torch.empty(B * R, dtype=torch.int32, device=device)
         self.sel_starts = torch.empty(B * R * (nsplit + 1), dtype=torch.int32, device=device)
         self.out = torch.zeros(B * layer.n_q_heads * layer.head_dim, dtype=torch.bfloat16, device=device)
-        self.ws = {w: workspace(layer, n_ctx, w, device) for w in
-                   (CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK)}
+        which = (CALL_DECODE_STEP,) if self.fused else (CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE,
+                                                         CALL_WINDOW_SINK)
+        # sized for the full capacity, so one step object serves any n_ctx <= n_cap
+        self.ws = {w: workspace(layer, cap, w, device) for w in which}
 
-    def run(self, q_pre, q, k_cache, v_cache, k_idx, w_q_idx, w_head_stride: Optional[int] = None, stream=None):
-        L, n = self.layer, self.n_ctx
+    def run(self, q_pre, q, k_cache, v_cache, k_idx, w_q_idx, w_head_stride: Optional[int] = None, stream=None,
+            n_ctx: Optional[int] = None):
+        L = self.layer
+        n = self.n_ctx if n_ctx is None else int(n_ctx)
         if w_head_stride is None:
             w_head_stride = L.head_dim * L.idx_dim
+        if self.fused:
+            rtp_decode_step(L, n, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, q, k_cache, v_cache,
+                            self.top_p, self.sm_scale, self.scores, self.row_max, self.row_sum, self.sel_idx,
+                            self.sel_count, self.sel_starts, self.out, self.ws[CALL_DECODE_STEP], stream)
+            return self.out
         rtp_indexer_score(L, n, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, self.scores, self.row_max,
                           self.row_sum, self.ws[CALL_INDEXER_SCORE], stream)
         rtp_topp_select(L, n, self.scores, self.row_max, self.row_sum, self.top_p, self.sel_idx, self.sel_count,

@@ -23,12 +23,15 @@
  *    IEEE bfloat16 raw bits (uint16_t); results are rounded to nearest even.
  *  - Ownership: the library allocates nothing.  Scratch space comes from the
  *    caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned); size it with
- *    rtp_workspace_bytes().  A workspace must be ZERO-FILLED before its first use:
- *    some calls keep counters and histograms in it that their kernels reset
- *    themselves, so every call that completes leaves the workspace zero-filled
- *    again.  A workspace may be reused by later calls on the same stream (of any
- *    call kind and size); calls that run concurrently need distinct workspaces.
- *    After a device fault, zero-fill it again before reuse.
+ *    rtp_workspace_bytes().  rtp_topp_select and rtp_decode_step keep radix
+ *    histograms, counters and look-back words in their workspace that their
+ *    kernels reset themselves: such a workspace must be ZERO-FILLED before its
+ *    first use, every call that completes leaves that region zero again, and it
+ *    must not be handed to another kind of call in between.  The region depends
+ *    on the descriptor only (not on n_ctx), so one workspace serves a growing
+ *    context.  The other calls need no particular content.  A workspace may be
+ *    reused by later calls on the same stream; calls that run concurrently need
+ *    distinct workspaces.  After a device fault, zero-fill it again before reuse.
  *  - Errors: every argument is validated on the host before anything is
  *    enqueued.  On error nothing is launched and no output is touched; the
  *    status is returned and rtp_last_error() (thread-local) explains it.
@@ -83,7 +86,8 @@ typedef enum rtp_call {
   RTP_CALL_TOPP_SELECT = 1,
   RTP_CALL_SPARSE_DECODE = 2,
   RTP_CALL_WINDOW_SINK = 3,
-  RTP_CALL_PREFILL = 4
+  RTP_CALL_PREFILL = 4,
+  RTP_CALL_DECODE_STEP = 5
 } rtp_call;
 
 /* Workspace bytes that call `which` needs for this layer at context n_ctx
@@ -204,6 +208,36 @@ rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, int32_t C,
                             const uint16_t* k_pre, const uint16_t* w_k_idx, int64_t w_head_stride,
                             uint16_t* k_idx_cache, float sm_scale, uint16_t* out,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_decode_step -- one whole decode step of a layer in one call: exactly
+ *   rtp_indexer_score -> rtp_topp_select -> rtp_sparse_decode_attn, and
+ *   rtp_window_sink_attn, with the same arguments and the same results bit for
+ *   bit (abstract, observations (1)-(3); summary, "Approach").
+ * It enqueues seven launches instead of thirteen: the local heads' attention
+ * runs in the same launch as the indexer scoring, the first radix pass also
+ * reduces the row statistics, and one merge launch serves both head kinds.
+ *
+ *   q_pre, w_q_idx, w_head_stride, k_idx, idx_scale   as rtp_indexer_score
+ *   q, k_cache, v_cache, sm_scale                     as the decode calls
+ *   top_p                                             as rtp_topp_select
+ *   scores, row_max, row_sum, sel_idx, sel_count      outputs, as the separate calls
+ *   sel_starts   optional output (NULL: kept in the workspace)
+ *   out          bf16 [B][Hq][D]: every head's row is written
+ * Pointers of the retrieval-head path may be NULL when the layer has no
+ * retrieval head.  Workspace: rtp_workspace_bytes(desc, n_ctx,
+ * RTP_CALL_DECODE_STEP), zero-filled before the first call (see the
+ * conventions above); its selection region sits first and depends only on the
+ * descriptor, so the same workspace serves every n_ctx <= n_cap of the layer.
+ */
+rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
+                           const uint16_t* q_pre, const uint16_t* w_q_idx, int64_t w_head_stride,
+                           const uint16_t* k_idx, float idx_scale,
+                           const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                           float top_p, float sm_scale,
+                           float* scores, float* row_max, float* row_sum,
+                           int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts,
+                           uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* rtp_status_string(rtp_status s);

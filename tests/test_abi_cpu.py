@@ -55,13 +55,38 @@ def _layer(**kw):
 
 def test_workspace_sizes():
     L = _layer()
-    for w in range(5):
+    for w in range(6):
         assert rtp.rtp_workspace_bytes(L, 131072 if w != 4 else 4096, w) > 0
+    # the selection region does not depend on n_ctx; the fused step holds it first
+    assert rtp.rtp_workspace_bytes(L, 1000, rtp.CALL_TOPP_SELECT) == \
+        rtp.rtp_workspace_bytes(L, 131072, rtp.CALL_TOPP_SELECT)
+    assert rtp.rtp_workspace_bytes(L, 131072, rtp.CALL_DECODE_STEP) >= \
+        rtp.rtp_workspace_bytes(L, 131072, rtp.CALL_TOPP_SELECT) + rtp.rtp_workspace_bytes(L, 131072, 0)
     # selection workspace: 3 histogram levels of 2048 (u64 mass + u32 count) per row
     assert rtp.rtp_workspace_bytes(L, 131072, rtp.CALL_TOPP_SELECT) >= 32 * 3 * 2048 * 12
     assert rtp.rtp_workspace_bytes(_layer(head_dim=96), 1000, 0) == 0          # invalid descriptor
     assert rtp.rtp_workspace_bytes(L, 0, 0) == 0
     assert rtp.rtp_workspace_bytes(L, 10, 9) == 0
+
+
+def _call_step(L, n_ctx=1000, ws_bytes=1 << 30, top_p=0.9, sm=0.1, ptr=FAKE, ws=FAKE):
+    lib = _lib()
+    return lib.rtp_decode_step(L.desc, n_ctx, ptr, ptr, 0, ptr, 1.0, ptr, ptr, ptr, top_p, sm, ptr, ptr, ptr, ptr,
+                               ptr, None, ptr, ws, ws_bytes, None)
+
+
+def test_decode_step_validation():
+    L = _layer()
+    assert _call_step(L, n_ctx=0) == rtp.RTP_EINVAL
+    assert _call_step(L, n_ctx=L.n_cap + 1) == rtp.RTP_EINVAL
+    for p in (0.0, -1.0, math.nan):
+        assert _call_step(L, top_p=p) == rtp.RTP_EINVAL
+    assert _call_step(L, sm=math.inf) == rtp.RTP_EINVAL
+    assert _call_step(L, ptr=None) == rtp.RTP_EINVAL
+    assert _call_step(L, ptr=FAKE + 4) == rtp.RTP_EINVAL
+    assert _call_step(L, ws_bytes=1024) == rtp.RTP_EWORKSPACE
+    assert _call_step(L, ws=FAKE + 16) == rtp.RTP_EWORKSPACE
+    assert "workspace" in _lib().rtp_last_error().decode()
 
 
 def _call_score(L, n_ctx=1000, ws_bytes=1 << 20, scale=1.0, ptr=FAKE):

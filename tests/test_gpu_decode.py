@@ -388,3 +388,92 @@ def test_decode_step_graph_replay_matches_eager():
             assert torch.equal(u.view(torch.uint8), v.view(torch.uint8)), f"replay {rep}"
         step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)      # eager work between replays
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- fused step
+def _step_outputs(step, B, R, n):
+    nsplit = (n + rtp.SEL_RANGE - 1) // rtp.SEL_RANGE
+    cnt = step.sel_count.view(B, R).cpu().numpy()
+    sel = step.sel_idx.view(B, R, -1).cpu().numpy()
+    cap = sel.shape[2]
+    sc = step.scores.view(B, R, cap)[:, :, :n].cpu().numpy()
+    st = step.sel_starts[:B * R * (nsplit + 1)].view(B, R, nsplit + 1).cpu().numpy()
+    sets = [sel[b, c, :cnt[b, c]].copy() for b in range(B) for c in range(R)]
+    return dict(out=rtp.from_device_bf16(step.out), scores=sc, row_max=step.row_max.cpu().numpy(),
+                row_sum=step.row_sum.cpu().numpy(), cnt=cnt, sets=sets, starts=st)
+
+
+def _assert_same(a, b, what):
+    for k in ("out", "scores", "row_max", "row_sum", "cnt", "starts"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), f"{what}: {k} differs"
+    assert all(np.array_equal(x, y) for x, y in zip(a["sets"], b["sets"])), f"{what}: sets differ"
+
+
+@pytest.mark.parametrize("name,p,over", [("decode_tiny_2k", 0.9, {}), ("decode_b8_32k", 0.95, dict(batch=2, n_ctx=9000)),
+                                         ("decode_b8_32k", 1.0, dict(batch=1, n_ctx=5000)),
+                                         ("decode_b4_128k", 0.99, dict(batch=1))])
+def test_fused_step_matches_separate_calls(name, p, over):
+    """rtp_decode_step gives the same bits as the four calls one after the other."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs(name, **over)
+    cfg = x.cfg
+    L = P.layer_for(cfg)
+    B, R = cfg.batch, cfg.n_kv_r * cfg.group
+    res = []
+    for fused in (False, True):
+        step = rtp.DecodeStep(L, cfg.n_ctx, p, fused=fused)
+        step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+        torch.cuda.synchronize()
+        res.append(_step_outputs(step, B, R, cfg.n_ctx))
+        if fused:
+            assert not step.ws[rtp.CALL_DECODE_STEP][:rtp.rtp_workspace_bytes(L, cfg.n_ctx, rtp.CALL_TOPP_SELECT)] \
+                .any().item(), "the selection region must be left zero-filled"
+    _assert_same(res[0], res[1], name)
+
+
+def test_fused_step_growing_context_one_workspace():
+    """One fused step object (one workspace) over a growing context: every step equals a
+    fresh run of the separate calls at that length."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=2, n_ctx=12000)
+    cfg = x.cfg
+    L = P.layer_for(cfg)
+    B, R = cfg.batch, cfg.n_kv_r * cfg.group
+    fused = rtp.DecodeStep(L, cfg.n_ctx, 0.95, fused=True)
+    for n in (4095, 4096, 4097, 8192 + 5, 12000, 3000):
+        fused.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx, n_ctx=n)
+        torch.cuda.synchronize()
+        a = _step_outputs(fused, B, R, n)
+        ref = rtp.DecodeStep(L, n, 0.95, fused=False)
+        ref.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx, n_ctx=n)
+        torch.cuda.synchronize()
+        _assert_same(_step_outputs(ref, B, R, n), a, f"n_ctx={n}")
+
+
+@pytest.mark.parametrize("roles", ["all_local", "all_retrieval"])
+def test_fused_step_single_head_kind(roles):
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=1, n_ctx=6000)
+    cfg = x.cfg
+    role = [0] * cfg.n_kv_heads if roles == "all_local" else [1] * cfg.n_kv_heads
+    L = rtp.Layer(1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx, role, cfg.n_sinks, cfg.window)
+    kidx = d.k_idx if roles == "all_local" else torch.zeros(cfg.n_kv_heads * cfg.n_ctx * 16, dtype=torch.bfloat16,
+                                                             device="cuda")
+    wq = d.w_q_idx                    # all retrieval: stride 0, every head reads the first matrix
+    outs = []
+    for fused in (False, True):
+        step = rtp.DecodeStep(L, cfg.n_ctx, 0.9, fused=fused)
+        step.run(d.q_pre, d.q, d.k, d.v, kidx, wq, w_head_stride=0 if roles == "all_retrieval" else None)
+        torch.cuda.synchronize()
+        outs.append(rtp.from_device_bf16(step.out))
+    assert np.array_equal(outs[0], outs[1])
+    if roles == "all_local":
+        lset = O.local_set(cfg.n_ctx, cfg.n_sinks, cfg.window)
+        g = outs[1].reshape(cfg.n_q_heads, cfg.head_dim)
+        ref = np.stack([O.attend(O.bf16_to_f64(x.q[0, h]), O.bf16_to_f64(x.k[0, h // cfg.group, :cfg.n_ctx]),
+                                 O.bf16_to_f64(x.v[0, h // cfg.group, :cfg.n_ctx]), lset, 1 / math.sqrt(128))
+                        for h in range(cfg.n_q_heads)])
+        P.check_outputs(g, ref, "all-local fused step")
