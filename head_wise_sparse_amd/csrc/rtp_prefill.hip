@@ -160,18 +160,6 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
   constexpr int KCH = BN * PD / 8;                            // 16-byte chunks per tile
   constexpr int KLD = KCH / kPreThreads;                      // copies per thread per tile (K and V each)
   constexpr int NWV = kPreThreads / 64;
-  auto load_tile = [&](int kt, int buf) {
-    const int64_t k0 = int64_t(kt) * BN;
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int base = (i * NWV + wave) * 64;
-      const int p = base + lane;
-      const int row = p >> 4, ck = (p & 15) ^ (row & 15), cv = (p & 15) ^ ((row & 3) << 2);
-      const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
-      g2lds_16(kbase + kr * PD + ck * 8, lds_addr(&s_k[buf][base * 8]));
-      g2lds_16(vbase + kr * PD + cv * 8, lds_addr(&s_v[buf][base * 8]));
-    }
-  };
   // V^T operand addresses.  ds_read_b64_tr_b16: within each 16-lane group, lane r names a
   // row of 4 bf16 and lane 4j+i receives element i of the rows named by lanes j, j+4, j+8,
   // j+12.  Lane r names V[key0 + r/4][d0 + 4*(r%4)], so lane l receives dims d0 + l%16 of
@@ -198,30 +186,24 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
     for (int db = 0; db < PD / 32; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[rb][db][v] = 0.0f;
+  // Running reference max (log2 domain) starts finite: a row that has seen no visible
+  // key yet gets exp2(-inf - m) = 0 everywhere and its first real max rescales by 0.
+  constexpr float kNoMax = -1.0e30f;
   float m_run[RB], l_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
+    m_run[rb] = kNoMax;
     l_run[rb] = 0.0f;
   }
 
-  load_tile(tile_of(0), 0);
-  wait_vm0();
-  __syncthreads();
-  for (int n = 0; n < n_tiles; ++n) {
-    const int buf = n & 1;
-    const int kt = tile_of(n);
-    const int64_t k0 = int64_t(kt) * BN;
-    if (n + 1 < n_tiles) load_tile(tile_of(n + 1), buf ^ 1);
-
-    // S^T = K Q^T for both row blocks; each K operand read from LDS serves both
-    f32x16 sacc[RB][2];
+  // S^T = K Q^T of one key tile; each K operand read from LDS serves every row block
+  auto qk = [&](int buf, f32x16 (&sa)[RB][2]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[rb][kb][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) sa[rb][kb][v] = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -229,41 +211,89 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
         const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][swz_k(kb * 32 + l32, 2 * ds + hf)]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[rb][ds], sacc[rb][kb], 0, 0, 0);
+          sa[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[rb][ds], sa[rb][kb], 0, 0, 0);
       }
+  };
+
+  // Pipeline: K runs one tile ahead of V.  Iteration n holds S(n) in registers, issues
+  // the copies of K(n+2) and V(n+1), computes S(n+1) = K(n+1) Q^T on the MFMA pipe
+  // while the softmax of S(n) runs on the VALU, then O^T += V(n)^T P(n)^T.
+  f32x16 sacc[RB][2], snext[RB][2];
+  auto load_k = [&](int kt, int buf) {
+    const int64_t k0 = int64_t(kt) * BN;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int base = (i * NWV + wave) * 64;
+      const int p = base + lane;
+      const int row = p >> 4, ck = (p & 15) ^ (row & 15);
+      const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
+      g2lds_16(kbase + kr * PD + ck * 8, lds_addr(&s_k[buf][base * 8]));
+    }
+  };
+  auto load_v = [&](int kt, int buf) {
+    const int64_t k0 = int64_t(kt) * BN;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int base = (i * NWV + wave) * 64;
+      const int p = base + lane;
+      const int row = p >> 4, cv = (p & 15) ^ ((row & 3) << 2);
+      const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
+      g2lds_16(vbase + kr * PD + cv * 8, lds_addr(&s_v[buf][base * 8]));
+    }
+  };
+  load_k(tile_of(0), 0);
+  load_v(tile_of(0), 0);
+  if (n_tiles > 1) load_k(tile_of(1), 1);
+  wait_vm0();
+  __syncthreads();
+  qk(0, sacc);
+  __syncthreads();              // K(0) is consumed: its buffer takes K(2)
+
+  for (int n = 0; n < n_tiles; ++n) {
+    const int kt = tile_of(n);
+    const int k0 = kt * BN;
+    if (n + 2 < n_tiles) load_k(tile_of(n + 2), n & 1);
+    if (n + 1 < n_tiles) load_v(tile_of(n + 1), (n + 1) & 1);
+    if (n + 1 < n_tiles) qk((n + 1) & 1, snext);
 
     // masks apply only where some (row, key) pair of the tile is invisible
     bool full;
     if (retr) {
-      full = (k0 + BN - 1 <= R0);
+      full = (int64_t(k0) + BN - 1 <= R0);
     } else {
-      full = (k0 + BN - 1 <= R0) && (k0 >= Rl - a.window + 1 || k0 + BN - 1 < a.n_sinks);
+      full = (int64_t(k0) + BN - 1 <= R0) && (int64_t(k0) >= Rl - a.window + 1 || k0 + BN - 1 < a.n_sinks);
+    }
+    if (!full) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rrel = int(my_row[rb] - k0);            // row relative to the tile's first key
+        const int sink_lim = a.n_sinks - k0;              // keys below this index are sinks
+        const int wlo = rrel - a.window;                  // window keys are > wlo
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kr = kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+            const bool vis = (kr <= rrel) && (retr || kr < sink_lim || kr > wlo);
+            sacc[rb][kb][v] = vis ? sacc[rb][kb][v] : -INFINITY;
+          }
+      }
     }
     uint32_t pk[RB][2][8];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // row max on the raw scores (the scale is positive), masked entries -inf
+      // row max on the raw scores (the scale is positive)
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[rb][kb][v];
-          if (!full) {
-            const int64_t key = k0 + kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-            bool vis = key <= my_row[rb];
-            if (!retr) vis = vis && (key < a.n_sinks || key > my_row[rb] - a.window);
-            x = vis ? x : -INFINITY;
-            sacc[rb][kb][v] = x;
-          }
-          tmax = fmaxf(tmax, x);
-        }
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[rb][kb][v]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;   // both halves hold the same row
       // lazy reference max (log2 domain): move it only when the row max grows past 2^8
       const bool grow = tmax > m_run[rb] + 8.0f;
       if (__ballot(grow)) {
         const float m_new = grow ? tmax : m_run[rb];
-        const float alpha = (m_run[rb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < PD / 32; ++db)
@@ -271,15 +301,14 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
           for (int v = 0; v < 16; ++v) oacc[rb][db][v] *= alpha;
         m_run[rb] = m_new;
       }
-      const bool live = m_run[rb] != -INFINITY;
       const float nm = -m_run[rb];
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
-          const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v], a.scale_log2, nm)) : 0.0f;
-          const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v + 1], a.scale_log2, nm)) : 0.0f;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v], a.scale_log2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v + 1], a.scale_log2, nm));
           pk[rb][kb][v >> 1] = pack_bf16x2(p0, p1);
           // row sum of the bf16 probabilities the PV product uses (one dot2 per pair)
           psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[rb][kb][v >> 1]),
@@ -288,13 +317,14 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
       l_run[rb] += psum;
     }
 
-    // O^T += V^T P^T: each V^T operand read from LDS serves both row blocks
+    // O^T += V^T P^T: each V^T operand read from LDS serves every row block
+    const int vbuf = n & 1;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb = ks >> 1, half = ks & 1;
 #pragma unroll
       for (int db = 0; db < PD / 32; ++db) {
-        const bf16x8_t vv = vt_operand(buf, db, ks);
+        const bf16x8_t vv = vt_operand(vbuf, db, ks);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint4 pb = make_uint4(pk[rb][kb][4 * half], pk[rb][kb][4 * half + 1], pk[rb][kb][4 * half + 2],
@@ -303,8 +333,12 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
         }
       }
     }
-    wait_vm0();                 // this wave's copies of the next tile have landed
-    __syncthreads();            // ... and everyone's; the current buffer is free again
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[rb][kb] = snext[rb][kb];
+    wait_vm0();                 // this wave's copies of K(n+2) and V(n+1) have landed
+    __syncthreads();            // ... and everyone's; K(n+1) and V(n) buffers are free again
   }
 
   // ---- normalise and store: lane holds row my_row[rb], dims db*32 + 8*(v/4) + 4*hf + (v%4)
