@@ -90,6 +90,8 @@ struct SelArgs {
   float* row_max_out;            // with score_part: row statistics written by the first pass
   float* row_sum_out;
   float top_p;
+  int by_count;                  // static top-k: bins weigh their token counts, the target is k_target
+  int64_t k_target;
   int n_ctx;
   int64_t n_cap;
   int nblk;                      // selection tiles per row (from n_ctx)

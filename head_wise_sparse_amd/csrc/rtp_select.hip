@@ -78,19 +78,25 @@ struct Resolved {            // result of resolving one level's digit
 
 // Resolve the digit of `level` from the finished histogram of that level.  Called by
 // one full wave; every lane returns the same result.  `in` carries the state after
-// the previous level (ignored for level 0, where the target is ceil(p * Z)).
+// the previous level (ignored for level 0, where the target is ceil(p * Z), or k when
+// the bins are weighed by their counts for the static top-k rule).
 __device__ Resolved resolve_level(const SelRows& R, int row, int level, const Resolved& in, float top_p,
-                                  int lane) {
+                                  bool by_count, int64_t k_target, int lane) {
   const int nc = level == 2 ? 32 : kCoarse;
   const uint64_t* cm = R.cmass + (int64_t(row) * 3 + level) * kCoarse;
   const uint32_t* cc = R.ccnt + (int64_t(row) * 3 + level) * kCoarse;
-  const uint64_t m_l = lane < nc ? ld_rlx(cm + lane) : 0ull;
   const uint32_t c_l = lane < nc ? ld_rlx(cc + lane) : 0u;
+  const uint64_t m_l = by_count ? uint64_t(c_l) : (lane < nc ? ld_rlx(cm + lane) : 0ull);
   Resolved o = in;
   if (level == 0) {
     const uint64_t z = wave_sum<uint64_t>(m_l);
-    const double tgt = ceil(double(top_p) * double(z));
-    uint64_t t = tgt < 1.0 ? 1ull : (uint64_t)tgt;
+    uint64_t t;
+    if (by_count) {
+      t = uint64_t(k_target);
+    } else {
+      const double tgt = ceil(double(top_p) * double(z));
+      t = tgt < 1.0 ? 1ull : (uint64_t)tgt;
+    }
     o.target = t > z ? z : t;
     o.above = 0;
     o.cnt_above = 0;
@@ -108,8 +114,8 @@ __device__ Resolved resolve_level(const SelRows& R, int row, int level, const Re
   // fine bins under the chosen coarse bin
   const uint64_t* fm = R.mass + (int64_t(row) * 3 + level) * kBins + cs * kFinePer;
   const uint32_t* fc = R.cnt + (int64_t(row) * 3 + level) * kBins + cs * kFinePer;
-  const uint64_t fm_l = lane < kFinePer ? ld_rlx(fm + lane) : 0ull;
   const uint32_t fc_l = lane < kFinePer ? ld_rlx(fc + lane) : 0u;
+  const uint64_t fm_l = by_count ? uint64_t(fc_l) : (lane < kFinePer ? ld_rlx(fm + lane) : 0ull);
   const uint64_t FS = wave_suffix_incl<uint64_t>(fm_l, lane);
   const uint32_t FSC = wave_suffix_incl<uint32_t>(fc_l, lane);
   const uint64_t fown = __ballot(lane < kFinePer && FS >= need && FS - fm_l < need);
@@ -178,9 +184,9 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
     h_m[i] = 0;
     h_c[i] = 0;
   }
-  float m;
+  float m = 0.0f;                                   // unused by the static top-k rule
   if constexpr (LEVEL == 0) {
-    m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red) : a.row_max[row];
+    if (!a.by_count) m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red) : a.row_max[row];
     if (blk == 0 && tid == 0) a.R.state[row].ref_max = m;
   } else {
     m = a.R.state[row].ref_max;                      // written by the level-0 launch
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
       in.cnt_above = ls.cnt_above;
       in.target = ls.target;
     }
-    const Resolved o = resolve_level(a.R, row, LEVEL - 1, in, a.top_p, lane);
+    const Resolved o = resolve_level(a.R, row, LEVEL - 1, in, a.top_p, a.by_count, a.k_target, lane);
     if (lane == 0) {
       s_prefix = o.prefix;
       if (blk == 0) {          // one block publishes; this launch's blocks read only lvl[LEVEL-2]
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
     const bool match = (j < a.n_ctx) && (LEVEL == 0 || (key >> PSHIFT) == prefix);
     if (match) {
       const uint32_t d = (key >> SHIFT) & uint32_t(NB - 1);
-      atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m));
+      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m));
       atomicAdd(&h_c[d], 1u);
     }
   }
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   uint32_t* gc = a.R.cnt + (int64_t(row) * 3 + LEVEL) * kBins;
   for (int i = tid; i < NB; i += kSelThreads) {
     if (h_c[i]) {
-      atomicAdd(reinterpret_cast<unsigned long long*>(gm + i), (unsigned long long)h_m[i]);
+      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(gm + i), (unsigned long long)h_m[i]);
       atomicAdd(gc + i, h_c[i]);
     }
   }
@@ -241,8 +247,9 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
       sc += h_c[f];
     }
     if (sc) {
-      atomicAdd(reinterpret_cast<unsigned long long*>(a.R.cmass + (int64_t(row) * 3 + LEVEL) * kCoarse + tid),
-                (unsigned long long)sm);
+      if (!a.by_count)
+        atomicAdd(reinterpret_cast<unsigned long long*>(a.R.cmass + (int64_t(row) * 3 + LEVEL) * kCoarse + tid),
+                  (unsigned long long)sm);
       atomicAdd(a.R.ccnt + (int64_t(row) * 3 + LEVEL) * kCoarse + tid, sc);
     }
   }
@@ -276,11 +283,11 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     in.above = ls.above;
     in.cnt_above = ls.cnt_above;
     in.target = ls.target;
-    const Resolved o = resolve_level(a.R, row, 2, in, a.top_p, lane);
+    const Resolved o = resolve_level(a.R, row, 2, in, a.top_p, a.by_count, a.k_target, lane);
     if (lane == 0) {
-      // tied tokens share one weight: take just enough of them to reach the target
+      // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
       s_t = o.prefix;
-      const uint64_t w = fixed_weight(key_score(o.prefix), a.R.state[row].ref_max);
+      const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(o.prefix), a.R.state[row].ref_max);
       const uint64_t rem = o.target - o.above;
       uint64_t r = (w == 0) ? o.tied : (rem + w - 1) / w;
       if (r < 1) r = 1;
@@ -460,6 +467,42 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.sel_count = sel_count;
   a.starts = sel_starts;
   a.nsplit = nsplit;
+  a.R = sel_rows(ws, lay);
+  return launch_select(a, rows, s);
+}
+
+extern "C" rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx, const float* scores, int64_t k,
+                                      int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  Layer L;
+  rtp_status st = check_desc(desc, &L);
+  if (st != RTP_OK) return st;
+  if (n_ctx < 1 || n_ctx > L.n_cap)
+    return fail(RTP_EINVAL, "n_ctx must be in [1, n_cap=%lld] (got %lld)", (long long)L.n_cap, (long long)n_ctx);
+  if (k < 1) return fail(RTP_EINVAL, "rtp_topk_select: k must be >= 1 (got %lld)", (long long)k);
+  if (L.n_ret == 0) return ok();
+  if (!scores || !sel_idx || !sel_count) return fail(RTP_EINVAL, "rtp_topk_select: NULL tensor pointer");
+  if (!aligned(scores, 16) || !aligned(sel_idx, 16))
+    return fail(RTP_EINVAL, "rtp_topk_select: tensors must be 16-byte aligned");
+  const int rows = L.B * L.n_ret * L.G;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const SelLayout lay = sel_layout(L);
+  if (k < n_ctx && (!ws || ws_bytes < lay.total || !aligned(ws, 256)))
+    return fail(RTP_EWORKSPACE, "rtp_topk_select: workspace needs %zu bytes, 256-aligned (got %zu)", lay.total,
+                ws_bytes);
+  SelArgs a{};
+  a.scores = scores;
+  a.top_p = k >= n_ctx ? 1.0f : 0.5f;          // >= 1: every token (the k_sel_all path)
+  a.by_count = 1;
+  a.k_target = k;
+  a.n_ctx = int(n_ctx);
+  a.n_cap = L.n_cap;
+  a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
+  a.lb_stride = lay.nblk_max;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.starts = sel_starts;
+  a.nsplit = int((n_ctx + kDecRange - 1) / kDecRange);
   a.R = sel_rows(ws, lay);
   return launch_select(a, rows, s);
 }

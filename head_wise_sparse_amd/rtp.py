@@ -23,8 +23,8 @@ CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK, CALL
 SEL_RANGE = 1024          # RTP_SEL_RANGE: token range of one entry of a selected-set range index
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
-            "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_status_string", "rtp_last_error",
-            "rtp_version"]
+            "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_status_string",
+            "rtp_last_error", "rtp_version"]
 
 
 class RtpError(RuntimeError):
@@ -65,6 +65,7 @@ def load() -> C.CDLL:
                                        _P, _P, C.c_size_t, _P]),
         "rtp_decode_step": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, C.c_float,
                                       C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_topk_select": (C.c_int, [D, C.c_int64, _P, C.c_int64, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_status_string": (C.c_char_p, [C.c_int]),
         "rtp_last_error": (C.c_char_p, []),
         "rtp_version": (C.c_char_p, []),
@@ -170,6 +171,12 @@ def rtp_topp_select(layer: Layer, n_ctx: int, scores, row_max, row_sum, top_p: f
     _check(load().rtp_topp_select(layer.desc, int(n_ctx), _ptr(scores), _ptr(row_max), _ptr(row_sum),
                                   float(top_p), _ptr(sel_idx), _ptr(sel_count), _ptr(sel_starts), p, n,
                                   _stream(stream)))
+
+
+def rtp_topk_select(layer: Layer, n_ctx: int, scores, k: int, sel_idx, sel_count, sel_starts, ws, stream=None):
+    p, n = _ws(ws)
+    _check(load().rtp_topk_select(layer.desc, int(n_ctx), _ptr(scores), int(k), _ptr(sel_idx), _ptr(sel_count),
+                                  _ptr(sel_starts), p, n, _stream(stream)))
 
 
 def rtp_sparse_decode_attn(layer: Layer, n_ctx: int, q, k_cache, v_cache, sel_idx, sel_count, sel_starts,

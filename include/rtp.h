@@ -150,6 +150,22 @@ rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * rtp_topk_select -- the static fixed-budget rule the abstract contrasts with
+ * top-p (abstract, observation (3); summary, "Key results": top-k baseline): the
+ * k tokens that rank first by (score descending, index ascending).
+ *
+ *   scores   fp32 [B][Hq_r][n_cap] (j < n_ctx read)
+ *   k        >= 1; k >= n_ctx keeps all n_ctx tokens
+ *   sel_idx, sel_count, sel_starts   as rtp_topp_select (sel_count = min(k, n_ctx))
+ * Same radix search as rtp_topp_select with every token weighing 1, so the
+ * result is exact (integer work) and bit-reproducible.  Workspace: the
+ * RTP_CALL_TOPP_SELECT size, under the same zero-fill rule.
+ */
+rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx, const float* scores, int64_t k,
+                           int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * rtp_sparse_decode_attn -- decode attention of the retrieval heads over their
  * selected tokens only (abstract: sparse attention through the token indexer).
  *

@@ -115,7 +115,10 @@ def topp_select(scores: np.ndarray, p: float) -> Tuple[np.ndarray, Dict[str, np.
 
 
 def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
-    """Fixed-budget contrast (abstract: "fixed top-k"): the k highest scores, ties by lower index."""
+    """Fixed-budget selection, the static rule the abstract contrasts with top-p: the k
+    tokens that rank first by (score descending, index ascending), in increasing index
+    order; k >= N keeps all N.  (Research-map summary, "Key results": top-k is the
+    fixed-budget baseline the adaptive rule is compared against.)"""
     s = np.asarray(scores, np.float64)
     order = np.lexsort((np.arange(s.size), -s))
     return np.sort(order[:min(int(k), s.size)])

@@ -477,3 +477,62 @@ def test_fused_step_single_head_kind(roles):
                                  O.bf16_to_f64(x.v[0, h // cfg.group, :cfg.n_ctx]), lset, 1 / math.sqrt(128))
                         for h in range(cfg.n_q_heads)])
         P.check_outputs(g, ref, "all-local fused step")
+
+
+# ----------------------------------------------------------------------------- static top-k
+def _run_topk(L, n_ctx, scores32, k):
+    torch = _torch()
+    rows, cap = scores32.shape[0], L.n_cap
+    s = np.zeros((rows, cap), np.float32)
+    s[:, :n_ctx] = scores32
+    sel = torch.full((rows * cap,), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    nsplit = (n_ctx + rtp.SEL_RANGE - 1) // rtp.SEL_RANGE
+    starts = torch.full((rows * (nsplit + 1),), -3, dtype=torch.int32, device="cuda")
+    ws = rtp.workspace(L, n_ctx, rtp.CALL_TOPP_SELECT)
+    rtp.rtp_topk_select(L, n_ctx, torch.from_numpy(s).cuda(), k, sel, cnt, starts, ws)
+    torch.cuda.synchronize()
+    assert not ws.any().item(), "the selection workspace must be left zero-filled"
+    seln, cntn = sel.view(rows, cap).cpu().numpy(), cnt.cpu().numpy()
+    stn = starts.view(rows, nsplit + 1).cpu().numpy()
+    for r in range(rows):
+        c = int(cntn[r])
+        want = O.topk_select(scores32[r].astype(np.float64), k)
+        assert c == want.size and np.array_equal(seln[r, :c], want), f"row {r}, k={k}"
+        assert np.all(seln[r, c:] == -7)
+        st = np.searchsorted(want, np.arange(nsplit + 1) * rtp.SEL_RANGE)
+        st[nsplit] = c
+        assert np.array_equal(stn[r], st)
+
+
+@pytest.mark.parametrize("k", [1, 2, 255, 1000, 4096, 20000, 33000, 40000])
+def test_topk_select_exact(k):
+    """Static top-k on oracle-style scores with many exact ties: bit-exact sets."""
+    P.require_gpu()
+    rng = np.random.default_rng(k)
+    n = 33000
+    s32 = np.round(rng.standard_normal((5, n)) * 3, 2).astype(np.float32)
+    s32[1, ::5] = 7.0                                     # a large tie group at the top
+    s32[2] = 0.0                                          # everything tied
+    s32[3, 1000:1300] = -0.0
+    L = rtp.Layer(s32.shape[0], 1, 1, 64, n + 100, [1], 0, 1)
+    _run_topk(L, n, s32, k)
+
+
+def test_topk_select_real_scores():
+    """Top-k over the indexer scores of the 32K decode workload, k = a typical top-p budget."""
+    P.require_gpu()
+    x, _ = _inputs("decode_b8_32k", batch=2)
+    cfg = x.cfg
+    G = cfg.group
+    rows = []
+    for b in range(cfg.batch):
+        for ci in range(cfg.n_kv_r * G):
+            r = ci // G
+            g = cfg.retrieval_kv[r]
+            qi = O.indexer_query(O.bf16_to_f64(x.q_pre[b, g * G + ci % G]), O.bf16_to_f64(x.w_q_idx[ci]))
+            rows.append(O.indexer_scores(qi, O.bf16_to_f64(x.k_idx[b, r, :cfg.n_ctx])).astype(np.float32))
+    s32 = np.stack(rows)
+    L = rtp.Layer(s32.shape[0], 1, 1, 128, cfg.n_ctx, [1], 0, 1)
+    for k in (64, 2048):
+        _run_topk(L, cfg.n_ctx, s32, k)

@@ -317,3 +317,43 @@ def test_recall_is_one_for_full_set():
     assert abs(O.attention_recall(q, k, None, 40, np.arange(40), 0.25) - 1.0) < 1e-12
     r = O.attention_recall(q, k, None, 40, np.arange(10), 0.25)
     assert 0.0 < r < 1.0
+
+
+# ----------------------------------------------------------------------------- static top-k
+def _ranks_before(s, i, j):
+    """Token i ranks before token j: higher score, or equal score and lower index."""
+    return s[i] > s[j] or (s[i] == s[j] and i < j)
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_topk_brute_force(seed):
+    """Among all k-subsets exactly one has every member ranked before every non-member;
+    the oracle returns that one (ties are frequent: scores are drawn from 4 values)."""
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(1, 10))
+    s = rng.choice([-1.0, 0.0, 0.5, 2.0], size=n)
+    for k in range(0, n + 2):
+        got = O.topk_select(s, k)
+        want = [c for c in itertools.combinations(range(n), min(k, n))
+                if all(_ranks_before(s, i, j) for i in c for j in set(range(n)) - set(c))]
+        assert len(want) == 1
+        assert got.tolist() == list(want[0])
+
+
+def test_topk_invariants_and_topp_prefix():
+    rng = np.random.default_rng(7)
+    s = np.round(rng.standard_normal(3000) * 2, 1)           # many exact ties
+    for k in (1, 17, 500, 2999, 3000, 5000):
+        sel = O.topk_select(s, k)
+        assert sel.size == min(k, s.size)
+        assert np.all(np.diff(sel) > 0)
+        if 0 < sel.size < s.size:
+            rest = np.setdiff1d(np.arange(s.size), sel)
+            assert s[sel].min() >= s[rest].max()
+            t = s[sel].min()                                 # boundary score: the lowest indices are kept
+            tied_in, tied_out = sel[s[sel] == t], rest[s[rest] == t]
+            assert tied_out.size == 0 or tied_in.max() < tied_out.min()
+    # the top-p set is a prefix of the same ranking: it is the top-k set with k = |S_p|
+    for p in (0.3, 0.9, 0.999):
+        sp, _ = O.topp_select(s, p)
+        assert np.array_equal(np.sort(sp), O.topk_select(s, sp.size))
