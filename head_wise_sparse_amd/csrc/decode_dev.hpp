@@ -52,6 +52,13 @@ struct DecArgs {
   float scale_log2;           // sm_scale * log2(e)
   int s_end, w_start, list_len;   // window only
   HeadMap map;
+  // cache addressing: head index = rank (compact layout) or KV head; rows per head;
+  // ring_w > 0: a local ring (token j >= ring_s at row ring_s + (j - ring_s) % ring_w)
+  int cache_heads;
+  int by_rank;
+  int64_t cache_rows;
+  int ring_s, ring_w;
+  int ring_off;               // (w_start - ring_s) % ring_w: ring row of the first window token
 };
 
 // One block of split-K decode: slice `split` of group `grp` (= b * n_heads_of_kind + rank).
@@ -67,8 +74,9 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
   const int lg = wave * TPW + lane / LPT;
   const int li = lane % LPT;
   const int b = grp / a.map.n, rr = grp % a.map.n, g = a.map.kv[rr];
-  const uint16_t* kb = a.k + (int64_t(b) * a.Hkv + g) * a.n_cap * D + li * 8;
-  const uint16_t* vb = a.v + (int64_t(b) * a.Hkv + g) * a.n_cap * D + li * 8;
+  const int64_t head_off = (int64_t(b) * a.cache_heads + (a.by_rank ? rr : g)) * a.cache_rows * D + li * 8;
+  const uint16_t* kb = a.k + head_off;
+  const uint16_t* vb = a.v + head_off;
 
   __shared__ uint16_t s_list[SPARSE ? RANGE : 1];
   __shared__ uint8_t s_lmask[SPARSE ? RANGE : 1];
@@ -182,7 +190,13 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
     } else {
       mask = (1u << G) - 1u;
       const int p = p0 + e;
-      return p < a.s_end ? int64_t(p) : int64_t(a.w_start) + (p - a.s_end);
+      if (p < a.s_end) return int64_t(p);
+      if (a.ring_w > 0) {                      // window token w_start + (p - s_end) in the ring
+        int t = a.ring_off + (p - a.s_end);    // < 2 * ring_w: the window holds at most ring_w tokens
+        if (t >= a.ring_w) t -= a.ring_w;
+        return int64_t(a.ring_s) + t;
+      }
+      return int64_t(a.w_start) + (p - a.s_end);
     }
   };
 
@@ -356,6 +370,30 @@ __device__ __forceinline__ void merge_row(const MergeArgs& ma, int row) {
       Lsum += s_l[i][d];
     }
     out[(int64_t(b) * Hq + h) * D + d] = f32_to_bf16(Lsum > 0.0f ? A / Lsum : 0.0f);
+  }
+}
+
+// Cache addressing of the two decode kinds for the descriptor's layout (host side).
+inline void set_sparse_cache(DecArgs& a, const Layer& L) {
+  const bool compact = L.kv_layout == RTP_KV_COMPACT;
+  a.cache_heads = compact ? L.n_ret : L.Hkv;
+  a.by_rank = compact;
+  a.cache_rows = L.n_cap;
+  a.ring_s = a.ring_w = a.ring_off = 0;
+}
+inline void set_window_cache(DecArgs& a, const Layer& L) {      // after s_end / w_start are set
+  if (L.kv_layout == RTP_KV_COMPACT) {
+    a.cache_heads = L.n_loc;
+    a.by_rank = 1;
+    a.cache_rows = int64_t(L.n_sinks) + L.window;
+    a.ring_s = L.n_sinks;
+    a.ring_w = L.window;
+    a.ring_off = a.w_start >= L.n_sinks ? int((int64_t(a.w_start) - L.n_sinks) % L.window) : 0;
+  } else {
+    a.cache_heads = L.Hkv;
+    a.by_rank = 0;
+    a.cache_rows = L.n_cap;
+    a.ring_s = a.ring_w = a.ring_off = 0;
   }
 }
 

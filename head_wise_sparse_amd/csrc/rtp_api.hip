@@ -50,6 +50,8 @@ rtp_status check_desc(const rtp_layer_desc* d, Layer* L) {
   if (!d->kv_role) return fail(RTP_EINVAL, "kv_role is NULL");
   if (d->n_sinks < 0) return fail(RTP_EINVAL, "n_sinks must be >= 0 (got %d)", d->n_sinks);
   if (d->window < 1) return fail(RTP_EINVAL, "window must be >= 1 (got %d)", d->window);
+  if (d->kv_layout != RTP_KV_FULL && d->kv_layout != RTP_KV_COMPACT)
+    return fail(RTP_EINVAL, "kv_layout must be RTP_KV_FULL or RTP_KV_COMPACT (got %d)", d->kv_layout);
   L->B = d->batch;
   L->Hq = d->n_q_heads;
   L->Hkv = d->n_kv_heads;
@@ -65,6 +67,7 @@ rtp_status check_desc(const rtp_layer_desc* d, Layer* L) {
   }
   L->n_sinks = d->n_sinks;
   L->window = d->window;
+  L->kv_layout = d->kv_layout;
   return ok();
 }
 

@@ -1,0 +1,123 @@
+// rtp_append_token: store one new token of every sequence in the caches a decode step
+// reads -- its post-RoPE key and value (every head), and for retrieval heads its
+// 16-dim pre-RoPE indexer key (abstract, observation (2); research-map summary,
+// "Approach": only retrieval heads keep the whole history, local heads keep their sinks
+// and window).
+//
+// One block per (batch, KV head): 16 lanes copy the 256-byte K and V rows, and for a
+// retrieval head 64 lanes form the 16 projections (4 lanes per output, fp32
+// accumulation, one bf16 rounding to nearest even).
+#include "rtp_internal.hpp"
+
+using namespace rtp;
+using namespace rtp_dev;
+
+namespace {
+
+struct AppendArgs {
+  int64_t pos;
+  const uint16_t* k_new;       // [B][Hkv][D]
+  const uint16_t* v_new;
+  const uint16_t* k_pre;       // [B][Hkv][D]
+  const uint16_t* w_k;         // [Hkv_r][D][16], w_stride elements apart
+  int64_t w_stride;
+  uint16_t* k_ret;             // full: [B][Hkv][n_cap][D]; compact: [B][Hkv_r][n_cap][D]
+  uint16_t* v_ret;
+  uint16_t* k_idx;             // [B][Hkv_r][n_cap][16]
+  uint16_t* k_loc;             // compact: [B][Hkv_l][n_sinks + window][D]
+  uint16_t* v_loc;
+  int Hkv, D, n_ret, n_loc;
+  int64_t n_cap;
+  int compact;
+  int64_t ring_rows;           // compact: rows per local head (n_sinks + window)
+  int64_t loc_row;             // compact: ring row of `pos`
+  int rank[kMaxHeads];         // KV head -> rank within its kind
+  uint8_t role[kMaxHeads];     // 1 = retrieval
+};
+
+__global__ __launch_bounds__(64) void k_append(AppendArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const bool ret = a.role[g];
+  const int r = a.rank[g];
+  const int64_t src = (int64_t(b) * a.Hkv + g) * a.D;
+  uint16_t *kd, *vd;
+  if (!a.compact) {
+    kd = a.k_ret + ((int64_t(b) * a.Hkv + g) * a.n_cap + a.pos) * a.D;
+    vd = a.v_ret + ((int64_t(b) * a.Hkv + g) * a.n_cap + a.pos) * a.D;
+  } else if (ret) {
+    kd = a.k_ret + ((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.D;
+    vd = a.v_ret + ((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.D;
+  } else {
+    kd = a.k_loc + ((int64_t(b) * a.n_loc + r) * a.ring_rows + a.loc_row) * a.D;
+    vd = a.v_loc + ((int64_t(b) * a.n_loc + r) * a.ring_rows + a.loc_row) * a.D;
+  }
+  const int nv = a.D / 8;                  // 16-byte pieces per row
+  if (lane < nv) {
+    reinterpret_cast<uint4*>(kd)[lane] = reinterpret_cast<const uint4*>(a.k_new + src)[lane];
+    reinterpret_cast<uint4*>(vd)[lane] = reinterpret_cast<const uint4*>(a.v_new + src)[lane];
+  }
+  if (!ret) return;
+  // k_idx[b][r][pos][c] = bf16(sum_d k_pre[d] * W[r][d][c]): lanes 4c .. 4c+3 split d
+  const int c = lane >> 2, part = lane & 3;
+  const uint16_t* w = a.w_k + int64_t(r) * a.w_stride;
+  float acc = 0.0f;
+  for (int d = part; d < a.D; d += 4) acc = fmaf(bf16_to_f32(a.k_pre[src + d]), bf16_to_f32(w[d * kIdxDim + c]), acc);
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  if (part == 0) a.k_idx[((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * kIdxDim + c] = f32_to_bf16(acc);
+}
+
+}  // namespace
+
+extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, const uint16_t* k_new,
+                                       const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx,
+                                       int64_t w_head_stride, uint16_t* k_cache, uint16_t* v_cache,
+                                       uint16_t* k_idx_cache, uint16_t* k_loc, uint16_t* v_loc, void* stream) {
+  Layer L;
+  rtp_status st = check_desc(desc, &L);
+  if (st != RTP_OK) return st;
+  if (pos < 0 || pos >= L.n_cap)
+    return fail(RTP_EINVAL, "rtp_append_token: pos must be in [0, n_cap=%lld) (got %lld)", (long long)L.n_cap,
+                (long long)pos);
+  const bool compact = L.kv_layout == RTP_KV_COMPACT;
+  if (!k_new || !v_new) return fail(RTP_EINVAL, "rtp_append_token: NULL tensor pointer");
+  if ((L.n_ret || !compact) && (!k_cache || !v_cache)) return fail(RTP_EINVAL, "rtp_append_token: NULL cache");
+  if (compact && L.n_loc && (!k_loc || !v_loc)) return fail(RTP_EINVAL, "rtp_append_token: NULL local ring");
+  if (L.n_ret && (!k_pre || !w_k_idx || !k_idx_cache)) return fail(RTP_EINVAL, "rtp_append_token: NULL indexer");
+  if (w_head_stride < 0) return fail(RTP_EINVAL, "w_head_stride must be >= 0");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(k_loc, 16) || !aligned(v_loc, 16) || !aligned(k_idx_cache, 2) || !aligned(k_pre, 2))
+    return fail(RTP_EINVAL, "rtp_append_token: tensors must be 16-byte aligned");
+  AppendArgs a{};
+  a.pos = pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pre = k_pre;
+  a.w_k = w_k_idx;
+  a.w_stride = w_head_stride;
+  a.k_ret = k_cache;
+  a.v_ret = v_cache;
+  a.k_idx = k_idx_cache;
+  a.k_loc = k_loc;
+  a.v_loc = v_loc;
+  a.Hkv = L.Hkv;
+  a.D = L.D;
+  a.n_ret = L.n_ret;
+  a.n_loc = L.n_loc;
+  a.n_cap = L.n_cap;
+  a.compact = compact;
+  const int64_t S = L.n_sinks, W = L.window;
+  a.ring_rows = S + W;
+  a.loc_row = pos < S ? pos : S + (pos - S) % W;
+  for (int i = 0; i < L.n_ret; ++i) {
+    a.rank[L.ret_kv[i]] = i;
+    a.role[L.ret_kv[i]] = 1;
+  }
+  for (int i = 0; i < L.n_loc; ++i) {
+    a.rank[L.loc_kv[i]] = i;
+    a.role[L.loc_kv[i]] = 0;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_append, dim3(L.Hkv, L.B), dim3(64), 0, s, a);
+  return check_launch("k_append");
+}

@@ -144,6 +144,7 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
   a.nsplit = nsplit;
   a.scale_log2 = sm_scale * kLog2e;
   a.map = ret_map(L);
+  set_sparse_cache(a, L);
   if ((st = dispatch_partial<true>(L, dim3(nsplit, L.B * L.n_ret), s, a)) != RTP_OK) return st;
   return launch_merge(L, rows, nsplit, a.map, part, out, s);
 }
@@ -182,6 +183,7 @@ extern "C" rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n
   a.w_start = int(w_start);
   a.list_len = int(len);
   a.map = loc_map(L);
+  set_window_cache(a, L);
   if ((st = dispatch_partial<false>(L, dim3(nsplit, L.B * L.n_loc), s, a)) != RTP_OK) return st;
   return launch_merge(L, rows, nsplit, a.map, a.part, out, s);
 }

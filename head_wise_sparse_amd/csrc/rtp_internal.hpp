@@ -28,6 +28,7 @@ struct Layer {
   int ret_kv[kMaxHeads];          // retrieval rank -> KV head
   int loc_kv[kMaxHeads];          // local rank -> KV head
   int n_sinks, window;
+  int kv_layout;                  // RTP_KV_FULL / RTP_KV_COMPACT
 };
 
 // Validate the descriptor (shared by every call).

@@ -420,6 +420,8 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
     return fail(RTP_EINVAL, "rtp_prefill_attn: need 0 <= c0 and c0 + C <= n_cap (c0=%lld, C=%d, n_cap=%lld)",
                 (long long)c0, C, (long long)L.n_cap);
   if (L.D != PD) return fail(RTP_EUNSUPPORTED, "rtp_prefill_attn: head_dim must be 128 (got %d)", L.D);
+  if (L.kv_layout != RTP_KV_FULL)
+    return fail(RTP_EUNSUPPORTED, "rtp_prefill_attn: the chunk needs the full cache layout (RTP_KV_FULL)");
   if (!q || !k_cache || !v_cache || !out) return fail(RTP_EINVAL, "rtp_prefill_attn: NULL tensor pointer");
   if (L.n_ret > 0 && (!k_pre || !w_k_idx || !k_idx_cache))
     return fail(RTP_EINVAL, "rtp_prefill_attn: NULL indexer pointer");

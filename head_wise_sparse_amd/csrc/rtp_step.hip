@@ -113,7 +113,8 @@ size_t step_ws_bytes(const Layer& L, int64_t n_ctx) { return step_layout(L, n_ct
 extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
                                       const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
                                       float idx_scale, const uint16_t* q, const uint16_t* k_cache,
-                                      const uint16_t* v_cache, float top_p, float sm_scale, float* scores,
+                                      const uint16_t* v_cache, const uint16_t* k_loc, const uint16_t* v_loc,
+                                      float top_p, float sm_scale, float* scores,
                                       float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
                                       int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
                                       void* stream) {
@@ -123,7 +124,14 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
   if (n_ctx < 1 || n_ctx > L.n_cap)
     return fail(RTP_EINVAL, "rtp_decode_step: n_ctx must be in [1, n_cap=%lld] (got %lld)", (long long)L.n_cap,
                 (long long)n_ctx);
-  if (!q || !k_cache || !v_cache || !out) return fail(RTP_EINVAL, "rtp_decode_step: NULL tensor pointer");
+  const bool compact = L.kv_layout == RTP_KV_COMPACT;
+  // the local heads' cache: the ring (compact layout) or the shared full cache
+  const uint16_t* k_loc_c = compact ? k_loc : k_cache;
+  const uint16_t* v_loc_c = compact ? v_loc : v_cache;
+  if (!q || !out || (L.n_ret && (!k_cache || !v_cache)) || (L.n_loc && (!k_loc_c || !v_loc_c)))
+    return fail(RTP_EINVAL, "rtp_decode_step: NULL tensor pointer");
+  if ((k_loc_c && !aligned(k_loc_c, 16)) || (v_loc_c && !aligned(v_loc_c, 16)))
+    return fail(RTP_EINVAL, "rtp_decode_step: q/k/v must be 16-byte aligned");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 2))
     return fail(RTP_EINVAL, "rtp_decode_step: q/k/v must be 16-byte aligned");
   if (!std::isfinite(sm_scale)) return fail(RTP_EINVAL, "rtp_decode_step: sm_scale must be finite");
@@ -179,6 +187,9 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
     wa.w_start = int(w_start);
     wa.list_len = int(len);
     wa.map = loc_map(L);
+    wa.k = k_loc_c;
+    wa.v = v_loc_c;
+    set_window_cache(wa, L);
   }
   if ((st = dispatch_score_window(L, unsigned(n_score + n_win), s, sa, n_score, score_gx, wa, win_gx)) != RTP_OK)
     return st;
@@ -228,6 +239,7 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
     da.nsplit = nsplit;
     da.scale_log2 = sm_scale * kLog2eStep;
     da.map = ret_map(L);
+    set_sparse_cache(da, L);
     if ((st = dispatch_sparse(L, dim3(nsplit, L.B * L.n_ret), s, da)) != RTP_OK) return st;
   }
 

@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libr
 RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EDEVICE = range(5)
 CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK, CALL_PREFILL, CALL_DECODE_STEP = range(6)
 SEL_RANGE = 1024          # RTP_SEL_RANGE: token range of one entry of a selected-set range index
+KV_FULL, KV_COMPACT = 0, 1
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
-            "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_status_string",
-            "rtp_last_error", "rtp_version"]
+            "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_append_token",
+            "rtp_status_string", "rtp_last_error", "rtp_version"]
 
 
 class RtpError(RuntimeError):
@@ -36,7 +37,8 @@ class RtpError(RuntimeError):
 class _Desc(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("idx_dim", C.c_int32), ("n_cap", C.c_int64),
-                ("kv_role", C.POINTER(C.c_uint8)), ("n_sinks", C.c_int32), ("window", C.c_int32)]
+                ("kv_role", C.POINTER(C.c_uint8)), ("n_sinks", C.c_int32), ("window", C.c_int32),
+                ("kv_layout", C.c_int32)]
 
 
 _lib = None
@@ -63,8 +65,9 @@ def load() -> C.CDLL:
         "rtp_window_sink_attn": (C.c_int, [D, C.c_int64, _P, _P, _P, C.c_float, _P, _P, C.c_size_t, _P]),
         "rtp_prefill_attn": (C.c_int, [D, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, C.c_int64, _P, C.c_float,
                                        _P, _P, C.c_size_t, _P]),
-        "rtp_decode_step": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, C.c_float,
-                                      C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_decode_step": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, _P, _P,
+                                      C.c_float, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_append_token": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, C.c_int64, _P, _P, _P, _P, _P, _P]),
         "rtp_topk_select": (C.c_int, [D, C.c_int64, _P, C.c_int64, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_status_string": (C.c_char_p, [C.c_int]),
         "rtp_last_error": (C.c_char_p, []),
@@ -102,11 +105,13 @@ class Layer:
     n_sinks: int
     window: int
     idx_dim: int = 16
+    kv_layout: int = KV_FULL
 
     def __post_init__(self):
         self._role = (C.c_uint8 * len(self.kv_role))(*[int(r) for r in self.kv_role])
         self._desc = _Desc(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.idx_dim,
-                           self.n_cap, C.cast(self._role, C.POINTER(C.c_uint8)), self.n_sinks, self.window)
+                           self.n_cap, C.cast(self._role, C.POINTER(C.c_uint8)), self.n_sinks, self.window,
+                           self.kv_layout)
 
     @property
     def desc(self):
@@ -202,13 +207,21 @@ def rtp_prefill_attn(layer: Layer, c0: int, C_rows: int, q, k_cache, v_cache, k_
 
 
 def rtp_decode_step(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_stride: int, k_idx, idx_scale: float, q,
-                    k_cache, v_cache, top_p: float, sm_scale: float, scores, row_max, row_sum, sel_idx, sel_count,
-                    sel_starts, out, ws, stream=None):
+                    k_cache, v_cache, k_loc, v_loc, top_p: float, sm_scale: float, scores, row_max, row_sum, sel_idx,
+                    sel_count, sel_starts, out, ws, stream=None):
     p, n = _ws(ws)
     _check(load().rtp_decode_step(layer.desc, int(n_ctx), _ptr(q_pre), _ptr(w_q_idx), int(w_head_stride),
-                                  _ptr(k_idx), float(idx_scale), _ptr(q), _ptr(k_cache), _ptr(v_cache), float(top_p),
-                                  float(sm_scale), _ptr(scores), _ptr(row_max), _ptr(row_sum), _ptr(sel_idx),
-                                  _ptr(sel_count), _ptr(sel_starts), _ptr(out), p, n, _stream(stream)))
+                                  _ptr(k_idx), float(idx_scale), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_loc),
+                                  _ptr(v_loc), float(top_p), float(sm_scale), _ptr(scores), _ptr(row_max),
+                                  _ptr(row_sum), _ptr(sel_idx), _ptr(sel_count), _ptr(sel_starts), _ptr(out), p, n,
+                                  _stream(stream)))
+
+
+def rtp_append_token(layer: Layer, pos: int, k_new, v_new, k_pre, w_k_idx, w_head_stride: int, k_cache, v_cache,
+                     k_idx_cache, k_loc=None, v_loc=None, stream=None):
+    _check(load().rtp_append_token(layer.desc, int(pos), _ptr(k_new), _ptr(v_new), _ptr(k_pre), _ptr(w_k_idx),
+                                   int(w_head_stride), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(k_loc),
+                                   _ptr(v_loc), _stream(stream)))
 
 
 def rtp_version() -> str:
@@ -256,14 +269,16 @@ class DecodeStep:
         self.ws = {w: workspace(layer, cap, w, device) for w in which}
 
     def run(self, q_pre, q, k_cache, v_cache, k_idx, w_q_idx, w_head_stride: Optional[int] = None, stream=None,
-            n_ctx: Optional[int] = None):
+            n_ctx: Optional[int] = None, k_loc=None, v_loc=None):
+        """k_cache/v_cache: the full cache (KV_FULL) or the retrieval cache (KV_COMPACT,
+        with the local ring in k_loc/v_loc)."""
         L = self.layer
         n = self.n_ctx if n_ctx is None else int(n_ctx)
         if w_head_stride is None:
             w_head_stride = L.head_dim * L.idx_dim
         if self.fused:
-            rtp_decode_step(L, n, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, q, k_cache, v_cache,
-                            self.top_p, self.sm_scale, self.scores, self.row_max, self.row_sum, self.sel_idx,
+            rtp_decode_step(L, n, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, q, k_cache, v_cache, k_loc,
+                            v_loc, self.top_p, self.sm_scale, self.scores, self.row_max, self.row_sum, self.sel_idx,
                             self.sel_count, self.sel_starts, self.out, self.ws[CALL_DECODE_STEP], stream)
             return self.out
         rtp_indexer_score(L, n, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, self.scores, self.row_max,
@@ -272,5 +287,7 @@ class DecodeStep:
                         self.sel_starts, self.ws[CALL_TOPP_SELECT], stream)
         rtp_sparse_decode_attn(L, n, q, k_cache, v_cache, self.sel_idx, self.sel_count, self.sel_starts,
                                self.sm_scale, self.out, self.ws[CALL_SPARSE_DECODE], stream)
-        rtp_window_sink_attn(L, n, q, k_cache, v_cache, self.sm_scale, self.out, self.ws[CALL_WINDOW_SINK], stream)
+        compact = L.kv_layout == KV_COMPACT
+        rtp_window_sink_attn(L, n, q, k_loc if compact else k_cache, v_loc if compact else v_cache, self.sm_scale,
+                             self.out, self.ws[CALL_WINDOW_SINK], stream)
         return self.out

@@ -75,7 +75,23 @@ typedef struct rtp_layer_desc {
   const uint8_t* kv_role; /* [Hkv] HOST array: 1 = retrieval head, 0 = local head */
   int32_t n_sinks;        /* local heads: sink tokens at the start of the sequence (>= 0) */
   int32_t window;         /* local heads: sliding window, counting the query token (>= 1) */
+  int32_t kv_layout;      /* RTP_KV_FULL or RTP_KV_COMPACT (decode calls; see below) */
 } rtp_layer_desc;
+
+/*
+ * K/V cache layouts of the decode calls (the cache pointer each call takes):
+ *  RTP_KV_FULL     every head: [B][Hkv][n_cap][D], token j at row j.
+ *  RTP_KV_COMPACT  only retrieval heads keep their whole history, local heads keep
+ *                  their sinks and window (abstract: the full KV cache is retained for
+ *                  retrieval heads only; summary, "Approach"):
+ *                    retrieval cache [B][Hkv_r][n_cap][D], token j at row j;
+ *                    local ring      [B][Hkv_l][n_sinks + window][D], token j at row
+ *                    j if j < n_sinks, else n_sinks + (j - n_sinks) % window.
+ *                  rtp_sparse_decode_attn takes the retrieval cache, rtp_window_sink_attn
+ *                  the ring; rtp_append_token writes both.  Prefill needs RTP_KV_FULL.
+ */
+#define RTP_KV_FULL 0
+#define RTP_KV_COMPACT 1
 
 /* Token-index range of one entry of a selected-set range index (sel_starts). */
 #define RTP_SEL_RANGE 1024
@@ -235,7 +251,10 @@ rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, int32_t C,
  * reduces the row statistics, and one merge launch serves both head kinds.
  *
  *   q_pre, w_q_idx, w_head_stride, k_idx, idx_scale   as rtp_indexer_score
- *   q, k_cache, v_cache, sm_scale                     as the decode calls
+ *   q, k_cache, v_cache, sm_scale                     as the decode calls (RTP_KV_COMPACT:
+ *                                                     k_cache/v_cache = the retrieval cache)
+ *   k_loc, v_loc   RTP_KV_COMPACT: the local heads' ring; ignored (may be NULL)
+ *                  with RTP_KV_FULL
  *   top_p                                             as rtp_topp_select
  *   scores, row_max, row_sum, sel_idx, sel_count      outputs, as the separate calls
  *   sel_starts   optional output (NULL: kept in the workspace)
@@ -250,10 +269,32 @@ rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
                            const uint16_t* q_pre, const uint16_t* w_q_idx, int64_t w_head_stride,
                            const uint16_t* k_idx, float idx_scale,
                            const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                           const uint16_t* k_loc, const uint16_t* v_loc,
                            float top_p, float sm_scale,
                            float* scores, float* row_max, float* row_sum,
                            int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts,
                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_append_token -- store the token at position `pos` (the next one; decode then
+ * runs with n_ctx = pos + 1) in every cache of the layout: its post-RoPE key and
+ * value for every head, and for retrieval heads its indexer key
+ * k_idx_cache[b][r][pos] = bf16(k_pre[b][g(r)] . W_k_idx[r]) (fp32 accumulation,
+ * one rounding; abstract, observation (2); summary, "Approach").
+ *
+ *   k_new, v_new  bf16 [B][Hkv][D] post-RoPE;  k_pre bf16 [B][Hkv][D] pre-RoPE
+ *   w_k_idx       bf16 [Hkv_r][D][16], head r at r*w_head_stride (0 = shared)
+ *   RTP_KV_FULL:    k_cache/v_cache [B][Hkv][n_cap][D]; k_loc/v_loc ignored
+ *   RTP_KV_COMPACT: k_cache/v_cache [B][Hkv_r][n_cap][D] (retrieval heads) and
+ *                   k_loc/v_loc [B][Hkv_l][n_sinks + window][D] (the ring)
+ *   k_idx_cache   bf16 [B][Hkv_r][n_cap][16]
+ * Requires 0 <= pos < n_cap.  Pointers of a head kind the layer lacks may be NULL.
+ */
+rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos,
+                            const uint16_t* k_new, const uint16_t* v_new, const uint16_t* k_pre,
+                            const uint16_t* w_k_idx, int64_t w_head_stride,
+                            uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache,
+                            uint16_t* k_loc, uint16_t* v_loc, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* rtp_status_string(rtp_status s);

@@ -71,8 +71,8 @@ def test_workspace_sizes():
 
 def _call_step(L, n_ctx=1000, ws_bytes=1 << 30, top_p=0.9, sm=0.1, ptr=FAKE, ws=FAKE):
     lib = _lib()
-    return lib.rtp_decode_step(L.desc, n_ctx, ptr, ptr, 0, ptr, 1.0, ptr, ptr, ptr, top_p, sm, ptr, ptr, ptr, ptr,
-                               ptr, None, ptr, ws, ws_bytes, None)
+    return lib.rtp_decode_step(L.desc, n_ctx, ptr, ptr, 0, ptr, 1.0, ptr, ptr, ptr, None, None, top_p, sm, ptr, ptr,
+                               ptr, ptr, ptr, None, ptr, ws, ws_bytes, None)
 
 
 def test_decode_step_validation():
@@ -87,6 +87,29 @@ def test_decode_step_validation():
     assert _call_step(L, ws_bytes=1024) == rtp.RTP_EWORKSPACE
     assert _call_step(L, ws=FAKE + 16) == rtp.RTP_EWORKSPACE
     assert "workspace" in _lib().rtp_last_error().decode()
+    # the compact layout needs the local ring; prefill needs the full layout
+    Lc = _layer(kv_layout=rtp.KV_COMPACT)
+    assert _call_step(Lc) == rtp.RTP_EINVAL
+    assert lib_prefill_compact() == rtp.RTP_EUNSUPPORTED
+
+
+def lib_prefill_compact():
+    L = _layer(batch=1, n_cap=32768, kv_layout=rtp.KV_COMPACT)
+    return _lib().rtp_prefill_attn(L.desc, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0.1, FAKE, FAKE, 1 << 30,
+                                   None)
+
+
+def test_append_validation():
+    lib = _lib()
+    L = _layer()
+    call = lambda L, pos=5, ptr=FAKE, kl=None: lib.rtp_append_token(L.desc, pos, ptr, ptr, ptr, ptr, 0, ptr, ptr, ptr,
+                                                                    kl, kl, None)
+    assert call(L, pos=-1) == rtp.RTP_EINVAL
+    assert call(L, pos=L.n_cap) == rtp.RTP_EINVAL
+    assert call(L, ptr=None) == rtp.RTP_EINVAL
+    assert call(L, ptr=FAKE + 8) == rtp.RTP_EINVAL
+    assert call(_layer(kv_layout=rtp.KV_COMPACT)) == rtp.RTP_EINVAL           # ring missing
+    assert call(_layer(kv_layout=2)) == rtp.RTP_EINVAL                        # unknown layout
 
 
 def _call_score(L, n_ctx=1000, ws_bytes=1 << 20, scale=1.0, ptr=FAKE):

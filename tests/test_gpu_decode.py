@@ -536,3 +536,123 @@ def test_topk_select_real_scores():
     L = rtp.Layer(s32.shape[0], 1, 1, 128, cfg.n_ctx, [1], 0, 1)
     for k in (64, 2048):
         _run_topk(L, cfg.n_ctx, s32, k)
+
+
+# ----------------------------------------------------------------------------- compact layout + append
+def _ring_slot(j, S, Wn):
+    return j if j < S else S + (j - S) % Wn
+
+
+def _compact_caches(x, n_ctx):
+    """Host-built compact caches holding the same tokens as the full cache: retrieval heads'
+    whole history, local heads' sinks and last `window` tokens at their ring rows."""
+    torch = _torch()
+    cfg = x.cfg
+    S, Wn = cfg.n_sinks, cfg.window
+    ret = [g for g in range(cfg.n_kv_heads) if x.kv_role[g]]
+    loc = [g for g in range(cfg.n_kv_heads) if not x.kv_role[g]]
+    kr, vr = x.k[:, ret], x.v[:, ret]
+    rows = S + Wn
+    kl = np.zeros((cfg.batch, len(loc), rows, cfg.head_dim), np.uint16)
+    vl = np.zeros_like(kl)
+    toks = list(range(min(S, n_ctx))) + list(range(max(n_ctx - Wn, min(S, n_ctx)), n_ctx))
+    for j in toks:
+        kl[:, :, _ring_slot(j, S, Wn)] = x.k[:, loc, j]
+        vl[:, :, _ring_slot(j, S, Wn)] = x.v[:, loc, j]
+    dev = lambda a: rtp.to_device_bf16(np.ascontiguousarray(a))
+    return dev(kr), dev(vr), dev(kl), dev(vl)
+
+
+def _layer_kind(cfg, layout, n_cap=None):
+    return rtp.Layer(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx if n_cap is None else n_cap,
+                     cfg.kv_role.tolist(), cfg.n_sinks, cfg.window, kv_layout=layout)
+
+
+@pytest.mark.parametrize("over", [dict(batch=2, n_ctx=9000), dict(batch=1, n_ctx=1500),
+                                  dict(batch=1, n_ctx=7777, window=1000, n_sinks=3)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_compact_layout_matches_full(over, fused):
+    """Retrieval-only full cache + local ring give the same bits as the full layout
+    (ring partly filled, and wrapped several times)."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", **over)
+    cfg = x.cfg
+    B, R = cfg.batch, cfg.n_kv_r * cfg.group
+    kr, vr, kl, vl = _compact_caches(x, cfg.n_ctx)
+    res = []
+    for layout in (rtp.KV_FULL, rtp.KV_COMPACT):
+        L = _layer_kind(cfg, layout)
+        step = rtp.DecodeStep(L, cfg.n_ctx, 0.95, fused=fused)
+        if layout == rtp.KV_FULL:
+            step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+        else:
+            step.run(d.q_pre, d.q, kr, vr, d.k_idx, d.w_q_idx, k_loc=kl, v_loc=vl)
+        torch.cuda.synchronize()
+        res.append(_step_outputs(step, B, R, cfg.n_ctx))
+    _assert_same(res[0], res[1], f"compact vs full {over}")
+
+
+def test_append_then_decode_both_layouts():
+    """Generate steps: append the next token into a full and a compact cache, then run the
+    fused step on each.  Rows are copied exactly, the indexer keys are the bf16 of the
+    projection within one bf16 ulp plus the fp32 bound, and both layouts give the same
+    bits at every step; the first step is checked against the oracle."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=2, n_ctx=6000, window=512)
+    cfg = x.cfg
+    B, R, D, Hkv = cfg.batch, cfg.n_kv_r * cfg.group, cfg.head_dim, cfg.n_kv_heads
+    n0, T = cfg.n_ctx - 6, 6
+    rng = np.random.default_rng(5)
+    k_pre_new = W.f32_to_bf16_bits(rng.standard_normal((T, B, Hkv, D)).astype(np.float32))
+    w_k = x.w_k_idx
+    # full layout: the generator's caches with the last T rows cleared; compact: built at n0
+    k_full, v_full = x.k.copy(), x.v.copy()
+    k_full[:, :, n0:] = 0
+    v_full[:, :, n0:] = 0
+    kidx = x.k_idx.copy()
+    kidx[:, :, n0:] = 0
+    dev = lambda a: rtp.to_device_bf16(np.ascontiguousarray(a))
+    kf, vf, kidx_f, kidx_c = dev(k_full), dev(v_full), dev(kidx), dev(kidx)
+    xc = type("X", (), {})()
+    xc.cfg, xc.k, xc.v, xc.kv_role = cfg, k_full, v_full, x.kv_role
+    kr, vr, kl, vl = _compact_caches(xc, n0)
+    Lf, Lc = _layer_kind(cfg, rtp.KV_FULL), _layer_kind(cfg, rtp.KV_COMPACT)
+    sf, sc = rtp.DecodeStep(Lf, cfg.n_ctx, 0.95), rtp.DecodeStep(Lc, cfg.n_ctx, 0.95)
+    ret = [g for g in range(Hkv) if x.kv_role[g]]
+    for t in range(T):
+        pos = n0 + t
+        k_new, v_new = dev(x.k[:, :, pos]), dev(x.v[:, :, pos])
+        kp = dev(k_pre_new[t])
+        rtp.rtp_append_token(Lf, pos, k_new, v_new, kp, dev(w_k), D * 16, kf, vf, kidx_f)
+        rtp.rtp_append_token(Lc, pos, k_new, v_new, kp, dev(w_k), D * 16, kr, vr, kidx_c, kl, vl)
+        sf.run(d.q_pre, d.q, kf, vf, kidx_f, d.w_q_idx, n_ctx=pos + 1)
+        sc.run(d.q_pre, d.q, kr, vr, kidx_c, d.w_q_idx, n_ctx=pos + 1, k_loc=kl, v_loc=vl)
+        torch.cuda.synchronize()
+        _assert_same(_step_outputs(sf, B, R, pos + 1), _step_outputs(sc, B, R, pos + 1), f"step {t}")
+        got_k = rtp.from_device_bf16(kf).reshape(B, Hkv, -1, D)[:, :, pos]
+        assert np.array_equal(got_k, x.k[:, :, pos])
+        gi = rtp.from_device_bf16(kidx_f).reshape(B, cfg.n_kv_r, -1, 16)[:, :, pos]
+        for b in range(B):
+            for r, g in enumerate(ret):
+                a = O.bf16_to_f64(k_pre_new[t, b, g])
+                wr = O.bf16_to_f64(w_k[r])
+                exact = a @ wr
+                allow = P.bf16_ulp(exact) + 1e-6 * (np.abs(a) @ np.abs(wr))
+                assert np.all(np.abs(O.bf16_to_f64(gi[b, r]) - exact) <= allow)
+        assert np.array_equal(gi, rtp.from_device_bf16(kidx_c).reshape(B, cfg.n_kv_r, -1, 16)[:, :, pos])
+        if t == 0:                                         # the first step against the oracle (local rows)
+            kk = k_full.copy()
+            kk[:, :, pos] = x.k[:, :, pos]
+            vv = v_full.copy()
+            vv[:, :, pos] = x.v[:, :, pos]
+            g_out = rtp.from_device_bf16(sf.out).reshape(B, cfg.n_q_heads, D)
+            lset = O.local_set(pos + 1, cfg.n_sinks, cfg.window)
+            for b in range(B):
+                for h in range(cfg.n_q_heads):
+                    if x.kv_role[h // cfg.group]:
+                        continue
+                    ref = O.attend(O.bf16_to_f64(x.q[b, h]), O.bf16_to_f64(kk[b, h // cfg.group, :pos + 1]),
+                                   O.bf16_to_f64(vv[b, h // cfg.group, :pos + 1]), lset, 1 / math.sqrt(D))
+                    P.check_outputs(g_out[b, h][None], ref[None], f"local row ({b},{h}) after append")
