@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the p = 0.9 / 0.99 decode timings")
+    ap.add_argument("--gen-steps", type=int, default=128,
+                    help="generated tokens of the growing-context workload (0: skip it)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run only one part (for profiling); the JSON line is still printed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -199,6 +201,61 @@ class DecodeBench:
                 "total": kidx + local + gathered + qo, "union_tokens": union, "per_head_tokens": per_head,
                 "sel_min": int(cnt.min()), "sel_median": int(np.median(cnt)), "sel_mean": float(cnt.mean()),
                 "sel_max": int(cnt.max())}
+
+
+# ----------------------------------------------------------------------------- long generation
+class GenBench:
+    """Generation over a growing context in the compact KV layout: every step appends the
+    next token (its K/V rows and, for retrieval heads, its indexer key) and runs the fused
+    decode step at the new length.  Launched eagerly: the context length changes every
+    step.  The retrieval heads keep their whole history, the local heads a ring of
+    sinks + window."""
+
+    def __init__(self, dec: "DecodeBench", steps: int):
+        torch, rtp = dec.torch, dec.rtp
+        self.torch, self.rtp = torch, rtp
+        cfg, x = dec.cfg, dec.x
+        self.cfg, self.T = cfg, steps
+        self.n0 = cfg.n_ctx - steps
+        self.L = rtp.Layer(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx, cfg.kv_role.tolist(),
+                           cfg.n_sinks, cfg.window, kv_layout=rtp.KV_COMPACT)
+        ret = [g for g in range(cfg.n_kv_heads) if cfg.kv_role[g]]
+        loc = [g for g in range(cfg.n_kv_heads) if not cfg.kv_role[g]]
+        S, Wn, n0 = cfg.n_sinks, cfg.window, self.n0
+        dev = lambda a: rtp.to_device_bf16(np.ascontiguousarray(a))
+        self.kr, self.vr = dev(x.k[:, ret]), dev(x.v[:, ret])
+        rows = S + Wn
+        kl = np.zeros((cfg.batch, len(loc), rows, cfg.head_dim), np.uint16)
+        vl = np.zeros_like(kl)
+        for j in list(range(min(S, n0))) + list(range(max(n0 - Wn, S), n0)):
+            slot = j if j < S else S + (j - S) % Wn
+            kl[:, :, slot] = x.k[:, loc, j]
+            vl[:, :, slot] = x.v[:, loc, j]
+        self.kl, self.vl = dev(kl), dev(vl)
+        self.kidx = dev(x.k_idx)
+        self.k_new = dev(np.moveaxis(x.k[:, :, n0:n0 + steps], 2, 0))      # [T][B][Hkv][D]
+        self.v_new = dev(np.moveaxis(x.v[:, :, n0:n0 + steps], 2, 0))
+        rng = np.random.default_rng(0)
+        from head_wise_sparse_amd.workloads import f32_to_bf16_bits
+        self.k_pre = dev(f32_to_bf16_bits(rng.standard_normal((steps, cfg.batch, cfg.n_kv_heads, cfg.head_dim))
+                                          .astype(np.float32)))
+        self.w_k = dev(x.w_k_idx)
+        self.q_pre, self.q, self.w_q = dev(x.q_pre), dev(x.q), dev(x.w_q_idx)
+        self.step = rtp.DecodeStep(self.L, cfg.n_ctx, cfg.top_p)
+        D = cfg.head_dim
+        self.tok = cfg.batch * cfg.n_kv_heads * D
+        self.full_bytes = cfg.batch * cfg.n_kv_heads * cfg.n_ctx * D * 4
+        self.compact_bytes = cfg.batch * (len(ret) * cfg.n_ctx + len(loc) * rows) * D * 4
+        torch.cuda.synchronize()
+
+    def run(self):
+        rtp, D = self.rtp, self.cfg.head_dim
+        for t in range(self.T):
+            pos = self.n0 + t
+            rtp.rtp_append_token(self.L, pos, self.k_new[t], self.v_new[t], self.k_pre[t], self.w_k, D * 16, self.kr,
+                                 self.vr, self.kidx, self.kl, self.vl)
+            self.step.run(self.q_pre, self.q, self.kr, self.vr, self.kidx, self.w_q, n_ctx=pos + 1, k_loc=self.kl,
+                          v_loc=self.vl)
 
 
 # ----------------------------------------------------------------------------- prefill
@@ -394,6 +451,24 @@ def main():
                                  "hbm_GBps": round(abp["total"] / (us * 1e-6) / 1e9, 1),
                                  "sel_mean": round(abp["sel_mean"], 1), "union_tokens": abp["union_tokens"]}
             res["decode"]["p_sweep"] = sweep
+    if dec and args.gen_steps > 0:
+        gen = GenBench(dec, args.gen_steps)
+        gen.run()                            # warm-up (re-appending the same tokens is idempotent)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        gen.run()
+        b.record()
+        torch.cuda.synchronize()
+        us_tok = a.elapsed_time(b) / gen.T * 1e3
+        res["generation"] = {
+            "workload": f"{gen.T} tokens generated from {gen.n0} to {gen.n0 + gen.T}, batch {dec.cfg.batch}, "
+                        "compact KV (retrieval heads: whole history; local heads: sinks + window ring), "
+                        "append + fused decode step per token, launched eagerly",
+            "us_per_token_per_layer": round(us_tok, 2),
+            "kv_bytes_full_layout": gen.full_bytes, "kv_bytes_compact_layout": gen.compact_bytes,
+            "memory_sparsity": round(1 - gen.compact_bytes / gen.full_bytes, 4)}
+        del gen
     if pre:
         fl = pre.flops()
         tflops = fl["total"] / (pre_ms * 1e-3) / 1e12
