@@ -44,7 +44,10 @@ rtp_status check_desc(const rtp_layer_desc* d, Layer* L) {
     return fail(RTP_EUNSUPPORTED, "GQA group size %d not supported (1, 2, 4, 8)", G);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(RTP_EUNSUPPORTED, "head_dim %d not supported (64, 128)", d->head_dim);
-  if (d->idx_dim != kIdxDim) return fail(RTP_EUNSUPPORTED, "idx_dim must be 16 (got %d)", d->idx_dim);
+  if (d->idx_dim != 4 && d->idx_dim != 8 && d->idx_dim != 16 && d->idx_dim != 32)
+    return fail(RTP_EUNSUPPORTED, "idx_dim must be 4, 8, 16 or 32 (got %d)", d->idx_dim);
+  if (d->idx_dim == 32 && d->n_q_heads / d->n_kv_heads > 4)
+    return fail(RTP_EUNSUPPORTED, "idx_dim 32 supports GQA groups of up to 4 heads");
   if (d->n_cap < 1 || d->n_cap >= (int64_t(1) << 30))
     return fail(RTP_EINVAL, "n_cap must be in [1, 2^30) (got %lld)", (long long)d->n_cap);
   if (!d->kv_role) return fail(RTP_EINVAL, "kv_role is NULL");
@@ -68,6 +71,7 @@ rtp_status check_desc(const rtp_layer_desc* d, Layer* L) {
   L->n_sinks = d->n_sinks;
   L->window = d->window;
   L->kv_layout = d->kv_layout;
+  L->idx = d->idx_dim;
   return ok();
 }
 
@@ -85,7 +89,7 @@ HeadMap loc_map(const Layer& L) {
 }
 
 size_t score_ws_bytes(const Layer& L, int64_t n_ctx) {
-  int64_t nblk = (n_ctx + kScoreTile - 1) / kScoreTile;
+  const int64_t nblk = (n_ctx + score_tile(L.idx) - 1) / score_tile(L.idx);
   return round_up(size_t(L.B) * L.n_ret * L.G * nblk * 2 * sizeof(float), 256);
 }
 

@@ -26,7 +26,7 @@ struct AppendArgs {
   uint16_t* k_idx;             // [B][Hkv_r][n_cap][16]
   uint16_t* k_loc;             // compact: [B][Hkv_l][n_sinks + window][D]
   uint16_t* v_loc;
-  int Hkv, D, n_ret, n_loc;
+  int Hkv, D, n_ret, n_loc, idx;
   int64_t n_cap;
   int compact;
   int64_t ring_rows;           // compact: rows per local head (n_sinks + window)
@@ -57,14 +57,15 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
     reinterpret_cast<uint4*>(vd)[lane] = reinterpret_cast<const uint4*>(a.v_new + src)[lane];
   }
   if (!ret) return;
-  // k_idx[b][r][pos][c] = bf16(sum_d k_pre[d] * W[r][d][c]): lanes 4c .. 4c+3 split d
-  const int c = lane >> 2, part = lane & 3;
+  // k_idx[b][r][pos][c] = bf16(sum_d k_pre[d] * W[r][d][c]): the 64 / idx lanes of output c
+  // split d, then a lane-group sum
+  const int lpo = 64 / a.idx;
+  const int c = lane / lpo, part = lane % lpo;
   const uint16_t* w = a.w_k + int64_t(r) * a.w_stride;
   float acc = 0.0f;
-  for (int d = part; d < a.D; d += 4) acc = fmaf(bf16_to_f32(a.k_pre[src + d]), bf16_to_f32(w[d * kIdxDim + c]), acc);
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  if (part == 0) a.k_idx[((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * kIdxDim + c] = f32_to_bf16(acc);
+  for (int d = part; d < a.D; d += lpo) acc = fmaf(bf16_to_f32(a.k_pre[src + d]), bf16_to_f32(w[d * a.idx + c]), acc);
+  for (int o = 1; o < lpo; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (part == 0) a.k_idx[((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.idx + c] = f32_to_bf16(acc);
 }
 
 }  // namespace
@@ -105,6 +106,7 @@ extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, 
   a.n_ret = L.n_ret;
   a.n_loc = L.n_loc;
   a.n_cap = L.n_cap;
+  a.idx = L.idx;
   a.compact = compact;
   const int64_t S = L.n_sinks, W = L.window;
   a.ring_rows = S + W;

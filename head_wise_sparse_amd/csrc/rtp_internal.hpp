@@ -10,7 +10,7 @@
 
 namespace rtp {
 
-constexpr int kIdxDim = 16;
+constexpr int kIdxDim = 16;       // the pages' indexer dimension (4, 8 and 32 are supported too)
 constexpr int kMaxHeads = 64;     // KV heads a descriptor may hold
 
 // ---------------------------------------------------------------- host-side helpers
@@ -29,6 +29,7 @@ struct Layer {
   int loc_kv[kMaxHeads];          // local rank -> KV head
   int n_sinks, window;
   int kv_layout;                  // RTP_KV_FULL / RTP_KV_COMPACT
+  int idx;                        // indexer dimension
 };
 
 // Validate the descriptor (shared by every call).
@@ -48,8 +49,10 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------- per-call workspace layouts
 // Indexer scoring: per-block (max, sum) partials.
 constexpr int kScoreThreads = 256;
-constexpr int kScoreItems = 8;                                  // tokens per thread
-constexpr int kScoreTile = kScoreThreads * kScoreItems;         // tokens per block
+constexpr int kScoreItems = 8;                                  // tokens per thread (indexer dim <= 16)
+constexpr int kScoreTile = kScoreThreads * kScoreItems;         // tokens per block (indexer dim <= 16)
+constexpr int score_items(int idx) { return idx <= 16 ? kScoreItems : kScoreItems / 2; }
+constexpr int score_tile(int idx) { return kScoreThreads * score_items(idx); }
 size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
 
 // Top-p selection (four launches; the workspace is zero before and after a call).

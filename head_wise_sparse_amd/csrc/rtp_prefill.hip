@@ -363,36 +363,46 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
 
 // Indexer keys of the chunk: k_idx[r][c0 + t][:] = bf16(k_pre[t][g(r)][:] . W_k_idx[r]).
 // One wave per 16 tokens on v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of
-// k_pre (one 16-byte load per lane and step), B = W^T staged in LDS.
+// k_pre (one 16-byte load per lane and step), B = W^T staged in LDS, one 16-column
+// block per 16 indexer outputs (dims 4 and 8 use one block, zero-padded).
+template <int IDX>
 __global__ __launch_bounds__(256) void k_kidx_proj(const uint16_t* __restrict__ k_pre,
                                                    const uint16_t* __restrict__ w_k, int64_t w_stride,
                                                    uint16_t* __restrict__ k_idx, int64_t c0, int C, int Hkv,
                                                    int64_t n_cap, HeadMap ret) {
+  constexpr int NCB = IDX > 16 ? IDX / 16 : 1;                  // 16-column output blocks
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = blockIdx.y;
   const int g = ret.kv[r];
-  __shared__ uint16_t s_wt[kIdxDim][PD + 8];                   // W^T: [out][d]
-  for (int i = tid; i < PD * kIdxDim; i += 256) {
-    const int d = i / kIdxDim, c = i % kIdxDim;
-    s_wt[c][d] = w_k[int64_t(r) * w_stride + i];
+  __shared__ uint16_t s_wt[16 * NCB][PD + 8];                   // W^T: [out][d]
+  for (int i = tid; i < PD * 16 * NCB; i += 256) {
+    const int d = i / (16 * NCB), c = i % (16 * NCB);
+    s_wt[c][d] = c < IDX ? w_k[int64_t(r) * w_stride + d * IDX + c] : uint16_t(0);
   }
   __syncthreads();
   const int t0 = (blockIdx.x * 4 + wave) * 16;                 // first token of this wave
   const int row = lane & 15, kq = lane >> 4;
   const int tok = min(t0 + row, C - 1);
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int st = 0; st < PD / 32; ++st) {
     const uint4 av = *reinterpret_cast<const uint4*>(k_pre + (int64_t(tok) * Hkv + g) * PD + 32 * st + 8 * kq);
-    const uint4 bv = *reinterpret_cast<const uint4*>(&s_wt[row][32 * st + 8 * kq]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint4 bv = *reinterpret_cast<const uint4*>(&s_wt[cb * 16 + row][32 * st + 8 * kq]);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[cb], 0, 0, 0);
+    }
   }
   // D (16 x 16): lane holds output column (lane & 15), token rows 4*(lane>>4) + v
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = t0 + 4 * kq + v;
-    if (t < C) k_idx[(int64_t(r) * n_cap + c0 + t) * kIdxDim + row] = f32_to_bf16(acc[v]);
-  }
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + 4 * kq + v, col = cb * 16 + row;
+      if (t < C && col < IDX) k_idx[(int64_t(r) * n_cap + c0 + t) * IDX + col] = f32_to_bf16(acc[cb][v]);
+    }
 }
 
 }  // namespace
@@ -433,8 +443,18 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
     return fail(RTP_EINVAL, "rtp_prefill_attn: tensors must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (L.n_ret > 0) {
-    hipLaunchKernelGGL(k_kidx_proj, dim3((C + 63) / 64, L.n_ret), dim3(256), 0, s, k_pre, w_k_idx, w_head_stride,
-                       k_idx_cache, c0, C, L.Hkv, L.n_cap, ret_map(L));
+    const dim3 pg((C + 63) / 64, L.n_ret);
+    const HeadMap rm = ret_map(L);
+    switch (L.idx) {
+      case 4: hipLaunchKernelGGL(k_kidx_proj<4>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache, c0,
+                                 C, L.Hkv, L.n_cap, rm); break;
+      case 8: hipLaunchKernelGGL(k_kidx_proj<8>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache, c0,
+                                 C, L.Hkv, L.n_cap, rm); break;
+      case 16: hipLaunchKernelGGL(k_kidx_proj<16>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache,
+                                  c0, C, L.Hkv, L.n_cap, rm); break;
+      default: hipLaunchKernelGGL(k_kidx_proj<32>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache,
+                                  c0, C, L.Hkv, L.n_cap, rm); break;
+    }
     if ((st = check_launch("k_kidx_proj")) != RTP_OK) return st;
   }
   PrefArgs a{};

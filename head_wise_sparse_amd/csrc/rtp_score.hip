@@ -19,9 +19,9 @@ using namespace rtp_dev;
 
 namespace {
 
-template <int G, int D>
+template <int G, int D, int IDX>
 __global__ __launch_bounds__(kScoreThreads) void k_indexer_score(ScoreArgs A) {
-  score_block<G, D>(A, blockIdx.x, blockIdx.y);
+  score_block<G, D, IDX>(A, blockIdx.x, blockIdx.y);
 }
 
 // One wave per score row: combine the per-block partials into (row_max, row_sum).
@@ -30,9 +30,25 @@ __global__ __launch_bounds__(64) void k_score_finalize(const float2* __restrict_
   score_finalize_row(part, nblk, row_max, row_sum, blockIdx.x);
 }
 
-template <int G, int D>
+template <int G, int D, int IDX>
 void launch_score(dim3 grid, hipStream_t st, const ScoreArgs& A) {
-  hipLaunchKernelGGL((k_indexer_score<G, D>), grid, dim3(kScoreThreads), 0, st, A);
+  hipLaunchKernelGGL((k_indexer_score<G, D, IDX>), grid, dim3(kScoreThreads), 0, st, A);
+}
+
+template <int IDX>
+bool dispatch_score(const Layer& L, dim3 grid, hipStream_t s, const ScoreArgs& A) {
+#define RTP_SCORE_CASE(GG, DD)                      \
+  if (L.G == GG && L.D == DD) {                     \
+    launch_score<GG, DD, IDX>(grid, s, A);          \
+    return true;                                    \
+  }
+  RTP_SCORE_CASE(1, 64) RTP_SCORE_CASE(2, 64) RTP_SCORE_CASE(4, 64)
+  RTP_SCORE_CASE(1, 128) RTP_SCORE_CASE(2, 128) RTP_SCORE_CASE(4, 128)
+  if constexpr (IDX <= 16) {
+    RTP_SCORE_CASE(8, 64) RTP_SCORE_CASE(8, 128)
+  }
+#undef RTP_SCORE_CASE
+  return false;
 }
 
 }  // namespace
@@ -60,17 +76,20 @@ extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ct
     return fail(RTP_EWORKSPACE, "rtp_indexer_score: workspace needs %zu bytes, 256-aligned (got %zu)", need,
                 ws_bytes);
 
-  const int nblk = int((n_ctx + kScoreTile - 1) / kScoreTile);
+  const int nblk = int((n_ctx + score_tile(L.idx) - 1) / score_tile(L.idx));
   const dim3 grid(nblk, L.B * L.n_ret);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws);
   const ScoreArgs A{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, int(n_ctx), L.n_cap, L.Hq,
                     ret_map(L), nblk};
-#define RTP_SCORE_CASE(GG, DD) \
-  if (L.G == GG && L.D == DD) launch_score<GG, DD>(grid, s, A);
-  RTP_SCORE_CASE(1, 64) RTP_SCORE_CASE(2, 64) RTP_SCORE_CASE(4, 64) RTP_SCORE_CASE(8, 64)
-  RTP_SCORE_CASE(1, 128) RTP_SCORE_CASE(2, 128) RTP_SCORE_CASE(4, 128) RTP_SCORE_CASE(8, 128)
-#undef RTP_SCORE_CASE
+  bool launched = false;
+  switch (L.idx) {
+    case 4: launched = dispatch_score<4>(L, grid, s, A); break;
+    case 8: launched = dispatch_score<8>(L, grid, s, A); break;
+    case 16: launched = dispatch_score<16>(L, grid, s, A); break;
+    case 32: launched = dispatch_score<32>(L, grid, s, A); break;
+  }
+  if (!launched) return fail(RTP_EUNSUPPORTED, "rtp_indexer_score: unsupported head_dim/group/idx_dim");
   if ((st = check_launch("k_indexer_score")) != RTP_OK) return st;
   hipLaunchKernelGGL(k_score_finalize, dim3(L.B * L.n_ret * L.G), dim3(64), 0, s, part, nblk, row_max, row_sum);
   return check_launch("k_score_finalize");

@@ -152,6 +152,8 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
     return fail(RTP_EWORKSPACE, "rtp_decode_step: workspace needs %zu bytes, 256-aligned (got %zu)", lay.total,
                 ws_bytes);
   if (!L.n_ret && !L.n_loc) return ok();
+  if (L.n_ret && L.idx != kIdxDim)
+    return fail(RTP_EUNSUPPORTED, "rtp_decode_step: idx_dim %d needs the separate calls (fused: 16)", L.idx);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   const int n = int(n_ctx);

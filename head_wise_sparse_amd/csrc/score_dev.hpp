@@ -24,9 +24,13 @@ struct ScoreArgs {
   int nblk;
 };
 
-// One block of the indexer scoring: token tile `blk` of group `grp` (= b * n_ret + r).
-template <int G, int D>
+// One block of the indexer scoring: token tile `blk` of group `grp` (= b * n_ret + r),
+// indexer dimension IDX (16 on the pages' design).
+template <int G, int D, int IDX = kIdxDim>
 __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp) {
+  constexpr int ITEMS = score_items(IDX);
+  constexpr int TILE = score_tile(IDX);
+  constexpr int KW = IDX / 2;                             // 32-bit words of one indexer key
   const uint16_t* __restrict__ q_pre = A.q_pre;
   const uint16_t* __restrict__ w_q = A.w_q;
   const int64_t w_stride = A.w_stride;
@@ -46,12 +50,12 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
   // LDS: raw bf16 q_pre rows and projection matrices of the group (padded so that every
   // lane of a direct-to-LDS load has a slot), the fp32 q_idx vectors, reduction scratch
   constexpr int QV = G * D / 8;                           // 16-byte pieces of q_pre
-  constexpr int WV = G * D * kIdxDim / 8;                 // 16-byte pieces of the G matrices
+  constexpr int WV = G * D * IDX / 8;                     // 16-byte pieces of the G matrices
   constexpr int QV_PAD = QV < 64 ? 64 : QV;
   constexpr int WPT = (WV + kScoreThreads - 1) / kScoreThreads;
   __shared__ uint4 s_qraw[QV_PAD];
   __shared__ uint4 s_w[WPT * kScoreThreads];
-  __shared__ float s_qidx[G][kIdxDim];
+  __shared__ float s_qidx[G][IDX];
   __shared__ float s_red[kScoreThreads / 64][G];
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   typedef __attribute__((address_space(1))) const void* glb_ptr_t;
@@ -68,70 +72,81 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
     const int pidx = min(i * kScoreThreads + tid, WV - 1);
-    const int t = pidx / (D * kIdxDim / 8), off = pidx % (D * kIdxDim / 8);
+    const int t = pidx / (D * IDX / 8), off = pidx % (D * IDX / 8);
     const uint16_t* src = w_q + int64_t(r * G + t) * w_stride + off * 8;
     __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(s_w + i * kScoreThreads + wave * 64), 16, 0, 0);
   }
-  // this tile's keys: thread tid takes tokens base + it*256 + tid (coalesced 32-byte rows)
-  const int64_t base = int64_t(blk) * kScoreTile;
-  const uint4* kp = reinterpret_cast<const uint4*>(k_idx + int64_t(grp) * n_cap * kIdxDim);
-  uint4 kr[kScoreItems][2];
+  // this tile's keys: thread tid takes tokens base + it*256 + tid (coalesced 2*IDX-byte rows)
+  const int64_t base = int64_t(blk) * TILE;
+  const uint16_t* kp = k_idx + int64_t(grp) * n_cap * IDX;
+  uint32_t kw[ITEMS][KW];
 #pragma unroll
-  for (int it = 0; it < kScoreItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     int64_t j = base + it * kScoreThreads + tid;
     j = j < n_ctx ? j : n_ctx - 1;
-    kr[it][0] = kp[2 * j];
-    kr[it][1] = kp[2 * j + 1];
+    if constexpr (IDX == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(kp + j * IDX);
+      kw[it][0] = u.x;
+      kw[it][1] = u.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < IDX / 8; ++c) {
+        const uint4 u = reinterpret_cast<const uint4*>(kp + j * IDX)[c];
+        kw[it][4 * c] = u.x;
+        kw[it][4 * c + 1] = u.y;
+        kw[it][4 * c + 2] = u.z;
+        kw[it][4 * c + 3] = u.w;
+      }
+    }
   }
   // wait for the LDS-direct loads only: vmcnt retires in issue order, so leaving the
-  // 2*kScoreItems key loads outstanding is vmcnt(2*kScoreItems)
-  static_assert(2 * kScoreItems < 64, "vmcnt field");
-  constexpr int NK = 2 * kScoreItems;
+  // NK key loads outstanding is vmcnt(NK)
+  constexpr int NK = ITEMS * (IDX >= 8 ? IDX / 8 : 1);
+  static_assert(NK < 64, "vmcnt field");
   __builtin_amdgcn_s_waitcnt((NK & 0xF) | ((NK >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   __builtin_amdgcn_s_barrier();   // a bare barrier: __syncthreads' fence would wait for the key loads too
 
   // ---- q_idx = q_pre . W_q_idx for the G heads of this group (fp32, not rounded)
   {
-    constexpr int P = kScoreThreads / (G * kIdxDim);     // threads per output
+    constexpr int P = kScoreThreads / (G * IDX);         // threads per output
+    static_assert(P >= 1 && P <= 64, "one wave reduces an output");
     const int o = tid / P, pi = tid % P;
-    const int t = o / kIdxDim, c = o % kIdxDim;
-    const uint16_t* w = reinterpret_cast<const uint16_t*>(s_w) + t * D * kIdxDim;
+    const int t = o / IDX, c = o % IDX;
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(s_w) + t * D * IDX;
     const uint16_t* qr = reinterpret_cast<const uint16_t*>(s_qraw) + t * D;
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < D / P; ++i) {
       const int d = pi + i * P;
-      acc = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(w[d * kIdxDim + c]), acc);
+      acc = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(w[d * IDX + c]), acc);
     }
 #pragma unroll
     for (int off = P / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (pi == 0) s_qidx[t][c] = acc * idx_scale;
   }
   __syncthreads();
-  float qi[G][kIdxDim];
+  float qi[G][IDX];
 #pragma unroll
   for (int t = 0; t < G; ++t)
 #pragma unroll
-    for (int c = 0; c < kIdxDim; ++c) qi[t][c] = s_qidx[t][c];
+    for (int c = 0; c < IDX; ++c) qi[t][c] = s_qidx[t][c];
 
   // ---- score the tile (keys were loaded before the q_idx prologue)
-  float sc[kScoreItems][G];
+  float sc[ITEMS][G];
 #pragma unroll
-  for (int it = 0; it < kScoreItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kScoreThreads + tid;
-    float kf[kIdxDim];
-    const uint32_t w8[8] = {kr[it][0].x, kr[it][0].y, kr[it][0].z, kr[it][0].w,
-                            kr[it][1].x, kr[it][1].y, kr[it][1].z, kr[it][1].w};
+    float kf[IDX];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kf[2 * e] = bf16_lo(w8[e]);
-      kf[2 * e + 1] = bf16_hi(w8[e]);
+    for (int e = 0; e < KW; ++e) {
+      kf[2 * e] = bf16_lo(kw[it][e]);
+      kf[2 * e + 1] = bf16_hi(kw[it][e]);
     }
 #pragma unroll
     for (int t = 0; t < G; ++t) {
       float s = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kIdxDim; ++c) s = fmaf(qi[t][c], kf[c], s);
+      for (int c = 0; c < IDX; ++c) s = fmaf(qi[t][c], kf[c], s);
       sc[it][t] = (j < n_ctx) ? s : -INFINITY;
       if (j < n_ctx) scores[(int64_t(grp) * G + t) * n_cap + j] = s;
     }
@@ -143,7 +158,7 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
   for (int t = 0; t < G; ++t) {
     float m = -INFINITY;
 #pragma unroll
-    for (int it = 0; it < kScoreItems; ++it) m = fmaxf(m, sc[it][t]);
+    for (int it = 0; it < ITEMS; ++it) m = fmaxf(m, sc[it][t]);
     m = wave_max(m);
     if (lane == 0) s_red[wave][t] = m;
   }
@@ -160,7 +175,7 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
   for (int t = 0; t < G; ++t) {
     float z = 0.0f;
 #pragma unroll
-    for (int it = 0; it < kScoreItems; ++it) z += __expf(sc[it][t] - mt[t]);
+    for (int it = 0; it < ITEMS; ++it) z += __expf(sc[it][t] - mt[t]);
     z = wave_sum(z);
     if (lane == 0) s_red[wave][t] = z;
   }

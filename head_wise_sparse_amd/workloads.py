@@ -122,6 +122,7 @@ class DecodeConfig:
     window: int
     n_needles: int
     lognormal_qscale: bool
+    idx_dim: int = IDX_DIM      # indexer dimension (16 on the pages' design; 4 / 8 / 32 for the ablation)
 
     @property
     def group(self) -> int:
@@ -152,6 +153,7 @@ class PrefillConfig:
     n_sinks: int
     window: int
     rows_per_head: int          # query rows per head the oracle checks
+    idx_dim: int = IDX_DIM
 
     @property
     def group(self) -> int:
@@ -235,10 +237,11 @@ def make_decode_inputs(cfg: DecodeConfig, n_cap: Optional[int] = None,
     Hkv_r, Hq_r = len(ret), len(ret) * G
     cid = cfg.cid
 
-    w_q = np.stack([_normal_bf16(_rng(cid, T_WQ, 0, i), (D, IDX_DIM), 1.0 / np.sqrt(D)) for i in range(Hq_r)]) \
-        if Hq_r else np.zeros((0, D, IDX_DIM), np.uint16)
-    w_k = np.stack([_normal_bf16(_rng(cid, T_WK, 0, i), (D, IDX_DIM), 1.0 / np.sqrt(D)) for i in range(Hkv_r)]) \
-        if Hkv_r else np.zeros((0, D, IDX_DIM), np.uint16)
+    I = cfg.idx_dim
+    w_q = np.stack([_normal_bf16(_rng(cid, T_WQ, 0, i), (D, I), 1.0 / np.sqrt(D)) for i in range(Hq_r)]) \
+        if Hq_r else np.zeros((0, D, I), np.uint16)
+    w_k = np.stack([_normal_bf16(_rng(cid, T_WK, 0, i), (D, I), 1.0 / np.sqrt(D)) for i in range(Hkv_r)]) \
+        if Hkv_r else np.zeros((0, D, I), np.uint16)
 
     q_scale = np.ones((B, Hq), np.float32)
     if cfg.lognormal_qscale:
@@ -255,7 +258,7 @@ def make_decode_inputs(cfg: DecodeConfig, n_cap: Optional[int] = None,
 
     k = np.zeros((B, Hkv, ncap, D), np.uint16)
     v = np.zeros((B, Hkv, ncap, D), np.uint16)
-    k_idx = np.zeros((B, Hkv_r, ncap, IDX_DIM), np.uint16)
+    k_idx = np.zeros((B, Hkv_r, ncap, I), np.uint16)
     n_needles = min(cfg.n_needles, N)
     needle_pos = np.zeros((B, Hkv_r, n_needles), np.int64)
     pos = np.arange(N)
@@ -296,7 +299,7 @@ class PrefillInputs:
     def __init__(self, cfg: PrefillConfig):
         self.cfg = cfg
         D, Hkv_r = cfg.head_dim, cfg.n_kv_r
-        self.w_k_idx = np.stack([_normal_bf16(_rng(cfg.cid, T_WK, 0, i), (D, IDX_DIM), 1.0 / np.sqrt(D))
+        self.w_k_idx = np.stack([_normal_bf16(_rng(cfg.cid, T_WK, 0, i), (D, cfg.idx_dim), 1.0 / np.sqrt(D))
                                  for i in range(Hkv_r)])
         self.kv_role = cfg.kv_role
 

@@ -43,8 +43,8 @@
  *    g*G .. g*G+G-1.  Retrieval KV heads (kv_role[g] == 1) are numbered by rank
  *    r = 0,1,.. in increasing g; retrieval query head g*G+t has the compact index
  *    r*G + t, which indexes w_q_idx, scores, row stats and selected sets.
- *  - Supported: head_dim 64 or 128; G in {1,2,4,8}; idx_dim == 16;
- *    n_cap < 2^30; batch >= 1 (prefill: batch == 1).
+ *  - Supported: head_dim 64 or 128; G in {1,2,4,8}; idx_dim in {4,8,16,32};
+ *    n_cap < 2^30; batch >= 1 (prefill: batch == 1).  I below = idx_dim.
  */
 #ifndef RTP_H
 #define RTP_H
@@ -70,7 +70,9 @@ typedef struct rtp_layer_desc {
   int32_t n_q_heads;      /* Hq */
   int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;       /* D */
-  int32_t idx_dim;        /* indexer dimension; must be 16 (abstract, observation (2)) */
+  int32_t idx_dim;        /* indexer dimension: 16 on the pages' design (abstract, observation
+                             (2)); 4, 8 and 32 for the ablation (summary, "Surprising
+                             findings"); 32 needs G <= 4; rtp_decode_step needs 16 */
   int64_t n_cap;          /* cache capacity = token stride of every per-token tensor */
   const uint8_t* kv_role; /* [Hkv] HOST array: 1 = retrieval head, 0 = local head */
   int32_t n_sinks;        /* local heads: sink tokens at the start of the sequence (>= 0) */
@@ -120,9 +122,9 @@ size_t rtp_workspace_bytes(const rtp_layer_desc* desc, int64_t n_ctx, int which)
  *   row_max[b,c] = max_j s[b,c,j];   row_sum[b,c] = sum_j exp(s[b,c,j] - row_max[b,c])
  *
  *   q_pre   bf16 [B][Hq][D]         pre-RoPE queries (all heads; only retrieval heads read)
- *   w_q_idx bf16 [Hq_r][D][16]      query projections; head c starts at c*w_head_stride
+ *   w_q_idx bf16 [Hq_r][D][I]       query projections; head c starts at c*w_head_stride
  *                                   elements (w_head_stride == 0: one matrix shared by all)
- *   k_idx   bf16 [B][Hkv_r][n_cap][16]  stored pre-RoPE key projections
+ *   k_idx   bf16 [B][Hkv_r][n_cap][I]   stored pre-RoPE key projections
  *   scores  fp32 [B][Hq_r][n_cap]   written for j < n_ctx
  *   row_max, row_sum fp32 [B][Hq_r]
  * n_ctx in [1, n_cap].  A layer with no retrieval head is valid and does nothing.
@@ -230,8 +232,8 @@ rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n_ctx,
  *   k_cache, v_cache bf16 [Hkv][n_cap][D]: rows [0, c0 + C) valid (the caller has
  *            appended the chunk's post-RoPE keys and values)
  *   k_pre    bf16 [C][Hkv][D] pre-RoPE keys of the chunk (retrieval heads read)
- *   w_k_idx  bf16 [Hkv_r][D][16]; head r starts at r*w_head_stride (0 = shared)
- *   k_idx_cache bf16 [Hkv_r][n_cap][16]: rows [c0, c0+C) are written
+ *   w_k_idx  bf16 [Hkv_r][D][I]; head r starts at r*w_head_stride (0 = shared)
+ *   k_idx_cache bf16 [Hkv_r][n_cap][I]: rows [c0, c0+C) are written
  *   out      bf16 [C][Hq][D]
  * Requires c0 >= 0, C >= 1, c0 + C <= n_cap, head_dim == 128.
  */
@@ -283,11 +285,11 @@ rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
  * one rounding; abstract, observation (2); summary, "Approach").
  *
  *   k_new, v_new  bf16 [B][Hkv][D] post-RoPE;  k_pre bf16 [B][Hkv][D] pre-RoPE
- *   w_k_idx       bf16 [Hkv_r][D][16], head r at r*w_head_stride (0 = shared)
+ *   w_k_idx       bf16 [Hkv_r][D][I], head r at r*w_head_stride (0 = shared)
  *   RTP_KV_FULL:    k_cache/v_cache [B][Hkv][n_cap][D]; k_loc/v_loc ignored
  *   RTP_KV_COMPACT: k_cache/v_cache [B][Hkv_r][n_cap][D] (retrieval heads) and
  *                   k_loc/v_loc [B][Hkv_l][n_sinks + window][D] (the ring)
- *   k_idx_cache   bf16 [B][Hkv_r][n_cap][16]
+ *   k_idx_cache   bf16 [B][Hkv_r][n_cap][I]
  * Requires 0 <= pos < n_cap.  Pointers of a head kind the layer lacks may be NULL.
  */
 rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos,

@@ -228,7 +228,8 @@ def prefill_kidx(k_pre: np.ndarray, w_k_idx: np.ndarray, kv_role) -> np.ndarray:
     retrieval KV head (pre-RoPE projection, summary "Approach"; the cache keeps
     the per-token 16-dim keys of retrieval heads, abstract).
 
-    k_pre: [C][Hkv][D] bf16 bits; w_k_idx: [Hkv_r][D][16] -> [Hkv_r][C][16] bf16 bits.
+    k_pre: [C][Hkv][D] bf16 bits; w_k_idx: [Hkv_r][D][I] -> [Hkv_r][C][I] bf16 bits (I = 16 on
+    the pages' design; the same projection for the other indexer dimensions).
     """
     roles = np.asarray(kv_role)
     ret = [g for g in range(len(roles)) if roles[g]]
@@ -236,7 +237,7 @@ def prefill_kidx(k_pre: np.ndarray, w_k_idx: np.ndarray, kv_role) -> np.ndarray:
     for r, g in enumerate(ret):
         proj = bf16_to_f64(k_pre[:, g]) @ bf16_to_f64(w_k_idx[r])
         out.append(f64_to_bf16(proj))
-    return np.stack(out) if out else np.zeros((0, k_pre.shape[0], IDX_DIM), np.uint16)
+    return np.stack(out) if out else np.zeros((0, k_pre.shape[0], np.shape(w_k_idx)[-1]), np.uint16)
 
 
 def prefill_row_set(i: int, retrieval: bool, n_sinks: int, window: int) -> np.ndarray:

@@ -47,7 +47,8 @@ def dev(bits: np.ndarray):
 
 def layer_for(cfg, n_cap=None) -> rtp.Layer:
     return rtp.Layer(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
-                     cfg.n_ctx if n_cap is None else n_cap, cfg.kv_role.tolist(), cfg.n_sinks, cfg.window)
+                     cfg.n_ctx if n_cap is None else n_cap, cfg.kv_role.tolist(), cfg.n_sinks, cfg.window,
+                     idx_dim=cfg.idx_dim)
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:

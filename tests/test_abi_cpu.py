@@ -122,7 +122,8 @@ def _call_score(L, n_ctx=1000, ws_bytes=1 << 20, scale=1.0, ptr=FAKE):
     (dict(head_dim=96), rtp.RTP_EUNSUPPORTED, "head_dim"),
     (dict(n_q_heads=30), rtp.RTP_EINVAL, "multiple"),
     (dict(n_q_heads=24, n_kv_heads=2, kv_role=[1, 0]), rtp.RTP_EUNSUPPORTED, "group"),
-    (dict(idx_dim=32), rtp.RTP_EUNSUPPORTED, "idx_dim"),
+    (dict(idx_dim=12), rtp.RTP_EUNSUPPORTED, "idx_dim"),
+    (dict(idx_dim=32, n_q_heads=64), rtp.RTP_EUNSUPPORTED, "idx_dim 32"),
     (dict(window=0), rtp.RTP_EINVAL, "window"),
     (dict(n_sinks=-1), rtp.RTP_EINVAL, "n_sinks"),
     (dict(batch=0), rtp.RTP_EINVAL, "batch"),

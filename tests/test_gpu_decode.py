@@ -40,7 +40,11 @@ def _torch():
 # ----------------------------------------------------------------------------- indexer scores
 @pytest.mark.parametrize("name,over", [("decode_tiny_2k", {}), ("decode_b8_32k", {}),
                                        ("decode_b8_32k", dict(n_ctx=3001, batch=2)),
-                                       ("decode_b4_128k", {})])
+                                       ("decode_b4_128k", {}),
+                                       ("decode_b8_32k", dict(n_ctx=5000, batch=2, idx_dim=4)),
+                                       ("decode_b8_32k", dict(n_ctx=5000, batch=2, idx_dim=8)),
+                                       ("decode_b8_32k", dict(n_ctx=5000, batch=2, idx_dim=32)),
+                                       ("decode_tiny_2k", dict(idx_dim=4))])
 def test_indexer_scores(name, over):
     P.require_gpu()
     torch = _torch()
@@ -52,7 +56,8 @@ def test_indexer_scores(name, over):
     rmax = torch.empty(B * R, dtype=torch.float32, device="cuda")
     rsum = torch.empty(B * R, dtype=torch.float32, device="cuda")
     ws = rtp.workspace(L, N, rtp.CALL_INDEXER_SCORE)
-    rtp.rtp_indexer_score(L, N, d.q_pre, d.w_q_idx, cfg.head_dim * 16, d.k_idx, 1.0, scores, rmax, rsum, ws)
+    rtp.rtp_indexer_score(L, N, d.q_pre, d.w_q_idx, cfg.head_dim * cfg.idx_dim, d.k_idx, 1.0, scores, rmax, rsum,
+                          ws)
     torch.cuda.synchronize()
     sg = scores.view(B, R, N).cpu().numpy().astype(np.float64)
     mg, zg = rmax.view(B, R).cpu().numpy(), rsum.view(B, R).cpu().numpy()
@@ -656,3 +661,38 @@ def test_append_then_decode_both_layouts():
                     ref = O.attend(O.bf16_to_f64(x.q[b, h]), O.bf16_to_f64(kk[b, h // cfg.group, :pos + 1]),
                                    O.bf16_to_f64(vv[b, h // cfg.group, :pos + 1]), lset, 1 / math.sqrt(D))
                     P.check_outputs(g_out[b, h][None], ref[None], f"local row ({b},{h}) after append")
+
+
+# ----------------------------------------------------------------------------- indexer dimensions
+@pytest.mark.parametrize("idx_dim", [4, 8, 32])
+def test_decode_step_other_indexer_dims(idx_dim):
+    """The separate calls with indexer dimensions 4 / 8 / 32 against the oracle (the fused
+    call takes 16 only and says so)."""
+    P.require_gpu()
+    x, d = _inputs("decode_b8_32k", batch=2, n_ctx=9000, idx_dim=idx_dim)
+    cfg = x.cfg
+    L = P.layer_for(cfg)
+    with pytest.raises(rtp.RtpError, match="idx_dim"):
+        rtp.DecodeStep(L, cfg.n_ctx, cfg.top_p, fused=True).run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+    step = rtp.DecodeStep(L, cfg.n_ctx, cfg.top_p, fused=False)
+    out = step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+    _torch().cuda.synchronize()
+    N, B, G = cfg.n_ctx, cfg.batch, cfg.group
+    R = cfg.n_kv_r * G
+    ora = O.decode_step(x.q_pre, x.q, x.k, x.v, x.k_idx, x.w_q_idx, x.kv_role, N, cfg.top_p, cfg.n_sinks, cfg.window)
+    g = rtp.from_device_bf16(out).reshape(B, cfg.n_q_heads, cfg.head_dim)
+    cnt = step.sel_count.view(B, R).cpu().numpy()
+    sel = step.sel_idx.view(B, R, N).cpu().numpy()
+    same_all = 0
+    for b in range(B):
+        for ci in range(R):
+            r = ci // G
+            same, _ = P.check_set(sel[b, ci, :cnt[b, ci]], ora["info"][(b, ci)], cfg.top_p, ora["scores"][(b, ci)],
+                                  P.FP32_SCORE_SLACK * P.score_scale(x, b, ci, r, N))
+            h = cfg.retrieval_kv[r] * G + ci % G
+            if same:
+                P.check_outputs(g[b, h][None], ora["out"][b, h][None], f"row ({b},{h})")
+            same_all += same
+    assert same_all >= 0.9 * B * R
+    loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
+    P.check_outputs(g[:, loc], ora["out"][:, loc], "local rows")

@@ -24,17 +24,18 @@ def _run_prefill(cfg, pi, k, v, kp, keep_rows=None):
     `keep_rows` is given, a dict row -> [Hq][D] holding only those rows."""
     import torch
     T, Hq, D = cfg.seq_len, cfg.n_q_heads, cfg.head_dim
-    L = rtp.Layer(1, Hq, cfg.n_kv_heads, D, T, cfg.kv_role.tolist(), cfg.n_sinks, cfg.window)
+    L = rtp.Layer(1, Hq, cfg.n_kv_heads, D, T, cfg.kv_role.tolist(), cfg.n_sinks, cfg.window, idx_dim=cfg.idx_dim)
+    I = cfg.idx_dim
     kd, vd = P.dev(k), P.dev(v)
     w = P.dev(pi.w_k_idx)
-    kidx = torch.zeros(cfg.n_kv_r * T * 16, dtype=torch.bfloat16, device="cuda")
+    kidx = torch.zeros(cfg.n_kv_r * T * I, dtype=torch.bfloat16, device="cuda")
     out = np.zeros((T, Hq, D), np.uint16) if keep_rows is None else {}
     ws = rtp.workspace(L, cfg.chunk, rtp.CALL_PREFILL)
     for c in range(cfg.n_chunks):
         c0, c1 = pi.chunk_bounds(c)
         q = P.dev(pi.q_chunk(c))
         o = torch.empty((c1 - c0) * Hq * D, dtype=torch.bfloat16, device="cuda")
-        rtp.rtp_prefill_attn(L, c0, c1 - c0, q, kd, vd, P.dev(kp[c0:c1]), w, D * 16, kidx, 1 / math.sqrt(D), o,
+        rtp.rtp_prefill_attn(L, c0, c1 - c0, q, kd, vd, P.dev(kp[c0:c1]), w, D * I, kidx, 1 / math.sqrt(D), o,
                              ws)
         torch.cuda.synchronize()
         ob = rtp.from_device_bf16(o).reshape(c1 - c0, Hq, D)
@@ -44,7 +45,7 @@ def _run_prefill(cfg, pi, k, v, kp, keep_rows=None):
             for r in keep_rows:
                 if c0 <= r < c1:
                     out[int(r)] = ob[r - c0]
-    return out, rtp.from_device_bf16(kidx).reshape(cfg.n_kv_r, T, 16)
+    return out, rtp.from_device_bf16(kidx).reshape(cfg.n_kv_r, T, I)
 
 
 def _check_rows(cfg, pi, k, v, out, rows_of_head):
@@ -95,6 +96,9 @@ def _check_kidx(cfg, pi, kp, kidx):
     dict(seq_len=640, chunk=192, window=1, n_sinks=0),            # query token only
     dict(seq_len=600, chunk=128, window=70, n_sinks=0),           # no sinks: first rows see few keys
     dict(seq_len=900, chunk=300, window=130, n_sinks=77),         # sinks span two key tiles
+    dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=4),   # indexer dims of the ablation
+    dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=8),
+    dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=32),
 ])
 def test_prefill_small_all_rows(over):
     P.require_gpu()
