@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0
 # changes the figure no longer describes the kernel and `traffic` is reported as null.
 COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
 MEASURED_KIB = {
-    "prefill_attn": {"src": ("rtp_prefill.hip", "0841fa6519701399"),
-                     "fetch": 1074.0 + 204736.5, "write": 256.0 + 32768.6},
-    "sparse_decode": {"src": ("rtp_decode.hip", "890b671f5d4fa52d"),
-                      "fetch": 2083.3 + 172603.8 + 946.0, "write": 54.6 + 2176.3 + 16.0},
+    "prefill_attn": {"src": ("rtp_prefill.hip", "281cf431e1d009b8"),
+                     "fetch": 1076.6 + 197398.6, "write": 256.0 + 32768.2},
+    "sparse_decode": {"src": ("decode_dev.hpp", "b858cb291012f65b"),
+                      "fetch": 172601.6 + 947.5, "write": 2176.3 + 16.0},
 }
 
 
