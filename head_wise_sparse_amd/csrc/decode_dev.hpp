@@ -44,7 +44,7 @@ struct DecArgs {
   const uint16_t* v;
   const int32_t* sel_idx;     // sparse only
   const int32_t* starts;      // sparse only: [rows][nsplit + 1]
-  float* part;                // [rows][nsplit][D + 2]
+  float* part;                // [rows][nsplit][D + 4]: accumulator, max, sum (16-byte rows)
   int n_ctx;
   int64_t n_cap;
   int Hq, Hkv;
@@ -307,7 +307,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
       A += s_wacc[w][t][d] * f;
       Lsum += s_wl[w][t] * f;
     }
-    float* pr = a.part + ((int64_t(grp) * G + t) * a.nsplit + split) * (D + 2);
+    float* pr = a.part + ((int64_t(grp) * G + t) * a.nsplit + split) * (D + 4);
     pr[d] = A;
     if (d == 0) {
       pr[D] = M;
@@ -317,10 +317,11 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
 }
 
 // Combine the per-slice partials of one (batch, head) row into the bf16 output.
-// 256 threads per row: SG = 256/D split groups, each thread sums the splits of its group
-// for one output dimension (independent loads, unrolled), then the groups are combined.
+// 256 threads per row: D/4 lanes read one split's accumulator as float4s, 256/(D/4)
+// split groups take every SG-th split (independent loads, unrolled), then the groups
+// are combined in LDS.
 struct MergeArgs {
-  const float* part;           // [rows][nsplit][D + 2]
+  const float* part;           // [rows][nsplit][D + 4]
   int nsplit;
   int G, Hq;
   HeadMap map;
@@ -329,47 +330,58 @@ struct MergeArgs {
 
 template <int D>
 __device__ __forceinline__ void merge_row(const MergeArgs& ma, int row) {
+  constexpr int PS = D + 4;                 // partial row stride (floats)
+  constexpr int Q = D / 4;                  // float4 columns
+  constexpr int SG = 256 / Q;               // split groups
   const float* __restrict__ part = ma.part;
   const int nsplit = ma.nsplit, G = ma.G, Hq = ma.Hq;
   const HeadMap& map = ma.map;
   uint16_t* __restrict__ out = ma.out;
-  constexpr int SG = 256 / D;
   const int tid = threadIdx.x;
-  const int d = tid % D, sg = tid / D;
+  const int q = tid % Q, sg = tid / Q;
   const int grp = row / G, t = row % G;
   const int b = grp / map.n, rr = grp % map.n;
   const int h = map.kv[rr] * G + t;
-  const float* pr = part + int64_t(row) * nsplit * (D + 2);
+  const float* pr = part + int64_t(row) * nsplit * PS;
   __shared__ float s_red[4];
-  __shared__ float s_a[SG][D], s_l[SG][D];
+  __shared__ float4 s_a[SG][Q];
+  __shared__ float s_l[SG];
   // reference max over the splits
   float M = -INFINITY;
-  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, pr[int64_t(s) * (D + 2) + D]);
+  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, pr[int64_t(s) * PS + D]);
   M = wave_max(M);
   if ((tid & 63) == 0) s_red[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float A = 0.0f, Lsum = 0.0f;
+  float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float Lsum = 0.0f;
   if (M != -INFINITY) {
 #pragma unroll 4
     for (int s = sg; s < nsplit; s += SG) {
-      const float* ps = pr + int64_t(s) * (D + 2);
+      const float* ps = pr + int64_t(s) * PS;
       const float ms = ps[D];
       const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
-      A = fmaf(ps[d], f, A);
+      const float4 o = *reinterpret_cast<const float4*>(ps + 4 * q);
+      A.x = fmaf(o.x, f, A.x);
+      A.y = fmaf(o.y, f, A.y);
+      A.z = fmaf(o.z, f, A.z);
+      A.w = fmaf(o.w, f, A.w);
       Lsum = fmaf(ps[D + 1], f, Lsum);
     }
   }
-  s_a[sg][d] = A;
-  s_l[sg][d] = Lsum;
+  s_a[sg][q] = A;
+  if (q == 0) s_l[sg] = Lsum;
   __syncthreads();
-  if (sg == 0) {
+  if (tid < D) {
+    const int qq = tid >> 2, e = tid & 3;
+    float a = 0.0f, l = 0.0f;
 #pragma unroll
-    for (int i = 1; i < SG; ++i) {
-      A += s_a[i][d];
-      Lsum += s_l[i][d];
+    for (int i = 0; i < SG; ++i) {
+      const float4 v = s_a[i][qq];
+      a += e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+      l += s_l[i];
     }
-    out[(int64_t(b) * Hq + h) * D + d] = f32_to_bf16(Lsum > 0.0f ? A / Lsum : 0.0f);
+    out[(int64_t(b) * Hq + h) * D + tid] = f32_to_bf16(l > 0.0f ? a / l : 0.0f);
   }
 }
 

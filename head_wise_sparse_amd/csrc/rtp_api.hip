@@ -119,7 +119,7 @@ SelLayout sel_layout(const Layer& L) {
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx) {
   const int64_t nsplit = (n_ctx + kDecRange - 1) / kDecRange;
   const size_t rows = size_t(L.B) * L.n_ret * L.G;
-  return round_up(rows * size_t(nsplit) * (L.D + 2) * sizeof(float), 256);
+  return round_up(rows * size_t(nsplit) * (L.D + 4) * sizeof(float), 256);
 }
 
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
@@ -136,7 +136,7 @@ size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
     nsplit = (len + kWinRange - 1) / kWinRange;
     rows = size_t(L.B) * L.n_loc * L.G;
   }
-  return round_up(rows * size_t(nsplit) * (L.D + 2) * sizeof(float), 256);
+  return round_up(rows * size_t(nsplit) * (L.D + 4) * sizeof(float), 256);
 }
 
 }  // namespace rtp

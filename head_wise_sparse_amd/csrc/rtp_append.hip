@@ -57,13 +57,23 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
     reinterpret_cast<uint4*>(vd)[lane] = reinterpret_cast<const uint4*>(a.v_new + src)[lane];
   }
   if (!ret) return;
-  // k_idx[b][r][pos][c] = bf16(sum_d k_pre[d] * W[r][d][c]): the 64 / idx lanes of output c
-  // split d, then a lane-group sum
+  // k_idx[b][r][pos][c] = bf16(sum_d k_pre[d] * W[r][d][c]).  The key row and the matrix
+  // are staged in LDS with 16-byte loads (all in flight at once); then the 64 / idx lanes
+  // of output c split d and a lane-group sum closes the dot product.
+  __shared__ uint4 s_w[128 * 32 / 8];
+  __shared__ uint4 s_kp[128 / 8];
+  const uint4* wg = reinterpret_cast<const uint4*>(a.w_k + int64_t(r) * a.w_stride);
+  const int nw = a.D * a.idx / 8;
+#pragma unroll 8
+  for (int i = lane; i < nw; i += 64) s_w[i] = wg[i];
+  if (lane < a.D / 8) s_kp[lane] = reinterpret_cast<const uint4*>(a.k_pre + src)[lane];
+  __syncthreads();
+  const uint16_t* w = reinterpret_cast<const uint16_t*>(s_w);
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(s_kp);
   const int lpo = 64 / a.idx;
   const int c = lane / lpo, part = lane % lpo;
-  const uint16_t* w = a.w_k + int64_t(r) * a.w_stride;
   float acc = 0.0f;
-  for (int d = part; d < a.D; d += lpo) acc = fmaf(bf16_to_f32(a.k_pre[src + d]), bf16_to_f32(w[d * a.idx + c]), acc);
+  for (int d = part; d < a.D; d += lpo) acc = fmaf(bf16_to_f32(kp[d]), bf16_to_f32(w[d * a.idx + c]), acc);
   for (int o = 1; o < lpo; o <<= 1) acc += __shfl_xor(acc, o, 64);
   if (part == 0) a.k_idx[((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.idx + c] = f32_to_bf16(acc);
 }
@@ -85,9 +95,11 @@ extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, 
   if ((L.n_ret || !compact) && (!k_cache || !v_cache)) return fail(RTP_EINVAL, "rtp_append_token: NULL cache");
   if (compact && L.n_loc && (!k_loc || !v_loc)) return fail(RTP_EINVAL, "rtp_append_token: NULL local ring");
   if (L.n_ret && (!k_pre || !w_k_idx || !k_idx_cache)) return fail(RTP_EINVAL, "rtp_append_token: NULL indexer");
-  if (w_head_stride < 0) return fail(RTP_EINVAL, "w_head_stride must be >= 0");
+  if (w_head_stride < 0 || w_head_stride % 8 != 0)
+    return fail(RTP_EINVAL, "w_head_stride must be a non-negative multiple of 8 (got %lld)", (long long)w_head_stride);
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(k_loc, 16) || !aligned(v_loc, 16) || !aligned(k_idx_cache, 2) || !aligned(k_pre, 2))
+      !aligned(k_loc, 16) || !aligned(v_loc, 16) || !aligned(k_idx_cache, 2) || !aligned(k_pre, 16) ||
+      !aligned(w_k_idx, 16))
     return fail(RTP_EINVAL, "rtp_append_token: tensors must be 16-byte aligned");
   AppendArgs a{};
   a.pos = pos;
