@@ -113,7 +113,7 @@ rtp_status launch_select(const SelArgs& a, int rows, hipStream_t s);
 // Decode attention (sparse and window share the layout).
 constexpr int kDecThreads = 256;
 constexpr int kDecRange = RTP_SEL_RANGE; // token-index range per block (sparse path)
-constexpr int kWinRange = 128;           // list positions per block (window path)
+constexpr int kWinRange = 256;           // list positions per block (window path)
 constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);   // partials [rows][nsplit][D + 4]
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows][nsplit+1] after partials
