@@ -451,6 +451,24 @@ def main():
                                  "hbm_GBps": round(abp["total"] / (us * 1e-6) / 1e9, 1),
                                  "sel_mean": round(abp["sel_mean"], 1), "union_tokens": abp["union_tokens"]}
             res["decode"]["p_sweep"] = sweep
+    if dec:
+        # the device's practical HBM read rate (plain streaming read of 4 GiB), the ceiling
+        # the decode kernels' bandwidth is read against; the roofline peak stays 8 TB/s
+        buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            rtp.rtp_hbm_read_probe(buf, sink)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(5):
+            rtp.rtp_hbm_read_probe(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        read_tbs = 5 * buf.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e12
+        res["decode"]["hbm_read_probe_TBps"] = round(read_tbs, 2)
+        res["decode"]["frac_of_read_probe"] = round(res["decode"]["hbm_GBps"] / 1e3 / read_tbs, 4)
+        del buf
     if dec and args.gen_steps > 0:
         gen = GenBench(dec, args.gen_steps)
         gen.run()                            # warm-up (re-appending the same tokens is idempotent)

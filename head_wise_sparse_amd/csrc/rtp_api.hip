@@ -171,3 +171,35 @@ extern "C" const char* rtp_status_string(rtp_status s) {
 extern "C" const char* rtp_last_error(void) { return g_err; }
 
 extern "C" const char* rtp_version(void) { return "rtp 0.1.0 (gfx950)"; }
+
+// ---------------------------------------------------------------- bandwidth probe
+namespace {
+// Streaming read of a buffer (16-byte loads, 8 in flight per lane, grid-stride): the
+// rate it reaches is the device's practical HBM read ceiling, the reference the
+// decode kernels' achieved bandwidth is read against.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, size_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  uint32_t acc = 0;
+  const size_t stride = size_t(gridDim.x) * 256 * U;
+  for (size_t base = size_t(blockIdx.x) * 256 * U + threadIdx.x; base < n16; base += stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + size_t(u) * 256;
+      v[u] = i < n16 ? p[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;      // keeps the loads; almost never stores
+}
+}  // namespace
+
+extern "C" rtp_status rtp_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16) return fail(RTP_EINVAL, "rtp_hbm_read_probe: NULL buffer or fewer than 16 bytes");
+  if (!aligned(buf, 16)) return fail(RTP_EINVAL, "rtp_hbm_read_probe: buffer must be 16-byte aligned");
+  hipLaunchKernelGGL(k_read_probe, dim3(2048), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  return check_launch("k_read_probe");
+}

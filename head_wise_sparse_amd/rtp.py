@@ -25,7 +25,7 @@ KV_FULL, KV_COMPACT = 0, 1
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
             "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_append_token",
-            "rtp_status_string", "rtp_last_error", "rtp_version"]
+            "rtp_hbm_read_probe", "rtp_status_string", "rtp_last_error", "rtp_version"]
 
 
 class RtpError(RuntimeError):
@@ -69,6 +69,7 @@ def load() -> C.CDLL:
                                       C.c_float, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_append_token": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, C.c_int64, _P, _P, _P, _P, _P, _P]),
         "rtp_topk_select": (C.c_int, [D, C.c_int64, _P, C.c_int64, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_hbm_read_probe": (C.c_int, [_P, C.c_size_t, _P, _P]),
         "rtp_status_string": (C.c_char_p, [C.c_int]),
         "rtp_last_error": (C.c_char_p, []),
         "rtp_version": (C.c_char_p, []),
@@ -222,6 +223,10 @@ def rtp_append_token(layer: Layer, pos: int, k_new, v_new, k_pre, w_k_idx, w_hea
     _check(load().rtp_append_token(layer.desc, int(pos), _ptr(k_new), _ptr(v_new), _ptr(k_pre), _ptr(w_k_idx),
                                    int(w_head_stride), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(k_loc),
                                    _ptr(v_loc), _stream(stream)))
+
+
+def rtp_hbm_read_probe(buf, sink, stream=None):
+    _check(load().rtp_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def rtp_version() -> str:

@@ -298,6 +298,15 @@ rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos,
                             uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache,
                             uint16_t* k_loc, uint16_t* v_loc, void* stream);
 
+/*
+ * rtp_hbm_read_probe -- diagnostic: stream `bytes` of `buf` (device, 16-byte
+ * aligned) through plain 16-byte loads and discard them (sink: a device word that is
+ * almost never written).  Timing it gives the device's practical HBM read rate, the
+ * reference against which the decode kernels' bandwidth is read; it is not part of
+ * the method.
+ */
+rtp_status rtp_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* rtp_status_string(rtp_status s);
 
