@@ -17,10 +17,17 @@
 //    O^T = V^T P^T, so P never goes through LDS.
 //  - online softmax in the exp2 domain with a lazy reference max (rescale only when
 //    a row max grows by more than 2^8); masks are applied only on boundary tiles.
-//  - K/V tiles are double-buffered in LDS; the next tile is copied HBM -> LDS directly
-//    (no registers) while the current tile is computed, and V^T operands are read with
-//    the transposing LDS read (ds_read_b64_tr_b16), so V needs no explicit transpose.
+//  - K/V tiles are double-buffered in LDS; the next tiles are copied HBM -> LDS directly
+//    (no registers; one scalar base plus a fixed per-lane offset per copy) while the
+//    current tile is computed, and V^T operands are read with the transposing LDS read
+//    (ds_read_b64_tr_b16), so V needs no explicit transpose.
+//  - per tile, the rare branches (boundary mask, reference-max move) come first; the
+//    next tile's QK^T, this tile's exponentials and its PV product then form one
+//    straight-line block that the compiler interleaves on the MFMA and VALU pipes.  The
+//    loop runs two tiles per trip so that LDS buffer indices are constants and the two
+//    S accumulator sets swap roles without register copies.
 #include <cmath>
+#include <type_traits>
 
 #include "rtp_internal.hpp"
 
@@ -36,11 +43,12 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int PD = 128;               // head dim
-#ifndef RTP_PREFILL_RB
-#define RTP_PREFILL_RB 1
+#ifndef RTP_PREFILL_NW
+#define RTP_PREFILL_NW 4
 #endif
-constexpr int RB = RTP_PREFILL_RB;    // 32-row column blocks per wave
-constexpr int BM = 128;               // query rows per block (waves x 32*RB rows)
+constexpr int RB = 1;                 // 32-row column blocks per wave
+constexpr int NW = RTP_PREFILL_NW;    // waves per block
+constexpr int BM = 32 * RB * NW;      // query rows per block
 constexpr int BN = 64;                // keys per tile
 // LDS tiles are 64 rows x 128 bf16 (256-byte rows, 16 chunks of 16 bytes), unpadded
 // (direct-to-LDS loads fill 1 KB contiguous runs), with the chunk index XOR-swizzled per
@@ -65,12 +73,20 @@ __device__ __forceinline__ void g2lds_16(const void* gaddr, uint32_t lds) {
                : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr)
                : "memory", "m0");
 }
+// Same copy with a wave-uniform global base (scalar registers) and a 32-bit per-lane
+// byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void g2lds_16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }   // vmcnt(0)
 
-constexpr int kPreThreads = 64 * (BM / (32 * RB));   // waves x 64 lanes
+constexpr int kPreThreads = 64 * NW;
 
 struct PrefArgs {
   const uint16_t* q;        // [C][Hq][D]
@@ -97,7 +113,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t* lds_s4;
 
-__global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(PrefArgs a) {
+__global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hf = lane >> 5;
 
@@ -141,8 +157,8 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
   const uint16_t* kbase = a.k + int64_t(kvh) * a.n_cap * PD;
   const uint16_t* vbase = a.v + int64_t(kvh) * a.n_cap * PD;
 
-  // ---- Q^T operands: a wave owns 64 rows as two 32-row column blocks; lane holds row
-  // R0 + wave*64 + rb*32 + l32, dims 16*ds + 8*hf .. +8
+  // ---- Q^T operands: a wave owns 32 rows; lane holds row R0 + wave*32 + l32, dims
+  // 16*ds + 8*hf .. +8 (all 128 dims of the row over the two wave halves)
   int64_t my_row[RB];
   bf16x8_t qop[RB][PD / 16];
 #pragma unroll
@@ -154,9 +170,8 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
       qop[rb][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + (qrow_c * a.Hq + qh) * PD + 16 * ds + 8 * hf));
   }
 
-  // ---- tile staging: the next tile's K and V rows go from HBM straight to the other LDS
-  // buffer while the current tile is computed.  Wave w's i-th copy fills physical chunks
-  // (i*NWV + w)*64 .. +63; each lane fetches the global chunk that belongs at its slot.
+  // ---- tile staging: the next tiles' K and V rows go from HBM straight to the other LDS
+  // buffer while the current tile is computed.
   constexpr int KCH = BN * PD / 8;                            // 16-byte chunks per tile
   constexpr int KLD = KCH / kPreThreads;                      // copies per thread per tile (K and V each)
   constexpr int NWV = kPreThreads / 64;
@@ -197,7 +212,8 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
   }
 
   // S^T = K Q^T of one key tile; each K operand read from LDS serves every row block
-  auto qk = [&](int buf, f32x16 (&sa)[RB][2]) {
+  auto qk = [&](auto bufc, f32x16 (&sa)[RB][2]) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -215,46 +231,48 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
       }
   };
 
-  // Pipeline: K runs one tile ahead of V.  Iteration n holds S(n) in registers, issues
-  // the copies of K(n+2) and V(n+1), computes S(n+1) = K(n+1) Q^T on the MFMA pipe
-  // while the softmax of S(n) runs on the VALU, then O^T += V(n)^T P(n)^T.
-  f32x16 sacc[RB][2], snext[RB][2];
-  auto load_k = [&](int kt, int buf) {
+  // Tile copies.  Wave w's i-th copy fills physical chunks (NW*i + w)*64 .. +63 of the
+  // tile, i.e. rows 4*NW*i + crow (crow = 4w + lane/16); the swizzled chunk a lane fetches
+  // does not depend on i, so a copy is one scalar base (the tile's first row, + NW KB per
+  // i) plus a fixed per-lane byte offset.  Only a tile that runs past the cache's last row
+  // takes the clamped path (its rows beyond n_cap - 1 repeat the last row; their scores
+  // are masked).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int crow = 4 * wave + (lane >> 4);
+  const uint32_t koff = uint32_t(crow * PD + (((lane & 15) ^ (crow & 15)) << 3)) * 2u;
+  const uint32_t voff = uint32_t(crow * PD + (((lane & 15) ^ ((crow & 3) << 2)) << 3)) * 2u;
+  static_assert(KLD * NWV * 64 == KCH && NWV == NW, "copy layout");
+  auto copy_tile = [&](const uint16_t* base, int kt, uint32_t off, uint16_t* lds_tile, bool is_k) {
     const int64_t k0 = int64_t(kt) * BN;
+    const uint32_t lds0 = lds_addr(lds_tile) + uint32_t(wave_u) * 1024u;
+    if (k0 + BN <= a.n_cap) {
+      const char* g0 = reinterpret_cast<const char*>(base + k0 * PD);
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int base = (i * NWV + wave) * 64;
-      const int p = base + lane;
-      const int row = p >> 4, ck = (p & 15) ^ (row & 15);
-      const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
-      g2lds_16(kbase + kr * PD + ck * 8, lds_addr(&s_k[buf][base * 8]));
+      for (int i = 0; i < KLD; ++i) g2lds_16s(g0 + 1024 * NW * i, off, lds0 + 1024u * NW * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KLD; ++i) {
+        const int row = 4 * NW * i + crow;
+        const int c = is_k ? ((lane & 15) ^ (crow & 15)) : ((lane & 15) ^ ((crow & 3) << 2));
+        const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
+        g2lds_16(base + kr * PD + c * 8, lds0 + 1024u * NW * i);
+      }
     }
   };
-  auto load_v = [&](int kt, int buf) {
-    const int64_t k0 = int64_t(kt) * BN;
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int base = (i * NWV + wave) * 64;
-      const int p = base + lane;
-      const int row = p >> 4, cv = (p & 15) ^ ((row & 3) << 2);
-      const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
-      g2lds_16(vbase + kr * PD + cv * 8, lds_addr(&s_v[buf][base * 8]));
-    }
-  };
-  load_k(tile_of(0), 0);
-  load_v(tile_of(0), 0);
-  if (n_tiles > 1) load_k(tile_of(1), 1);
-  wait_vm0();
-  __syncthreads();
-  qk(0, sacc);
-  __syncthreads();              // K(0) is consumed: its buffer takes K(2)
 
-  for (int n = 0; n < n_tiles; ++n) {
+  // one pipeline step: S(n) is in `cur`; copies K(n+2) -> buffer B and V(n+1) -> buffer
+  // 1-B, then (when there is a next tile) computes S(n+1) = K(n+1) Q^T into `nxt` on the
+  // MFMA pipe while the softmax of S(n) runs on the VALU, then O^T += V(n)^T P(n)^T from
+  // buffer B.  The rare branches (boundary-tile mask, reference-max move) come first so
+  // that the MFMA and VALU work of the step is one straight-line block the compiler can
+  // interleave.
+  auto step = [&](auto bc, auto has_next_c, int n, f32x16 (&cur)[RB][2], f32x16 (&nxt)[RB][2]) {
+    constexpr int B = decltype(bc)::value;
+    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
     const int kt = tile_of(n);
     const int k0 = kt * BN;
-    if (n + 2 < n_tiles) load_k(tile_of(n + 2), n & 1);
-    if (n + 1 < n_tiles) load_v(tile_of(n + 1), (n + 1) & 1);
-    if (n + 1 < n_tiles) qk((n + 1) & 1, snext);
+    if (n + 2 < n_tiles) copy_tile(kbase, tile_of(n + 2), koff, s_k[B], true);
+    if (HAS_NEXT) copy_tile(vbase, tile_of(n + 1), voff, s_v[1 - B], false);
 
     // masks apply only where some (row, key) pair of the tile is invisible
     bool full;
@@ -274,22 +292,23 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kr = kb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-            const bool vis = (kr <= rrel) && (retr || kr < sink_lim || kr > wlo);
-            sacc[rb][kb][v] = vis ? sacc[rb][kb][v] : -INFINITY;
+            const bool vis = (kr <= rrel) & (retr | (kr < sink_lim) | (kr > wlo));   // no short-circuit branches
+            cur[rb][kb][v] = vis ? cur[rb][kb][v] : -INFINITY;
           }
       }
     }
-    uint32_t pk[RB][2][8];
+    // row max on the raw scores (the scale is positive); the two wave halves hold the same
+    // rows (different keys) and exchange their maxima with one lane swap.  The reference
+    // max (log2 domain) moves only when a row max grows past it by more than 2^8.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // row max on the raw scores (the scale is positive)
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[rb][kb][v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;   // both halves hold the same row
-      // lazy reference max (log2 domain): move it only when the row max grows past 2^8
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, cur[rb][kb][v]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
       const bool grow = tmax > m_run[rb] + 8.0f;
       if (__ballot(grow)) {
         const float m_new = grow ? tmax : m_run[rb];
@@ -301,44 +320,72 @@ __global__ __launch_bounds__(kPreThreads, RB == 1 ? 2 : 1) void k_prefill_attn(P
           for (int v = 0; v < 16; ++v) oacc[rb][db][v] *= alpha;
         m_run[rb] = m_new;
       }
-      const float nm = -m_run[rb];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v], a.scale_log2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][v + 1], a.scale_log2, nm));
-          pk[rb][kb][v >> 1] = pack_bf16x2(p0, p1);
-          // row sum of the bf16 probabilities the PV product uses (one dot2 per pair)
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[rb][kb][v >> 1]),
-                                                 __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
-        }
-      l_run[rb] += psum;
     }
 
-    // O^T += V^T P^T: each V^T operand read from LDS serves every row block
-    const int vbuf = n & 1;
+    // ---- straight-line part: QK of the next tile, softmax and PV of this one
+    if constexpr (HAS_NEXT) qk(std::integral_constant<int, 1 - B>{}, nxt);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb = ks >> 1, half = ks & 1;
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t pk[RB][8];
 #pragma unroll
-      for (int db = 0; db < PD / 32; ++db) {
-        const bf16x8_t vv = vt_operand(vbuf, db, ks);
+      for (int rb = 0; rb < RB; ++rb) {
+        const float nm = -m_run[rb];
+        float psum = 0.0f;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const uint4 pb = make_uint4(pk[rb][kb][4 * half], pk[rb][kb][4 * half + 1], pk[rb][kb][4 * half + 2],
-                                      pk[rb][kb][4 * half + 3]);
-          oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(pb), oacc[rb][db], 0, 0, 0);
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[rb][kb][v], a.scale_log2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[rb][kb][v + 1], a.scale_log2, nm));
+          pk[rb][v >> 1] = pack_bf16x2(p0, p1);
+          // row sum of the bf16 probabilities the PV product uses (one dot2 per pair)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[rb][v >> 1]),
+                                                 __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+        }
+        l_run[rb] += psum;
+      }
+      // O^T += V^T P^T over this 32-key half: each V^T operand read serves every row block
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ks = 2 * kb + half;
+#pragma unroll
+        for (int db = 0; db < PD / 32; ++db) {
+          const bf16x8_t vv = vt_operand(B, db, ks);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const uint4 pb = make_uint4(pk[rb][4 * half], pk[rb][4 * half + 1], pk[rb][4 * half + 2], pk[rb][4 * half + 3]);
+            oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(pb), oacc[rb][db], 0, 0, 0);
+          }
         }
       }
     }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[rb][kb] = snext[rb][kb];
     wait_vm0();                 // this wave's copies of K(n+2) and V(n+1) have landed
     __syncthreads();            // ... and everyone's; K(n+1) and V(n) buffers are free again
+  };
+
+  f32x16 sacc[RB][2], snext[RB][2];
+  copy_tile(kbase, tile_of(0), koff, s_k[0], true);
+  copy_tile(vbase, tile_of(0), voff, s_v[0], false);
+  if (n_tiles > 1) copy_tile(kbase, tile_of(1), koff, s_k[1], true);
+  wait_vm0();
+  __syncthreads();
+  qk(std::integral_constant<int, 0>{}, sacc);
+  __syncthreads();              // K(0) is consumed: its buffer takes K(2)
+
+  // two steps per trip so that the buffer index is a constant and S alternates between
+  // the two accumulator sets without copies; the last step (no next tile) is peeled
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  int n = 0;
+  for (; n + 2 < n_tiles; n += 2) {
+    step(I0{}, T{}, n, sacc, snext);
+    step(I1{}, T{}, n + 1, snext, sacc);
+  }
+  if (n + 1 < n_tiles) {
+    step(I0{}, T{}, n, sacc, snext);
+    step(I1{}, F{}, n + 1, snext, sacc);
+  } else {
+    step(I0{}, F{}, n, sacc, snext);
   }
 
   // ---- normalise and store: lane holds row my_row[rb], dims db*32 + 8*(v/4) + 4*hf + (v%4)
