@@ -110,8 +110,8 @@ SelLayout sel_layout(const Layer& L) {
   off = round_up(off + rows * sizeof(SelRowState), 256);
   s.ctr = off;
   off = round_up(off + rows * 2 * sizeof(uint32_t), 256);
-  s.lookback = off;
-  off = round_up(off + rows * size_t(s.nblk_max) * sizeof(uint64_t), 256);
+  s.tilerec = off;
+  off = round_up(off + rows * size_t(s.nblk_max) * sizeof(uint4), 256);
   s.total = off;
   return s;
 }

@@ -73,7 +73,7 @@ struct SelRowState {             // one per score row, lives in the workspace
 };
 static_assert(sizeof(SelRowState) == 56, "row state layout");
 struct SelLayout {                // depends on the layer only (n_cap), not on n_ctx: the
-  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, lookback, total;
+  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, tilerec, total;
   int nblk_max;                   // zero-filled region stays in place while n_ctx grows
 };
 SelLayout sel_layout(const Layer& L);
@@ -83,8 +83,8 @@ struct SelRows {                 // device views of the selection workspace
   uint64_t* cmass;               // [rows][3][64]   coarse summaries (32 fine bins each)
   uint32_t* ccnt;                // [rows][3][64]
   SelRowState* state;            // [rows]
-  uint32_t* ctr;                 // [rows][2]       compaction: dynamic tile ids, blocks done
-  uint64_t* lookback;            // [rows][nblk]
+  uint32_t* ctr;                 // [rows][2]       compaction: [1] blocks done
+  uint4* tilerec;                // [rows][nblk]    per tile: counts against the level-1 prefix (hist<2>)
 };
 struct SelArgs {
   const float* scores;           // [rows][n_cap]
@@ -99,7 +99,7 @@ struct SelArgs {
   int n_ctx;
   int64_t n_cap;
   int nblk;                      // selection tiles per row (from n_ctx)
-  int lb_stride;                 // look-back words per row (from n_cap)
+  int rec_stride;                // tile records per row (from n_cap)
   int32_t* sel_idx;
   int32_t* sel_count;
   int32_t* starts;               // [rows][nsplit + 1] range index of the selected lists, or null

@@ -19,16 +19,24 @@
 //             from the 32 fine bins under the chosen coarse bin (two small reads): the
 //             digit is where the mass accumulated from the top first reaches what is
 //             still needed.  The kernel boundary is the only synchronisation.
+//             hist<2> also leaves one record per tile: how many of its tokens lie above
+//             the 22-bit prefix (certainly selected) and, for up to kRecPairs distinct
+//             low 10-bit digits among the tokens that share it (candidates), the digit
+//             and its count.
 //   compact   resolves the last digit (t is now the full key), the tie count r in
 //             closed form (tied tokens carry equal weight), and writes the selected
-//             indices in increasing order: each tile counts its above / tied tokens and
-//             learns the counts of all earlier tiles through a decoupled look-back
-//             (relaxed atomics on 64-bit status words that carry the counts themselves).
+//             indices in increasing order.  A tile's output offset comes from the
+//             records of the earlier tiles (written by the previous launch: no waiting
+//             on other blocks): tokens above the prefix, plus candidates above t, plus
+//             at most r ties.  Candidates share 22 key bits with t, so a tile holds few
+//             distinct ones (exact ties collapse into one pair); only for a tile with
+//             more distinct candidates than its record keeps does the block count them
+//             again from that tile's scores.
 //             It also writes the range index of every list when asked for.
 // The workspace is all zero when a call starts and when it ends: each launch clears
 // what earlier launches left and nobody reads any more (hist<2> the level-0
 // histogram, compact the level-1 histogram), and the last compaction block of a row
-// to finish clears the rest of that row (level-2 histogram, look-back words, row state
+// to finish clears the rest of that row (level-2 histogram, tile records, row state
 // and counters).
 #include <cmath>
 
@@ -40,15 +48,11 @@ using namespace rtp_dev;
 
 namespace {
 
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr int kCoarse = 64;          // coarse bins of levels 0/1 (32 at level 2)
 constexpr int kFinePer = 32;         // fine bins under one coarse bin
-constexpr int kSpinLimit = 1 << 20;  // bound of a look-back wait (never reached in a valid launch)
+constexpr int kRecPairs = 3;         // (digit, count) pairs a tile record holds (one per 32-bit word)
+constexpr int kMaxHeavy = 256;       // heavy earlier tiles a compaction block recounts one by one
 
-__device__ __forceinline__ void st_rlx(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint64_t ld_rlx(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -128,6 +132,76 @@ __device__ Resolved resolve_level(const SelRows& R, int row, int level, const Re
   return o;
 }
 
+// Level 2 (1024 bins, histogram complete since the previous launch) in one round trip:
+// lane l loads bins 16l .. 16l+15 and the owner bin is found by the same rule as above
+// (mass of the bins above < need <= that plus the bin's own mass), from lane suffix sums
+// and a scan inside the owning lane.
+__device__ Resolved resolve_level2_direct(const SelRows& R, int row, const Resolved& in, bool by_count, int lane) {
+  constexpr int PER = 1024 / 64;
+  const uint32_t* fc = R.cnt + (int64_t(row) * 3 + 2) * kBins + lane * PER;
+  const uint64_t* fm = R.mass + (int64_t(row) * 3 + 2) * kBins + lane * PER;
+  uint32_t c[PER];
+  uint64_t m[PER];
+#pragma unroll
+  for (int k = 0; k < PER / 4; ++k) {
+    const uint4 v = reinterpret_cast<const uint4*>(fc)[k];
+    c[4 * k] = v.x;
+    c[4 * k + 1] = v.y;
+    c[4 * k + 2] = v.z;
+    c[4 * k + 3] = v.w;
+  }
+  if (!by_count) {
+#pragma unroll
+    for (int k = 0; k < PER / 2; ++k) {
+      const uint4 v = reinterpret_cast<const uint4*>(fm)[k];
+      m[2 * k] = uint64_t(v.x) | (uint64_t(v.y) << 32);
+      m[2 * k + 1] = uint64_t(v.z) | (uint64_t(v.w) << 32);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) m[k] = c[k];
+  }
+  uint64_t lm = 0;
+  uint32_t lc = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    lm += m[k];
+    lc += c[k];
+  }
+  Resolved o = in;
+  const uint64_t need = o.target - o.above;
+  const uint64_t S = wave_suffix_incl<uint64_t>(lm, lane);
+  const uint32_t SC = wave_suffix_incl<uint32_t>(lc, lane);
+  const uint64_t own = __ballot(S >= need && S - lm < need);
+  const int ol = own ? __ffsll((unsigned long long)own) - 1 : 0;
+  // inside the owning lane: bins from the top down
+  uint64_t acc = S - lm;
+  uint32_t cacc = SC - lc;
+  int fb = 0;
+  uint32_t tied = c[0];
+  uint64_t above_f = acc;
+  uint32_t cnt_above_f = cacc;
+  bool found = false;
+#pragma unroll
+  for (int k = PER - 1; k >= 0; --k) {
+    if (!found && acc + m[k] >= need) {
+      found = true;
+      fb = k;
+      tied = c[k];
+      above_f = acc;
+      cnt_above_f = cacc;
+    }
+    acc += m[k];
+    cacc += c[k];
+  }
+  const uint32_t digit = uint32_t(ol * PER + __shfl(fb, ol, 64));
+  o.above += __shfl(above_f, ol, 64);
+  o.cnt_above += __shfl(cnt_above_f, ol, 64);
+  o.tied = __shfl(tied, ol, 64);
+  o.prefix = (o.prefix << 10) | digit;
+  return o;
+}
+
 // Clear one level's histogram of a row (plain stores: the next launch sees them).
 // Block `blk` of `nblk` clears its share.
 __device__ __forceinline__ void clear_level(const SelRows& R, int row, int level, int blk, int nblk) {
@@ -170,6 +244,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   __shared__ uint32_t h_c[NB];
   __shared__ uint32_t s_prefix;
   __shared__ float s_red[kSelThreads / 64];
+  __shared__ uint32_t s_na[kSelThreads / 64], s_np, s_pair[kRecPairs];   // level 2: tile record
 
   // scores of the tile: unconditional loads (index clamped), validity kept aside
   const float* sp = a.scores + int64_t(row) * a.n_cap;
@@ -184,6 +259,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
     h_m[i] = 0;
     h_c[i] = 0;
   }
+  if (LEVEL == 2 && tid == 0) s_np = 0;
   float m = 0.0f;                                   // unused by the static top-k rule
   if constexpr (LEVEL == 0) {
     if (!a.by_count) m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red) : a.row_max[row];
@@ -215,6 +291,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   }
   __syncthreads();
   const uint32_t prefix = LEVEL > 0 ? s_prefix : 0u;
+  uint32_t n_above = 0;                             // level 2: tokens above the 22-bit prefix
 #pragma unroll
   for (int it = 0; it < kSelItems; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
@@ -225,14 +302,37 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
       if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m));
       atomicAdd(&h_c[d], 1u);
     }
+    if constexpr (LEVEL == 2) n_above += uint32_t((j < a.n_ctx) && (key >> PSHIFT) > prefix);
+  }
+  if constexpr (LEVEL == 2) {
+    n_above = wave_sum(n_above);
+    if (lane == 0) s_na[tid / 64] = n_above;
   }
   __syncthreads();
+
   uint64_t* gm = a.R.mass + (int64_t(row) * 3 + LEVEL) * kBins;
   uint32_t* gc = a.R.cnt + (int64_t(row) * 3 + LEVEL) * kBins;
   for (int i = tid; i < NB; i += kSelThreads) {
     if (h_c[i]) {
       if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(gm + i), (unsigned long long)h_m[i]);
       atomicAdd(gc + i, h_c[i]);
+      if constexpr (LEVEL == 2) {              // this tile's distinct candidate digits
+        const uint32_t k = atomicAdd(&s_np, 1u);
+        if (k < uint32_t(kRecPairs)) s_pair[k] = uint32_t(i) | (h_c[i] << 10);
+      }
+    }
+  }
+  if constexpr (LEVEL == 2) {
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t na = 0;
+#pragma unroll
+      for (int w = 0; w < kSelThreads / 64; ++w) na += s_na[w];
+      const uint32_t np = s_np;
+      uint32_t pw[kRecPairs];
+#pragma unroll
+      for (int k = 0; k < kRecPairs; ++k) pw[k] = uint32_t(k) < np ? s_pair[k] : 0u;
+      a.R.tilerec[int64_t(row) * a.rec_stride + blk] = make_uint4(na | (np << 16), pw[0], pw[1], pw[2]);
     }
   }
   // coarse summary: thread c < NB/32 sums its 32 fine bins, starting at a different
@@ -258,16 +358,16 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
 // Resolve the last digit, then write {key > t} U {first r with key == t} in order.
 __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int row = blockIdx.y;
+  const int row = blockIdx.y, tile = blockIdx.x;
   constexpr int NW = kSelThreads / 64;
+  static_assert(kSelItems * NW == 64, "one wave scans the per-(item, wave) counts");
   __shared__ uint32_t s_t, s_r;
-  __shared__ uint32_t s_wa[kSelItems][NW], s_we[kSelItems][NW];
-  __shared__ uint32_t s_pa, s_pe, s_last;
+  __shared__ uint32_t s_wa[kSelItems * NW], s_we[kSelItems * NW];   // counts, then exclusive prefixes
+  __shared__ uint32_t s_pa, s_pe, s_heavy, s_last;
+  __shared__ uint32_t s_ra[NW], s_re[NW];
+  __shared__ uint32_t s_heavy_list[kMaxHeavy];
   uint32_t* ctr = a.R.ctr + 2 * int64_t(row);
-  // Static tile ids: a tile waits only for lower-numbered tiles of its row, which the
-  // dispatcher has issued before it (workgroups of a launch start in index order), so
-  // the look-back always ends; its spin count is bounded all the same.
-  const int tile = blockIdx.x;
+  const uint4* rec = a.R.tilerec + int64_t(row) * a.rec_stride;
   const float* sp = a.scores + int64_t(row) * a.n_cap;
   const int64_t base = int64_t(tile) * kSelTile;
   float sv[kSelItems];
@@ -276,6 +376,8 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     const int64_t j = base + it * kSelThreads + tid;
     sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
   }
+  uint4 rec0 = make_uint4(0u, 0u, 0u, 0u);           // records of the first 64 earlier tiles
+  if (wave == 1 && lane < tile) rec0 = rec[lane];
   if (wave == 0) {
     const SelLevelState& ls = a.R.state[row].lvl[1];
     Resolved in{};
@@ -283,7 +385,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     in.above = ls.above;
     in.cnt_above = ls.cnt_above;
     in.target = ls.target;
-    const Resolved o = resolve_level(a.R, row, 2, in, a.top_p, a.by_count, a.k_target, lane);
+    const Resolved o = resolve_level2_direct(a.R, row, in, a.by_count, lane);
     if (lane == 0) {
       // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
       s_t = o.prefix;
@@ -303,6 +405,41 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   __syncthreads();
   clear_level(a.R, row, 1, tile, a.nblk);             // read last by hist<2>
   const uint32_t t = s_t, r = s_r;
+  // ---- tokens of earlier tiles with key > t (pa) and key == t (pe), from their records;
+  // tiles whose record overflowed ("heavy") are listed and counted from their scores
+  if (wave == 1) {
+    const uint32_t tl = t & 1023u;
+    uint32_t ca = 0, ce = 0, nh = 0;
+    for (int c = 0; c < tile; c += 64) {
+      const int i = c + lane;
+      const uint4 q = (c == 0) ? rec0 : (i < tile ? rec[i] : make_uint4(0u, 0u, 0u, 0u));
+      const uint32_t np = q.x >> 16;
+      ca += q.x & 0xFFFFu;
+      const bool heavy = np > uint32_t(kRecPairs);
+      if (!heavy) {
+        const uint32_t pw[kRecPairs] = {q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < kRecPairs; ++k) {
+          const uint32_t dig = pw[k] & 1023u, cnt = pw[k] >> 10;   // empty pairs have cnt 0
+          ca += dig > tl ? cnt : 0u;
+          ce += dig == tl ? cnt : 0u;
+        }
+      }
+      const uint64_t hb = __ballot(heavy);
+      if (heavy) {
+        const uint32_t slot = nh + __popcll(hb & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        if (slot < uint32_t(kMaxHeavy)) s_heavy_list[slot] = uint32_t(i);
+      }
+      nh += __popcll(hb);
+    }
+    ca = wave_sum(ca);
+    ce = wave_sum(ce);
+    if (lane == 0) {
+      s_pa = ca;
+      s_pe = ce;
+      s_heavy = nh;
+    }
+  }
   bool fa[kSelItems], fe[kSelItems];
   uint64_t ba[kSelItems], be[kSelItems];
 #pragma unroll
@@ -314,85 +451,95 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     ba[it] = __ballot(fa[it]);
     be[it] = __ballot(fe[it]);
     if (lane == 0) {
-      s_wa[it][wave] = __popcll(ba[it]);
-      s_we[it][wave] = __popcll(be[it]);
+      s_wa[it * NW + wave] = __popcll(ba[it]);
+      s_we[it * NW + wave] = __popcll(be[it]);
     }
   }
   __syncthreads();
-  // decoupled look-back, one wave wide
-  if (wave == 0) {
-    uint32_t a_ = 0, e_ = 0;
-    for (int it = 0; it < kSelItems; ++it)
-      for (int w = 0; w < NW; ++w) {
-        a_ += s_wa[it][w];
-        e_ += s_we[it][w];
+  const uint32_t nheavy = s_heavy;
+  if (nheavy) {
+    // candidates of the heavy tiles (all earlier tiles when there are too many of them)
+    const bool listed = nheavy <= uint32_t(kMaxHeavy);
+    const int nt = listed ? int(nheavy) : tile;
+    uint32_t ga = 0, ge = 0;
+    for (int h = 0; h < nt; ++h) {
+      const int64_t tb = int64_t(listed ? s_heavy_list[h] : h) * kSelTile;
+#pragma unroll 4
+      for (int k = tid; k < kSelTile; k += kSelThreads) {
+        const uint32_t key = score_key(sp[tb + k]);          // earlier tiles are full: tb + k < base
+        const bool cand = (key >> 10) == (t >> 10);
+        ga += uint32_t(cand && key > t);
+        ge += uint32_t(key == t);
       }
-    uint64_t* lb = a.R.lookback + int64_t(row) * a.lb_stride;
-    uint64_t pa = 0, pe = 0;
-    if (tile == 0) {
-      if (lane == 0) st_rlx(lb, kFlagIncl | (uint64_t(a_) << 31) | e_);
-    } else {
-      if (lane == 0) st_rlx(lb + tile, kFlagAgg | (uint64_t(a_) << 31) | e_);
-      int k = tile - 1;                       // lanes inspect tiles k, k-1, ..., k-63
-      int spins = 0;
-      while (true) {
-        const int idx = k - lane;
-        const uint64_t v = (idx >= 0) ? ld_rlx(lb + idx) : kFlagIncl;
-        const uint64_t f = v >> 62;
-        const uint64_t incl = __ballot(f == 2);
-        const uint64_t none = __ballot(f == 0);
-        const int first = incl ? __ffsll((unsigned long long)incl) - 1 : 64;
-        const uint64_t upto = (first >= 63) ? ~0ull : ((2ull << first) - 1ull);
-        if ((none & upto) && ++spins < kSpinLimit) {   // a needed predecessor has not published yet
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        const bool use = lane <= first;
-        pa += wave_sum<uint64_t>(use ? ((v >> 31) & 0x7FFFFFFFull) : 0ull);
-        pe += wave_sum<uint64_t>(use ? (v & 0x7FFFFFFFull) : 0ull);
-        if (first < 64) break;
-        k -= 64;
-      }
-      if (lane == 0) st_rlx(lb + tile, kFlagIncl | ((pa + a_) << 31) | (pe + e_));
     }
+    ga = wave_sum(ga);
+    ge = wave_sum(ge);
     if (lane == 0) {
-      s_pa = uint32_t(pa);
-      s_pe = uint32_t(pe);
+      s_ra[wave] = ga;
+      s_re[wave] = ge;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t ga_all = 0, ge_all = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        ga_all += s_ra[w];
+        ge_all += s_re[w];
+      }
+      if (listed) {                 // the records already gave the light tiles' candidates
+        s_pa += ga_all;
+        s_pe += ge_all;
+      } else {                      // recounted every earlier tile: keep only the above-prefix sum
+        uint32_t na = 0;
+        for (int i = 0; i < tile; ++i) na += rec[i].x & 0xFFFFu;
+        s_pa = na + ga_all;
+        s_pe = ge_all;
+      }
     }
   }
+  // This block reads no more of the tile records, the level-2 histogram or the row state:
+  // count it as done now, and learn whether it was the last one only at the end.
+  uint32_t done_before = 0;
+  if (tid == 0) done_before = atomicAdd(ctr + 1, 1u);
+  // exclusive prefix of the per-(item, wave) counts, in token order (item-major)
+  if (wave == 0) {
+    const uint32_t va = s_wa[lane], ve = s_we[lane];
+    uint32_t xa = va, xe = ve;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t ya = __shfl_up(xa, o, 64), ye = __shfl_up(xe, o, 64);
+      if (lane >= o) {
+        xa += ya;
+        xe += ye;
+      }
+    }
+    s_wa[lane] = xa - va;
+    s_we[lane] = xe - ve;
+  }
   __syncthreads();
-  uint32_t ca = s_pa, ce = s_pe;              // counts of every earlier token
+  const uint32_t pa = s_pa, pe = s_pe;                 // counts of every earlier token
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = a.sel_idx + int64_t(row) * a.n_cap;
   constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
 #pragma unroll
   for (int it = 0; it < kSelItems; ++it) {
+    const uint32_t ca = pa + s_wa[it * NW + wave], ce = pe + s_we[it * NW + wave];
     if (a.starts && it % IT_PER_RANGE == 0 && tid == 0) {
       // first token of a decode range: the number of selected tokens before it
       const int64_t q = (base + it * kSelThreads) / kDecRange;
       if (q < a.nsplit) a.starts[int64_t(row) * (a.nsplit + 1) + q] = int32_t(ca + (ce < r ? ce : r));
     }
-    uint32_t wa = 0, we = 0;
-    for (int w = 0; w < wave; ++w) {
-      wa += s_wa[it][w];
-      we += s_we[it][w];
-    }
-    const uint32_t a_before = ca + wa + __popcll(ba[it] & lt);
-    const uint32_t e_before = ce + we + __popcll(be[it] & lt);
+    const uint32_t a_before = ca + __popcll(ba[it] & lt);
+    const uint32_t e_before = ce + __popcll(be[it] & lt);
     const bool take = fa[it] || (fe[it] && e_before < r);
     if (take) out[a_before + (e_before < r ? e_before : r)] = int32_t(base + it * kSelThreads + tid);
-    for (int w = 0; w < NW; ++w) {
-      ca += s_wa[it][w];
-      ce += s_we[it][w];
-    }
   }
-  // the last block of the row to finish clears what this launch read: every other
-  // block has finished its look-back and its reads of the level-2 histogram and state
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(ctr + 1, 1u) == uint32_t(a.nblk - 1));
+  // the last block of the row to be counted clears what this launch read: every other
+  // block has finished its reads of the tile records, the level-2 histogram and the state
+  if (tid == 0) s_last = (done_before == uint32_t(a.nblk - 1));
   __syncthreads();
   if (s_last) {
-    for (int i = tid; i < a.nblk; i += kSelThreads) a.R.lookback[int64_t(row) * a.lb_stride + i] = 0;
+    for (int i = tid; i < a.nblk; i += kSelThreads) a.R.tilerec[int64_t(row) * a.rec_stride + i] = make_uint4(0u, 0u, 0u, 0u);
     uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
     if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
     clear_level(a.R, row, 2, 0, 1);
@@ -423,7 +570,7 @@ SelRows sel_rows(void* ws, const SelLayout& lay) {
   return SelRows{reinterpret_cast<uint64_t*>(w + lay.hist_mass), reinterpret_cast<uint32_t*>(w + lay.hist_cnt),
                  reinterpret_cast<uint64_t*>(w + lay.coarse_mass), reinterpret_cast<uint32_t*>(w + lay.coarse_cnt),
                  reinterpret_cast<SelRowState*>(w + lay.state), reinterpret_cast<uint32_t*>(w + lay.ctr),
-                 reinterpret_cast<uint64_t*>(w + lay.lookback)};
+                 reinterpret_cast<uint4*>(w + lay.tilerec)};
 }
 
 }  // namespace rtp
@@ -462,7 +609,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
   a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
-  a.lb_stride = lay.nblk_max;
+  a.rec_stride = lay.nblk_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.starts = sel_starts;
@@ -498,7 +645,7 @@ extern "C" rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
   a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
-  a.lb_stride = lay.nblk_max;
+  a.rec_stride = lay.nblk_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.starts = sel_starts;

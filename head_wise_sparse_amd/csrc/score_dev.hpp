@@ -125,11 +125,13 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
     if (pi == 0) s_qidx[t][c] = acc * idx_scale;
   }
   __syncthreads();
+  // q_idx is the same for every lane: keep it in scalar registers (frees G*IDX VGPRs)
   float qi[G][IDX];
 #pragma unroll
   for (int t = 0; t < G; ++t)
 #pragma unroll
-    for (int c = 0; c < IDX; ++c) qi[t][c] = s_qidx[t][c];
+    for (int c = 0; c < IDX; ++c)
+      qi[t][c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_qidx[t][c])));
 
   // ---- score the tile (keys were loaded before the q_idx prologue)
   float sc[ITEMS][G];

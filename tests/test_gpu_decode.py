@@ -189,6 +189,18 @@ def _edge_rows():
     yield "wide_spread", (rng.standard_normal((2, 9000)) * 300).astype(np.float32), 0.95
     yield "narrow_spread", (5 + rng.standard_normal((2, 20000)) * 1e-3).astype(np.float32), 0.9
     yield "ragged_many_tiles", rng.standard_normal((4, 2048 * 5 + 3)).astype(np.float32) * 3, 0.99
+    # near-equal clusters in every 4096-token tile: scores 1 + k ulp share the top 22 key
+    # bits, so the cut falls among tokens the radix passes cannot tell apart until the
+    # last 10 bits; 8 per tile stay within a tile record's digits, 12 per tile overflow it
+    for name, per in (("clustered_light", 8), ("clustered_heavy", 12)):
+        n = 4096 * 5 + 700
+        c = np.full((2, n), -12.0, np.float32)
+        for tile in range((n + 4095) // 4096):
+            lo, hi = tile * 4096, min(n, tile * 4096 + 4096)
+            pos = rng.choice(np.arange(lo, hi), per, replace=False)
+            ulps = rng.integers(0, 4, per)
+            c[:, pos] = (np.float32(1.0).view(np.uint32) + ulps.astype(np.uint32)).view(np.float32)
+        yield name, c, 0.5
 
 
 @pytest.mark.parametrize("case", list(_edge_rows()), ids=lambda c: c[0])
