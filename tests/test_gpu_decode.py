@@ -201,6 +201,9 @@ def _edge_rows():
             ulps = rng.integers(0, 4, per)
             c[:, pos] = (np.float32(1.0).view(np.uint32) + ulps.astype(np.uint32)).view(np.float32)
         yield name, c, 0.5
+    # a narrow spread over more than 256 tiles: every tile holds many distinct candidates,
+    # so late tiles recount all earlier tiles instead of a list of the heavy ones
+    yield "narrow_many_heavy_tiles", (5 + rng.standard_normal((1, 4096 * 268 + 100)) * 1e-3).astype(np.float32), 0.9
 
 
 @pytest.mark.parametrize("case", list(_edge_rows()), ids=lambda c: c[0])
