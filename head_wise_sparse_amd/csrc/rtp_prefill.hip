@@ -48,6 +48,7 @@ constexpr int PD = 128;               // head dim
 #endif
 constexpr int RB = 1;                 // 32-row column blocks per wave
 constexpr int NW = RTP_PREFILL_NW;    // waves per block
+constexpr int kOpAhead = 2;           // LDS operand reads in flight ahead of their MFMA
 constexpr int BM = 32 * RB * NW;      // query rows per block
 constexpr int BN = 64;                // keys per tile
 // LDS tiles are 64 rows x 128 bf16 (256-byte rows, 16 chunks of 16 bytes), unpadded
@@ -260,6 +261,19 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
     }
   };
 
+  // row max of a tile's raw scores, both wave halves (the two halves hold the same rows,
+  // different keys: one lane swap), in the log2 domain (the scale is positive)
+  auto row_max = [&](const f32x16 (&sc)[RB][2], int rb) -> float {
+    float t = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t = fmaxf(t, sc[rb][kb][v]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+  };
+  float tmax_carry[RB];          // row max of the S tile the next step starts from (unmasked)
+
   // one pipeline step: S(n) is in `cur`; copies K(n+2) -> buffer B and V(n+1) -> buffer
   // 1-B, then (when there is a next tile) computes S(n+1) = K(n+1) Q^T into `nxt` on the
   // MFMA pipe while the softmax of S(n) runs on the VALU, then O^T += V(n)^T P(n)^T from
@@ -295,6 +309,7 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
             const bool vis = (kr <= rrel) & (retr | (kr < sink_lim) | (kr > wlo));   // no short-circuit branches
             cur[rb][kb][v] = vis ? cur[rb][kb][v] : -INFINITY;
           }
+        tmax_carry[rb] = row_max(cur, rb);              // the carried max did not see the mask
       }
     }
     // row max on the raw scores (the scale is positive); the two wave halves hold the same
@@ -302,13 +317,7 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
     // max (log2 domain) moves only when a row max grows past it by more than 2^8.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, cur[rb][kb][v]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+      const float tmax = tmax_carry[rb];
       const bool grow = tmax > m_run[rb] + 8.0f;
       if (__ballot(grow)) {
         const float m_new = grow ? tmax : m_run[rb];
@@ -323,7 +332,75 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
     }
 
     // ---- straight-line part: QK of the next tile, softmax and PV of this one
+    if constexpr (HAS_NEXT) {
+      // 32 MFMA slots, pinned in this order by scheduling barriers: QK^T(n+1) in slots
+      // 0..15 (alternating the two 32-key chains), each carrying one pair of this tile's
+      // exponentials; PV(n) in slots 16..31, which also carry the next tile's row max (its
+      // chains finished by then).  K and V^T operands are read kOpAhead slots ahead; left
+      // to itself the compiler reads each operand one MFMA before its use.
+      static_assert(RB == 1, "slot schedule assumes one row block per wave");
+      constexpr int KB1 = 1 - B;
+      bf16x8_t kop[16], vop[16];
+      uint32_t pk[2][8];
+      float psum = 0.0f;
+      const float nm = -m_run[0];
+      auto kread = [&](int s) {
+        const int kbp = s & 1, ds = s >> 1;
+        kop[s] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_k[KB1][swz_k(kbp * 32 + l32, 2 * ds + hf)]));
+      };
+      auto vread = [&](int p) { vop[p] = vt_operand(B, p & 3, p >> 2); };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) nxt[0][kb][v] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kOpAhead; ++s) kread(s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        nxt[0][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[0][s >> 1], nxt[0][s & 1], 0, 0, 0);
+        if (s + kOpAhead < 16) kread(s + kOpAhead);
+        if (s >= 16 - kOpAhead) vread(s - (16 - kOpAhead));
+        {
+          const int kb = s >> 3, v = 2 * (s & 7);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[0][kb][v], a.scale_log2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[0][kb][v + 1], a.scale_log2, nm));
+          pk[kb][s & 7] = pack_bf16x2(p0, p1);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb][s & 7]),
+                                                 __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // PV slots; the next tile's row max rides along (its S chains finished in slots 14/15)
+      float tm0 = -INFINITY, tm1 = -INFINITY;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int ks = p >> 2, db = p & 3, kb = ks >> 1, half = ks & 1;
+        if (p + kOpAhead < 16) vread(p + kOpAhead);
+        const uint4 pb = make_uint4(pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2], pk[kb][4 * half + 3]);
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[p], as_bf16x8(pb), oacc[0][db], 0, 0, 0);
+        if (p >= 2 && p < 10) {
+          tm0 = fmaxf(fmaxf(tm0, nxt[0][0][2 * (p - 2)]), nxt[0][0][2 * (p - 2) + 1]);
+          asm volatile("" : "+v"(tm0));          // keep this partial max in its slot
+        }
+        if (p >= 8) {
+          tm1 = fmaxf(fmaxf(tm1, nxt[0][1][2 * (p - 8)]), nxt[0][1][2 * (p - 8) + 1]);
+          asm volatile("" : "+v"(tm1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const float t = fmaxf(tm0, tm1);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+        tmax_carry[0] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+      }
+      l_run[0] += psum;
+    } else {
     if constexpr (HAS_NEXT) qk(std::integral_constant<int, 1 - B>{}, nxt);
+    if constexpr (HAS_NEXT) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) tmax_carry[rb] = row_max(nxt, rb);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       uint32_t pk[RB][8];
@@ -357,6 +434,7 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
         }
       }
     }
+    }
     wait_vm0();                 // this wave's copies of K(n+2) and V(n+1) have landed
     __syncthreads();            // ... and everyone's; K(n+1) and V(n) buffers are free again
   };
@@ -368,6 +446,8 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
   wait_vm0();
   __syncthreads();
   qk(std::integral_constant<int, 0>{}, sacc);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) tmax_carry[rb] = row_max(sacc, rb);
   __syncthreads();              // K(0) is consumed: its buffer takes K(2)
 
   // two steps per trip so that the buffer index is a constant and S alternates between
