@@ -68,6 +68,8 @@ def parse():
                     help="generated tokens of the growing-context workload (0: skip it)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run only one part (for profiling); the JSON line is still printed")
+    ap.add_argument("--report-configs", action="store_true",
+                    help="per-config timings of every decode and prefill workload (one JSON report line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -92,12 +94,12 @@ def log(msg):
 
 # ----------------------------------------------------------------------------- decode
 class DecodeBench:
-    def __init__(self, copies: int):
+    def __init__(self, copies: int, name: str = "decode_b4_128k"):
         import torch
         from head_wise_sparse_amd import rtp
         from head_wise_sparse_amd import workloads as W
         self.torch, self.rtp = torch, rtp
-        self.cfg = cfg = W.CONFIGS["decode_b4_128k"]
+        self.cfg = cfg = W.CONFIGS[name]
         t = time.time()
         self.x = x = W.make_decode_inputs(cfg)
         log(f"decode inputs drawn in {time.time() - t:.1f}s")
@@ -264,16 +266,20 @@ class GenBench:
 
 # ----------------------------------------------------------------------------- prefill
 class PrefillBench:
-    def __init__(self):
+    def __init__(self, name: str = "prefill_32k", q_distinct: int = 0):
+        """q_distinct > 0: draw only that many distinct query chunks and cycle them (the
+        prefill's work does not depend on the values; drawing all 64 chunks of the 1M
+        workload would take minutes of host time)."""
         import torch
         from head_wise_sparse_amd import rtp
         from head_wise_sparse_amd import workloads as W
         self.torch, self.rtp = torch, rtp
-        self.cfg = cfg = W.CONFIGS["prefill_32k"]
+        self.cfg = cfg = W.CONFIGS[name]
         t = time.time()
         self.pi = W.PrefillInputs(cfg)
         k, v, kp = self.pi.full_kv()
-        qs = [self.pi.q_chunk(c) for c in range(cfg.n_chunks)]
+        nq = cfg.n_chunks if q_distinct <= 0 else min(q_distinct, cfg.n_chunks)
+        qs = [self.pi.q_chunk(c) for c in range(nq)]
         log(f"prefill inputs drawn in {time.time() - t:.1f}s")
         dev = rtp.to_device_bf16
         self.L = rtp.Layer(1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.kv_role.tolist(),
@@ -281,10 +287,11 @@ class PrefillBench:
         self.k, self.v = dev(k), dev(v)
         self.k_pre = [dev(kp[c * cfg.chunk:(c + 1) * cfg.chunk]) for c in range(cfg.n_chunks)]
         self.q = [dev(q) for q in qs]
+        del k, v, kp, qs
         self.w = dev(self.pi.w_k_idx)
         self.k_idx = torch.zeros(cfg.n_kv_r * cfg.seq_len * 16, dtype=torch.bfloat16, device="cuda")
         self.out = [torch.empty(cfg.chunk * cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
-                    for _ in range(cfg.n_chunks)]
+                    for _ in range(len(self.q))]
         self.ws = rtp.workspace(self.L, cfg.chunk, rtp.CALL_PREFILL)
         self.sm = 1.0 / math.sqrt(cfg.head_dim)
         torch.cuda.synchronize()
@@ -293,8 +300,9 @@ class PrefillBench:
         cfg, rtp = self.cfg, self.rtp
         for c in range(cfg.n_chunks):
             c0, c1 = self.pi.chunk_bounds(c)
-            rtp.rtp_prefill_attn(self.L, c0, c1 - c0, self.q[c], self.k, self.v, self.k_pre[c], self.w,
-                                 cfg.head_dim * 16, self.k_idx, self.sm, self.out[c], self.ws)
+            j = c % len(self.q)
+            rtp.rtp_prefill_attn(self.L, c0, c1 - c0, self.q[j], self.k, self.v, self.k_pre[c], self.w,
+                                 cfg.head_dim * 16, self.k_idx, self.sm, self.out[j], self.ws)
 
     def flops(self):
         """Algorithmic FLOPs: 4*D per attended (row, key) pair, exact mask pair counts, plus the projection."""
@@ -334,6 +342,59 @@ def cpu_baseline(dec: DecodeBench):
                       f"p=0.95), fp64 numpy on 1 thread, scaled by batch {cfg.batch}"}
 
 
+def report_configs(args):
+    """Per-config timings (not the headline line): the fused decode step of every decode
+    workload at its p, and the chunked prefill of both prefill workloads."""
+    import torch
+    from head_wise_sparse_amd import rtp
+    torch.cuda.set_device(0)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = {"report": "per-config timings", "device": torch.cuda.get_device_name(0), "rtp": rtp.rtp_version(),
+           "data": "synthetic (seeded)", "configs": {}}
+    for name, p, copies in (("decode_tiny_2k", 0.9, 3), ("decode_b8_32k", 0.95, 3), ("decode_b4_128k", 0.95, 3),
+                            ("decode_b1_1m", 0.95, 2)):
+        dec = DecodeBench(copies, name)
+        for i in range(max(args.warmup, len(dec.sets))):
+            dec.step(p, i)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for i in range(args.steps):
+            dec.step(p, i)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / args.steps * 1e3
+        ab = dec.algorithmic_bytes(p)
+        gbs = ab["total"] / (us * 1e-6) / 1e9
+        out["configs"][name] = {"p": p, "us_per_step": round(us, 2), "hbm_GBps": round(gbs, 1),
+                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["total"],
+                                "union_tokens": ab["union_tokens"], "sel_mean": ab["sel_mean"],
+                                "sel_median": ab["sel_median"]}
+        log(f"{name}: {us:.1f} us/step")
+        del dec
+        torch.cuda.empty_cache()
+    for name, qd, passes in (("prefill_32k", 0, args.steps), ("prefill_1m", 4, 2)):
+        pre = PrefillBench(name, qd)
+        pre.run()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(passes):
+            pre.run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / passes
+        fl = pre.flops()["total"]
+        tf = fl / (ms * 1e-3) / 1e12
+        out["configs"][name] = {"ms": round(ms, 3), "tflops": round(tf, 1), "mfma_util": round(tf / BF16_PEAK_TFLOPS, 4),
+                                "algorithmic_flops": fl, "chunks": pre.cfg.n_chunks,
+                                "distinct_q_chunks": len(pre.q), "passes": passes}
+        log(f"{name}: {ms:.2f} ms")
+        del pre
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -341,6 +402,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.report_configs:
+        report_configs(args)
         return
     import torch
     from head_wise_sparse_amd import rtp
