@@ -385,6 +385,67 @@ __device__ __forceinline__ void merge_row(const MergeArgs& ma, int row) {
   }
 }
 
+// First level of a two-level merge: splits [chunk*kMergeFan, +kMergeFan) of one row
+// combined into one partial of the same form (accumulator relative to its own max, max,
+// sum), at part2[row][chunk].  256 threads: D/4 float4 lanes x 256/(D/4) split groups.
+template <int D>
+__device__ __forceinline__ void merge_pre_chunk(const MergeArgs& ma, float* __restrict__ part2, int nchunks,
+                                                int row, int chunk) {
+  constexpr int PS = D + 4;
+  constexpr int Q = D / 4;
+  constexpr int SG = 256 / Q;
+  const int tid = threadIdx.x;
+  const int q = tid % Q, sg = tid / Q;
+  const int s0 = chunk * kMergeFan, s1 = min(ma.nsplit, s0 + kMergeFan);
+  const float* pr = ma.part + int64_t(row) * ma.nsplit * PS;
+  __shared__ float s_red[4];
+  __shared__ float4 s_a[SG][Q];
+  __shared__ float s_l[SG];
+  float M = -INFINITY;
+  if (s0 + tid < s1) M = pr[int64_t(s0 + tid) * PS + D];
+  M = wave_max(M);
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float Lsum = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = s0 + sg; s < s1; s += SG) {
+      const float* ps = pr + int64_t(s) * PS;
+      const float ms = ps[D];
+      const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
+      const float4 o = *reinterpret_cast<const float4*>(ps + 4 * q);
+      A.x = fmaf(o.x, f, A.x);
+      A.y = fmaf(o.y, f, A.y);
+      A.z = fmaf(o.z, f, A.z);
+      A.w = fmaf(o.w, f, A.w);
+      Lsum = fmaf(ps[D + 1], f, Lsum);
+    }
+  }
+  s_a[sg][q] = A;
+  if (q == 0) s_l[sg] = Lsum;
+  __syncthreads();
+  float* po = part2 + (int64_t(row) * nchunks + chunk) * PS;
+  if (tid < D) {
+    const int qq = tid >> 2, e = tid & 3;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SG; ++i) {
+      const float4 v = s_a[i][qq];
+      a += e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+    }
+    po[tid] = a;
+  }
+  if (tid == 0) {
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SG; ++i) l += s_l[i];
+    po[D] = M;
+    po[D + 1] = l;
+  }
+}
+
 // Cache addressing of the two decode kinds for the descriptor's layout (host side).
 inline void set_sparse_cache(DecArgs& a, const Layer& L) {
   const bool compact = L.kv_layout == RTP_KV_COMPACT;

@@ -122,13 +122,20 @@ size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx) {
   return round_up(rows * size_t(nsplit) * (L.D + 4) * sizeof(float), 256);
 }
 
+size_t dec_sparse_part2_offset(const Layer& L, int64_t n_ctx) {
+  const int64_t nsplit = (n_ctx + kDecRange - 1) / kDecRange;
+  const size_t rows = size_t(L.B) * L.n_ret * L.G;
+  return round_up(dec_sparse_starts_offset(L, n_ctx) + rows * size_t(nsplit + 1) * sizeof(int32_t), 256);
+}
+
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
   int64_t nsplit;
   size_t rows;
   if (sparse) {
     nsplit = (n_ctx + kDecRange - 1) / kDecRange;
     rows = size_t(L.B) * L.n_ret * L.G;
-    return round_up(dec_sparse_starts_offset(L, n_ctx) + rows * size_t(nsplit + 1) * sizeof(int32_t), 256);
+    const size_t chunks = size_t(merge_chunks(int(nsplit)));
+    return round_up(dec_sparse_part2_offset(L, n_ctx) + rows * chunks * (L.D + 4) * sizeof(float), 256);
   } else {
     int64_t s_end = L.n_sinks < n_ctx ? L.n_sinks : n_ctx;
     int64_t w_start = n_ctx - L.window > s_end ? n_ctx - L.window : s_end;

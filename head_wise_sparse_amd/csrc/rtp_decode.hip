@@ -77,8 +77,26 @@ rtp_status dispatch_partial(const Layer& L, dim3 grid, hipStream_t s, const DecA
   return fail(RTP_EUNSUPPORTED, "decode: unsupported head_dim/group");
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_merge_pre(MergeArgs ma, float* part2, int nchunks) {
+  merge_pre_chunk<D>(ma, part2, nchunks, blockIdx.y, blockIdx.x);
+}
+
+// part2: second-level partials for rows with more than kMergeDirect splits (else unused)
 rtp_status launch_merge(const Layer& L, int rows, int nsplit, const HeadMap& map, const float* part,
-                        uint16_t* out, hipStream_t s) {
+                        uint16_t* out, hipStream_t s, float* part2 = nullptr) {
+  const int nchunks = part2 ? merge_chunks(nsplit) : 0;
+  if (nchunks) {
+    const MergeArgs m1{part, nsplit, L.G, L.Hq, map, out};
+    if (L.D == 128)
+      hipLaunchKernelGGL(k_decode_merge_pre<128>, dim3(nchunks, rows), dim3(256), 0, s, m1, part2, nchunks);
+    else
+      hipLaunchKernelGGL(k_decode_merge_pre<64>, dim3(nchunks, rows), dim3(256), 0, s, m1, part2, nchunks);
+    rtp_status st = check_launch("k_decode_merge_pre");
+    if (st != RTP_OK) return st;
+    part = part2;
+    nsplit = nchunks;
+  }
   const MergeArgs ma{part, nsplit, L.G, L.Hq, map, out};
   if (L.D == 128)
     hipLaunchKernelGGL(k_decode_merge<128>, dim3(rows), dim3(256), 0, s, ma);
@@ -146,7 +164,8 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
   a.map = ret_map(L);
   set_sparse_cache(a, L);
   if ((st = dispatch_partial<true>(L, dim3(nsplit, L.B * L.n_ret), s, a)) != RTP_OK) return st;
-  return launch_merge(L, rows, nsplit, a.map, part, out, s);
+  return launch_merge(L, rows, nsplit, a.map, part, out, s,
+                      reinterpret_cast<float*>(static_cast<char*>(ws) + dec_sparse_part2_offset(L, n_ctx)));
 }
 
 extern "C" rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q,

@@ -117,6 +117,12 @@ constexpr int kWinRange = 256;           // list positions per block (window pat
 constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);   // partials [rows][nsplit][D + 4]
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows][nsplit+1] after partials
+// Rows with more than kMergeDirect splits are merged in two levels: first kMergeFan
+// splits at a time into second-level partials (after the range index), then those.
+constexpr int kMergeFan = 32;
+constexpr int kMergeDirect = 128;
+inline int merge_chunks(int nsplit) { return nsplit > kMergeDirect ? (nsplit + kMergeFan - 1) / kMergeFan : 0; }
+size_t dec_sparse_part2_offset(const Layer& L, int64_t n_ctx);    // float [rows][chunks][D + 4]
 
 // Prefill.
 size_t prefill_ws_bytes(const Layer& L, int64_t C);

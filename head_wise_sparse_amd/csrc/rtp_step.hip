@@ -38,6 +38,11 @@ __global__ __launch_bounds__(kDecThreads, 4) void k_step_sparse(DecArgs a) {
 }
 
 template <int D>
+__global__ __launch_bounds__(256) void k_step_merge_pre(MergeArgs ms, float* part2, int nchunks) {
+  merge_pre_chunk<D>(ms, part2, nchunks, blockIdx.y, blockIdx.x);
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void k_step_merge(MergeArgs ms, int rows_s, MergeArgs mw) {
   const int i = blockIdx.x;
   if (i < rows_s) merge_row<D>(ms, i);
@@ -247,7 +252,18 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
 
   // ---- launch 7: merge the split partials of both head kinds
   const int rows_w = L.B * L.n_loc * L.G;
-  const MergeArgs ms{reinterpret_cast<const float*>(w + lay.sparse), nsplit, L.G, L.Hq, ret_map(L), out};
+  MergeArgs ms{reinterpret_cast<const float*>(w + lay.sparse), nsplit, L.G, L.Hq, ret_map(L), out};
+  const int nchunks = L.n_ret ? merge_chunks(nsplit) : 0;
+  if (nchunks) {           // long rows: merge kMergeFan splits at a time first
+    float* part2 = reinterpret_cast<float*>(w + lay.sparse + dec_sparse_part2_offset(L, n_ctx));
+    if (L.D == 128)
+      hipLaunchKernelGGL(k_step_merge_pre<128>, dim3(nchunks, rows_s), dim3(256), 0, s, ms, part2, nchunks);
+    else
+      hipLaunchKernelGGL(k_step_merge_pre<64>, dim3(nchunks, rows_s), dim3(256), 0, s, ms, part2, nchunks);
+    if ((st = check_launch("k_step_merge_pre")) != RTP_OK) return st;
+    ms.part = part2;
+    ms.nsplit = nchunks;
+  }
   const MergeArgs mw{reinterpret_cast<const float*>(w + lay.window), win_gx, L.G, L.Hq, loc_map(L), out};
   const unsigned mrows = unsigned((L.n_ret ? rows_s : 0) + (L.n_loc ? rows_w : 0));
   const int rs = L.n_ret ? rows_s : 0;

@@ -233,7 +233,8 @@ def _sel_tensors(sets, B, R, cap):
 
 
 @pytest.mark.parametrize("name,over", [("decode_tiny_2k", {}), ("decode_b8_32k", {}),
-                                       ("decode_b8_32k", dict(batch=2, n_ctx=5000))])
+                                       ("decode_b8_32k", dict(batch=2, n_ctx=5000)),
+                                       ("decode_b1_1m", dict(n_ctx=200000))])     # > 128 splits: two-level merge
 def test_sparse_decode_on_oracle_sets(name, over):
     P.require_gpu()
     torch = _torch()
@@ -431,7 +432,8 @@ def _assert_same(a, b, what):
 
 @pytest.mark.parametrize("name,p,over", [("decode_tiny_2k", 0.9, {}), ("decode_b8_32k", 0.95, dict(batch=2, n_ctx=9000)),
                                          ("decode_b8_32k", 1.0, dict(batch=1, n_ctx=5000)),
-                                         ("decode_b4_128k", 0.99, dict(batch=1))])
+                                         ("decode_b4_128k", 0.99, dict(batch=1)),
+                                         ("decode_b1_1m", 0.95, dict(n_ctx=200000))])
 def test_fused_step_matches_separate_calls(name, p, over):
     """rtp_decode_step gives the same bits as the four calls one after the other."""
     P.require_gpu()
