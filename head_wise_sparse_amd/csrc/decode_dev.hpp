@@ -44,11 +44,12 @@ struct DecArgs {
   const uint16_t* v;
   const int32_t* sel_idx;     // sparse only
   const int32_t* starts;      // sparse only: [rows][nsplit + 1]
-  float* part;                // [rows][nsplit][D + 4]: accumulator, max, sum (16-byte rows)
+  float* part;                // [rows][nsplit * nsub][D + 4]: accumulator, max, sum (16-byte rows)
   int n_ctx;
   int64_t n_cap;
   int Hq, Hkv;
-  int nsplit;
+  int nsplit;                 // sparse: index ranges (row stride of `starts` is nsplit + 1); window: slices
+  int nsub;                   // sparse: blocks per range, each taking one slice of its union list
   float scale_log2;           // sm_scale * log2(e)
   int s_end, w_start, list_len;   // window only
   HeadMap map;
@@ -61,9 +62,13 @@ struct DecArgs {
   int ring_off;               // (w_start - ring_s) % ring_w: ring row of the first window token
 };
 
-// One block of split-K decode: slice `split` of group `grp` (= b * n_heads_of_kind + rank).
+// One block of split-K decode: partial slot `slot` of group `grp` (= b * n_heads_of_kind
+// + rank).  Sparse path: slot = range * nsub + sub; the block builds the union list of
+// index range `range` and takes the sub-th of nsub equal slices of it (whole stages).
 template <int D, int G, bool SPARSE>
-__device__ __forceinline__ void decode_block(const DecArgs& a, int split, int grp) {
+__device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp) {
+  const int split = SPARSE ? slot / a.nsub : slot;       // index range (sparse) / list slice (window)
+  const int sub = SPARSE ? slot % a.nsub : 0;
   constexpr int LPT = D / 8;            // lanes per cached row
   constexpr int TPW = 64 / LPT;         // rows per wave step
   constexpr int NLG = (kDecThreads / 64) * TPW;
@@ -95,7 +100,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
     qw[t][3] = qv.w;
   }
 
-  int U, j0 = 0, p0 = 0;
+  int U, j0 = 0, p0 = 0, e0 = 0;
   if constexpr (SPARSE) {
     j0 = split * RANGE;
     for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
@@ -169,6 +174,12 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
     }
     U = total;
     __syncthreads();
+    if (a.nsub > 1) {          // this block's slice of the union list: positions [e0, e0 + U)
+      constexpr int STEP0 = kDecUnroll * NLG;
+      const int chunk = ((U + a.nsub - 1) / a.nsub + STEP0 - 1) / STEP0 * STEP0;
+      e0 = min(U, sub * chunk);
+      U = min(U, e0 + chunk) - e0;
+    }
   } else {
     p0 = split * RANGE;
     U = min(RANGE, a.list_len - p0);
@@ -185,8 +196,8 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
 
   auto token_of = [&](int e, uint32_t& mask) -> int64_t {
     if constexpr (SPARSE) {
-      mask = s_lmask[e];
-      return int64_t(j0) + s_list[e];
+      mask = s_lmask[e0 + e];
+      return int64_t(j0) + s_list[e0 + e];
     } else {
       mask = (1u << G) - 1u;
       const int p = p0 + e;
@@ -307,7 +318,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int split, int gr
       A += s_wacc[w][t][d] * f;
       Lsum += s_wl[w][t] * f;
     }
-    float* pr = a.part + ((int64_t(grp) * G + t) * a.nsplit + split) * (D + 4);
+    float* pr = a.part + ((int64_t(grp) * G + t) * a.nsplit * a.nsub + slot) * (D + 4);
     pr[d] = A;
     if (d == 0) {
       pr[D] = M;
@@ -453,8 +464,10 @@ inline void set_sparse_cache(DecArgs& a, const Layer& L) {
   a.by_rank = compact;
   a.cache_rows = L.n_cap;
   a.ring_s = a.ring_w = a.ring_off = 0;
+  a.nsub = dec_sub(a.nsplit, L.B * L.n_ret);
 }
 inline void set_window_cache(DecArgs& a, const Layer& L) {      // after s_end / w_start are set
+  a.nsub = 1;
   if (L.kv_layout == RTP_KV_COMPACT) {
     a.cache_heads = L.n_loc;
     a.by_rank = 1;

@@ -119,7 +119,10 @@ SelLayout sel_layout(const Layer& L) {
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx) {
   const int64_t nsplit = (n_ctx + kDecRange - 1) / kDecRange;
   const size_t rows = size_t(L.B) * L.n_ret * L.G;
-  return round_up(rows * size_t(nsplit) * (L.D + 4) * sizeof(float), 256);
+  // sized for the most blocks per range any call may use, so that a workspace sized
+  // for a longer context also serves every shorter one
+  const size_t slots = size_t(nsplit) * kDecSubMax;
+  return round_up(rows * slots * (L.D + 4) * sizeof(float), 256);
 }
 
 size_t dec_sparse_part2_offset(const Layer& L, int64_t n_ctx) {
@@ -134,7 +137,7 @@ size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
   if (sparse) {
     nsplit = (n_ctx + kDecRange - 1) / kDecRange;
     rows = size_t(L.B) * L.n_ret * L.G;
-    const size_t chunks = size_t(merge_chunks(int(nsplit)));
+    const size_t chunks = size_t(merge_chunks(int(nsplit) * kDecSubMax));
     return round_up(dec_sparse_part2_offset(L, n_ctx) + rows * chunks * (L.D + 4) * sizeof(float), 256);
   } else {
     int64_t s_end = L.n_sinks < n_ctx ? L.n_sinks : n_ctx;

@@ -163,8 +163,8 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
   a.scale_log2 = sm_scale * kLog2e;
   a.map = ret_map(L);
   set_sparse_cache(a, L);
-  if ((st = dispatch_partial<true>(L, dim3(nsplit, L.B * L.n_ret), s, a)) != RTP_OK) return st;
-  return launch_merge(L, rows, nsplit, a.map, part, out, s,
+  if ((st = dispatch_partial<true>(L, dim3(nsplit * a.nsub, L.B * L.n_ret), s, a)) != RTP_OK) return st;
+  return launch_merge(L, rows, nsplit * a.nsub, a.map, part, out, s,
                       reinterpret_cast<float*>(static_cast<char*>(ws) + dec_sparse_part2_offset(L, n_ctx)));
 }
 

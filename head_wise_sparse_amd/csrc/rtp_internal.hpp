@@ -115,7 +115,15 @@ constexpr int kDecThreads = 256;
 constexpr int kDecRange = RTP_SEL_RANGE; // token-index range per block (sparse path)
 constexpr int kWinRange = 256;           // list positions per block (window path)
 constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
-size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);   // partials [rows][nsplit][D + 4]
+// Sparse path: blocks per index range (each takes one slice of the range's union list),
+// chosen per call so that the grid is about one round of resident blocks
+constexpr int kDecSubMax = 4;
+constexpr int kDecBlocksTarget = 1024;
+inline int dec_sub(int nsplit, int groups) {
+  int n = kDecBlocksTarget / (nsplit * groups > 0 ? nsplit * groups : 1);
+  return n < 1 ? 1 : (n > kDecSubMax ? kDecSubMax : n);
+}
+size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);   // partials [rows][slots][D + 4]
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows][nsplit+1] after partials
 // Rows with more than kMergeDirect splits are merged in two levels: first kMergeFan
 // splits at a time into second-level partials (after the range index), then those.

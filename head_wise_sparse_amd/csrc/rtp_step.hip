@@ -247,13 +247,14 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
     da.scale_log2 = sm_scale * kLog2eStep;
     da.map = ret_map(L);
     set_sparse_cache(da, L);
-    if ((st = dispatch_sparse(L, dim3(nsplit, L.B * L.n_ret), s, da)) != RTP_OK) return st;
+    if ((st = dispatch_sparse(L, dim3(nsplit * da.nsub, L.B * L.n_ret), s, da)) != RTP_OK) return st;
   }
 
   // ---- launch 7: merge the split partials of both head kinds
   const int rows_w = L.B * L.n_loc * L.G;
-  MergeArgs ms{reinterpret_cast<const float*>(w + lay.sparse), nsplit, L.G, L.Hq, ret_map(L), out};
-  const int nchunks = L.n_ret ? merge_chunks(nsplit) : 0;
+  const int nslots = nsplit * (L.n_ret ? dec_sub(nsplit, L.B * L.n_ret) : 1);   // sparse partials per row
+  MergeArgs ms{reinterpret_cast<const float*>(w + lay.sparse), nslots, L.G, L.Hq, ret_map(L), out};
+  const int nchunks = L.n_ret ? merge_chunks(nslots) : 0;
   if (nchunks) {           // long rows: merge kMergeFan splits at a time first
     float* part2 = reinterpret_cast<float*>(w + lay.sparse + dec_sparse_part2_offset(L, n_ctx));
     if (L.D == 128)
