@@ -50,6 +50,7 @@ struct DecArgs {
   int Hq, Hkv;
   int nsplit;                 // sparse: index ranges (row stride of `starts` is nsplit + 1); window: slices
   int nsub;                   // sparse: blocks per range, each taking one slice of its union list
+  int wrange;                 // window: list positions per block
   float scale_log2;           // sm_scale * log2(e)
   int s_end, w_start, list_len;   // window only
   HeadMap map;
@@ -72,7 +73,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
   constexpr int LPT = D / 8;            // lanes per cached row
   constexpr int TPW = 64 / LPT;         // rows per wave step
   constexpr int NLG = (kDecThreads / 64) * TPW;
-  constexpr int RANGE = SPARSE ? kDecRange : kWinRange;
+  constexpr int RANGE = kDecRange;      // sparse path (the window path slices a.wrange positions)
   constexpr int NW = kDecThreads / 64;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -181,8 +182,8 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
       U = min(U, e0 + chunk) - e0;
     }
   } else {
-    p0 = split * RANGE;
-    U = min(RANGE, a.list_len - p0);
+    p0 = split * a.wrange;
+    U = min(a.wrange, a.list_len - p0);
   }
 
   float m[G], l[G], acc[G][8];

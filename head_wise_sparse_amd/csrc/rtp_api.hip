@@ -131,6 +131,11 @@ size_t dec_sparse_part2_offset(const Layer& L, int64_t n_ctx) {
   return round_up(dec_sparse_starts_offset(L, n_ctx) + rows * size_t(nsplit + 1) * sizeof(int32_t), 256);
 }
 
+int win_range_for(const Layer& L, int64_t n_ctx, int64_t len) {
+  const int64_t score_blocks = L.n_ret ? (n_ctx + kScoreTile - 1) / kScoreTile * L.B * L.n_ret : 0;
+  return win_range(len, L.B * L.n_loc, int(score_blocks > kDecBlocksTarget ? kDecBlocksTarget : score_blocks));
+}
+
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
   int64_t nsplit;
   size_t rows;
@@ -143,7 +148,7 @@ size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse) {
     int64_t s_end = L.n_sinks < n_ctx ? L.n_sinks : n_ctx;
     int64_t w_start = n_ctx - L.window > s_end ? n_ctx - L.window : s_end;
     int64_t len = s_end + (n_ctx - w_start);
-    nsplit = (len + kWinRange - 1) / kWinRange;
+    nsplit = (len + kWinRangeShort - 1) / kWinRangeShort;   // the most slices any call uses
     rows = size_t(L.B) * L.n_loc * L.G;
   }
   return round_up(rows * size_t(nsplit) * (L.D + 4) * sizeof(float), 256);

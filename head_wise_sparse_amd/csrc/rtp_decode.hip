@@ -185,7 +185,8 @@ extern "C" rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n
   const int64_t s_end = std::min<int64_t>(L.n_sinks, n_ctx);
   const int64_t w_start = std::max<int64_t>(n_ctx - L.window, s_end);
   const int64_t len = s_end + (n_ctx - w_start);
-  const int nsplit = int((len + kWinRange - 1) / kWinRange);
+  const int wr = win_range_for(L, n_ctx, len);
+  const int nsplit = int((len + wr - 1) / wr);
   const int rows = L.B * L.n_loc * L.G;
   DecArgs a{};
   a.q = q;
@@ -201,6 +202,7 @@ extern "C" rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n
   a.s_end = int(s_end);
   a.w_start = int(w_start);
   a.list_len = int(len);
+  a.wrange = wr;
   a.map = loc_map(L);
   set_window_cache(a, L);
   if ((st = dispatch_partial<false>(L, dim3(nsplit, L.B * L.n_loc), s, a)) != RTP_OK) return st;

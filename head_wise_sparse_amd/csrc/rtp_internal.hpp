@@ -113,7 +113,8 @@ rtp_status launch_select(const SelArgs& a, int rows, hipStream_t s);
 // Decode attention (sparse and window share the layout).
 constexpr int kDecThreads = 256;
 constexpr int kDecRange = RTP_SEL_RANGE; // token-index range per block (sparse path)
-constexpr int kWinRange = 256;           // list positions per block (window path)
+constexpr int kWinRange = 256;           // list positions per block (window path) ...
+constexpr int kWinRangeShort = 128;      // ... or half that when the launch then still fits one round
 constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
 // Sparse path: blocks per index range (each takes one slice of the range's union list),
 // chosen per call so that the grid is about one round of resident blocks
@@ -123,7 +124,16 @@ inline int dec_sub(int nsplit, int groups) {
   int n = kDecBlocksTarget / (nsplit * groups > 0 ? nsplit * groups : 1);
   return n < 1 ? 1 : (n > kDecSubMax ? kDecSubMax : n);
 }
+// window slice length for `len` list positions and `groups` (batch x local KV heads),
+// sharing a launch with `other` blocks
+inline int win_range(int64_t len, int groups, int other) {
+  const int64_t n_short = (len + kWinRangeShort - 1) / kWinRangeShort * groups;
+  return other + n_short <= kDecBlocksTarget ? kWinRangeShort : kWinRange;
+}
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);   // partials [rows][slots][D + 4]
+// window slice length of a call (the same for the separate call and the fused step, which
+// would run the scoring blocks beside the window blocks; equal results need equal slices)
+int win_range_for(const Layer& L, int64_t n_ctx, int64_t len);
 size_t dec_sparse_starts_offset(const Layer& L, int64_t n_ctx);   // int32 [rows][nsplit+1] after partials
 // Rows with more than kMergeDirect splits are merged in two levels: first kMergeFan
 // splits at a time into second-level partials (after the range index), then those.

@@ -178,7 +178,8 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
     const int64_t s_end = std::min<int64_t>(L.n_sinks, n_ctx);
     const int64_t w_start = std::max<int64_t>(n_ctx - L.window, s_end);
     const int64_t len = s_end + (n_ctx - w_start);
-    win_gx = int((len + kWinRange - 1) / kWinRange);
+    wa.wrange = win_range_for(L, n_ctx, len);
+    win_gx = int((len + wa.wrange - 1) / wa.wrange);
     n_win = win_gx * L.B * L.n_loc;
     wa.q = q;
     wa.k = k_cache;
