@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0
 # changes the figure no longer describes the kernel and `traffic` is reported as null.
 COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
 MEASURED_KIB = {
-    "prefill_attn": {"src": ("rtp_prefill.hip", "8def4a56e3892bc0"),
-                     "fetch": 1076.8 + 188489.6, "write": 256.0 + 32771.8},
-    "sparse_decode": {"src": ("decode_dev.hpp", "1c8849e44a8c1cac"),
-                      "fetch": 172590.7 + 1081.0, "write": 2176.3 + 8.0},
+    "prefill_attn": {"src": ("rtp_prefill.hip", "e84777a0b3f5702b"),
+                     "fetch": 1076.8 + 216242.6, "write": 256.0 + 33793.5},
+    "sparse_decode": {"src": ("decode_dev.hpp", "a902b732dd649f6d"),
+                      "fetch": 172605.7 + 1086.5, "write": 2176.2 + 8.0},
 }
 
 
