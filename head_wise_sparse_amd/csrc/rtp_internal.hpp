@@ -83,7 +83,7 @@ struct SelRows {                 // device views of the selection workspace
   uint64_t* cmass;               // [rows][3][64]   coarse summaries (32 fine bins each)
   uint32_t* ccnt;                // [rows][3][64]
   SelRowState* state;            // [rows]
-  uint32_t* ctr;                 // [rows][2]       compaction: [1] blocks done
+  uint32_t* ctr;                 // [rows][2]       compaction: [1] blocks done ([0] unused, kept zero)
   uint4* tilerec;                // [rows][nblk]    per tile: counts against the level-1 prefix (hist<2>)
 };
 struct SelArgs {
