@@ -58,7 +58,9 @@ size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
 // Top-p selection (four launches; the workspace is zero before and after a call).
 constexpr int kSelThreads = 256;
 constexpr int kSelItems = 16;
-constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per block
+constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per block ...
+constexpr int kSelItemsLong = 32;                                // ... or twice that when a pass would
+                                                                 // otherwise take more than one round of blocks
 constexpr int kBins = 2048;                                     // 11-bit digits (last level 10 bits)
 struct SelLevelState {           // what is known after resolving one level's digit
   uint32_t prefix;               // key bits resolved so far
@@ -98,7 +100,8 @@ struct SelArgs {
   int64_t k_target;
   int n_ctx;
   int64_t n_cap;
-  int nblk;                      // selection tiles per row (from n_ctx)
+  int nblk;                      // selection tiles per row (from n_ctx; set by launch_select)
+  int items;                     // scores per thread per tile (kSelItems or kSelItemsLong; set by launch_select)
   int rec_stride;                // tile records per row (from n_cap)
   int32_t* sel_idx;
   int32_t* sel_count;

@@ -233,8 +233,9 @@ __device__ float row_max_from_partials(const SelArgs& a, int row, int blk, int t
   return m;
 }
 
-template <int LEVEL>
+template <int LEVEL, int ITEMS>
 __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
+  constexpr int TILE = kSelThreads * ITEMS;
   constexpr int NB = LEVEL == 2 ? 1024 : 2048;
   constexpr int SHIFT = LEVEL == 0 ? 21 : (LEVEL == 1 ? 10 : 0);
   constexpr int PSHIFT = LEVEL == 1 ? 21 : 10;                     // prefix bits start (levels 1, 2)
@@ -248,10 +249,10 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
 
   // scores of the tile: unconditional loads (index clamped), validity kept aside
   const float* sp = a.scores + int64_t(row) * a.n_cap;
-  const int64_t base = int64_t(blk) * kSelTile;
-  float sv[kSelItems];
+  const int64_t base = int64_t(blk) * TILE;
+  float sv[ITEMS];
 #pragma unroll
-  for (int it = 0; it < kSelItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
     sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
   }
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   const uint32_t prefix = LEVEL > 0 ? s_prefix : 0u;
   uint32_t n_above = 0;                             // level 2: tokens above the 22-bit prefix
 #pragma unroll
-  for (int it = 0; it < kSelItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
     const uint32_t key = score_key(sv[it]);
     const bool match = (j < a.n_ctx) && (LEVEL == 0 || (key >> PSHIFT) == prefix);
@@ -356,23 +357,26 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
 }
 
 // Resolve the last digit, then write {key > t} U {first r with key == t} in order.
+template <int ITEMS>
 __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
+  constexpr int TILE = kSelThreads * ITEMS;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int row = blockIdx.y, tile = blockIdx.x;
   constexpr int NW = kSelThreads / 64;
-  static_assert(kSelItems * NW == 64, "one wave scans the per-(item, wave) counts");
+  constexpr int PL = ITEMS * NW / 64;                 // (item, wave) counts per lane of the scanning wave
+  static_assert(ITEMS * NW % 64 == 0 && ITEMS <= 32, "one wave scans the per-(item, wave) counts");
   __shared__ uint32_t s_t, s_r;
-  __shared__ uint32_t s_wa[kSelItems * NW], s_we[kSelItems * NW];   // counts, then exclusive prefixes
+  __shared__ uint32_t s_wa[ITEMS * NW], s_we[ITEMS * NW];   // counts, then exclusive prefixes
   __shared__ uint32_t s_pa, s_pe, s_heavy, s_last;
   __shared__ uint32_t s_ra[NW], s_re[NW];
   __shared__ uint32_t s_heavy_list[kMaxHeavy];
   uint32_t* ctr = a.R.ctr + 2 * int64_t(row);
   const uint4* rec = a.R.tilerec + int64_t(row) * a.rec_stride;
   const float* sp = a.scores + int64_t(row) * a.n_cap;
-  const int64_t base = int64_t(tile) * kSelTile;
-  float sv[kSelItems];
+  const int64_t base = int64_t(tile) * TILE;
+  float sv[ITEMS];
 #pragma unroll
-  for (int it = 0; it < kSelItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
     sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
   }
@@ -440,19 +444,20 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
       s_heavy = nh;
     }
   }
-  bool fa[kSelItems], fe[kSelItems];
-  uint64_t ba[kSelItems], be[kSelItems];
+  // this thread's tokens above t / tied with t, one bit per item (ballots are taken again
+  // when writing, so that they need not stay in registers)
+  uint32_t fa = 0, fe = 0;
 #pragma unroll
-  for (int it = 0; it < kSelItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
     const uint32_t key = score_key(sv[it]);
-    fa[it] = (j < a.n_ctx) && key > t;
-    fe[it] = (j < a.n_ctx) && key == t;
-    ba[it] = __ballot(fa[it]);
-    be[it] = __ballot(fe[it]);
+    const bool above = (j < a.n_ctx) && key > t, tied = (j < a.n_ctx) && key == t;
+    fa |= uint32_t(above) << it;
+    fe |= uint32_t(tied) << it;
+    const uint64_t ba = __ballot(above), be = __ballot(tied);
     if (lane == 0) {
-      s_wa[it * NW + wave] = __popcll(ba[it]);
-      s_we[it * NW + wave] = __popcll(be[it]);
+      s_wa[it * NW + wave] = __popcll(ba);
+      s_we[it * NW + wave] = __popcll(be);
     }
   }
   __syncthreads();
@@ -463,9 +468,9 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     const int nt = listed ? int(nheavy) : tile;
     uint32_t ga = 0, ge = 0;
     for (int h = 0; h < nt; ++h) {
-      const int64_t tb = int64_t(listed ? s_heavy_list[h] : h) * kSelTile;
+      const int64_t tb = int64_t(listed ? s_heavy_list[h] : h) * TILE;
 #pragma unroll 4
-      for (int k = tid; k < kSelTile; k += kSelThreads) {
+      for (int k = tid; k < TILE; k += kSelThreads) {
         const uint32_t key = score_key(sp[tb + k]);          // earlier tiles are full: tb + k < base
         const bool cand = (key >> 10) == (t >> 10);
         ga += uint32_t(cand && key > t);
@@ -503,8 +508,15 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   if (tid == 0) done_before = atomicAdd(ctr + 1, 1u);
   // exclusive prefix of the per-(item, wave) counts, in token order (item-major)
   if (wave == 0) {
-    const uint32_t va = s_wa[lane], ve = s_we[lane];
-    uint32_t xa = va, xe = ve;
+    uint32_t va[PL], ve[PL], sa = 0, se = 0;      // lane takes entries PL*lane .. PL*lane+PL-1
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      va[k] = s_wa[PL * lane + k];
+      ve[k] = s_we[PL * lane + k];
+      sa += va[k];
+      se += ve[k];
+    }
+    uint32_t xa = sa, xe = se;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t ya = __shfl_up(xa, o, 64), ye = __shfl_up(xe, o, 64);
@@ -513,8 +525,15 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
         xe += ye;
       }
     }
-    s_wa[lane] = xa - va;
-    s_we[lane] = xe - ve;
+    xa -= sa;
+    xe -= se;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      s_wa[PL * lane + k] = xa;
+      s_we[PL * lane + k] = xe;
+      xa += va[k];
+      xe += ve[k];
+    }
   }
   __syncthreads();
   const uint32_t pa = s_pa, pe = s_pe;                 // counts of every earlier token
@@ -522,16 +541,17 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   int32_t* out = a.sel_idx + int64_t(row) * a.n_cap;
   constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
 #pragma unroll
-  for (int it = 0; it < kSelItems; ++it) {
+  for (int it = 0; it < ITEMS; ++it) {
     const uint32_t ca = pa + s_wa[it * NW + wave], ce = pe + s_we[it * NW + wave];
     if (a.starts && it % IT_PER_RANGE == 0 && tid == 0) {
       // first token of a decode range: the number of selected tokens before it
       const int64_t q = (base + it * kSelThreads) / kDecRange;
       if (q < a.nsplit) a.starts[int64_t(row) * (a.nsplit + 1) + q] = int32_t(ca + (ce < r ? ce : r));
     }
-    const uint32_t a_before = ca + __popcll(ba[it] & lt);
-    const uint32_t e_before = ce + __popcll(be[it] & lt);
-    const bool take = fa[it] || (fe[it] && e_before < r);
+    const bool above = (fa >> it) & 1u, tied = (fe >> it) & 1u;
+    const uint32_t a_before = ca + __popcll(__ballot(above) & lt);
+    const uint32_t e_before = ce + __popcll(__ballot(tied) & lt);
+    const bool take = above || (tied && e_before < r);
     if (take) out[a_before + (e_before < r ? e_before : r)] = int32_t(base + it * kSelThreads + tid);
   }
   // the last block of the row to be counted clears what this launch read: every other
@@ -608,7 +628,6 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.top_p = top_p;
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
-  a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
   a.rec_stride = lay.nblk_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
@@ -644,7 +663,6 @@ extern "C" rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.k_target = k;
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
-  a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
   a.rec_stride = lay.nblk_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
@@ -664,14 +682,29 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
                        a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
     return check_launch("k_sel_all");
   }
-  const dim3 grid(a.nblk, rows);
-  hipLaunchKernelGGL(k_sel_hist<0>, grid, dim3(kSelThreads), 0, s, a);
-  if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
-  hipLaunchKernelGGL(k_sel_hist<1>, grid, dim3(kSelThreads), 0, s, a);
-  if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
-  hipLaunchKernelGGL(k_sel_hist<2>, grid, dim3(kSelThreads), 0, s, a);
-  if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
-  hipLaunchKernelGGL(k_sel_compact, grid, dim3(kSelThreads), 0, s, a);
+  // tile size: 16 scores per thread, or 32 when that keeps a pass to one round of blocks
+  SelArgs b = a;
+  const int64_t nblk16 = (int64_t(a.n_ctx) + kSelTile - 1) / kSelTile;
+  b.items = nblk16 * rows > kDecBlocksTarget ? kSelItemsLong : kSelItems;
+  b.nblk = int((int64_t(a.n_ctx) + kSelThreads * b.items - 1) / (kSelThreads * b.items));
+  const dim3 grid(b.nblk, rows);
+  if (b.items == kSelItems) {
+    hipLaunchKernelGGL((k_sel_hist<0, kSelItems>), grid, dim3(kSelThreads), 0, s, b);
+    if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
+    hipLaunchKernelGGL((k_sel_hist<1, kSelItems>), grid, dim3(kSelThreads), 0, s, b);
+    if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
+    hipLaunchKernelGGL((k_sel_hist<2, kSelItems>), grid, dim3(kSelThreads), 0, s, b);
+    if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
+    hipLaunchKernelGGL((k_sel_compact<kSelItems>), grid, dim3(kSelThreads), 0, s, b);
+  } else {
+    hipLaunchKernelGGL((k_sel_hist<0, kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
+    if ((st = check_launch("k_sel_hist<0>")) != RTP_OK) return st;
+    hipLaunchKernelGGL((k_sel_hist<1, kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
+    if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
+    hipLaunchKernelGGL((k_sel_hist<2, kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
+    if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
+    hipLaunchKernelGGL((k_sel_compact<kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
+  }
   return check_launch("k_sel_compact");
 }
 

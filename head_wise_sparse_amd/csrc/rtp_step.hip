@@ -219,8 +219,7 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
     a.top_p = top_p;
     a.n_ctx = n;
     a.n_cap = L.n_cap;
-    a.nblk = int((n_ctx + kSelTile - 1) / kSelTile);
-    a.rec_stride = sl.nblk_max;
+      a.rec_stride = sl.nblk_max;
     a.sel_idx = sel_idx;
     a.sel_count = sel_count;
     a.starts = starts;

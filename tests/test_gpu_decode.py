@@ -204,6 +204,13 @@ def _edge_rows():
     # a narrow spread over more than 256 tiles: every tile holds many distinct candidates,
     # so late tiles recount all earlier tiles instead of a list of the heavy ones
     yield "narrow_many_heavy_tiles", (5 + rng.standard_normal((1, 4096 * 268 + 100)) * 1e-3).astype(np.float32), 0.9
+    # enough rows x tiles that the passes use 8192-token tiles: plain, tied and narrow rows,
+    # ragged tail
+    n = 8192 * 15 + 123
+    z = (rng.standard_normal((36, n)) * 3).astype(np.float32)
+    z[12:24] = np.round(z[12:24], 2)
+    z[24:] = (5 + rng.standard_normal((12, n)) * 1e-3).astype(np.float32)
+    yield "long_tiles", z, 0.9
 
 
 @pytest.mark.parametrize("case", list(_edge_rows()), ids=lambda c: c[0])
