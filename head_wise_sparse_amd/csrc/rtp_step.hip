@@ -10,7 +10,9 @@
 //      statistics (no separate finalize launch);
 //   3-4. the two further radix passes;  5. compaction, which also writes the range
 //      index of every selected list;  6. the retrieval heads' split-K blocks;
-//   7. one merge launch for the split partials of both head kinds.
+//   7. one merge launch for the split partials of both head kinds (preceded, when a
+//      retrieval row has more than 128 split partials, by a launch that combines
+//      them 32 at a time).
 #include <cmath>
 
 #include "score_dev.hpp"

@@ -250,7 +250,9 @@ rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, int32_t C,
  *   bit (abstract, observations (1)-(3); summary, "Approach").
  * It enqueues seven launches instead of thirteen: the local heads' attention
  * runs in the same launch as the indexer scoring, the first radix pass also
- * reduces the row statistics, and one merge launch serves both head kinds.
+ * reduces the row statistics, and one merge launch serves both head kinds
+ * (above 128K tokens the retrieval rows' merge takes one more launch: it
+ * combines 32 split partials at a time first).
  *
  *   q_pre, w_q_idx, w_head_stride, k_idx, idx_scale   as rtp_indexer_score
  *   q, k_cache, v_cache, sm_scale                     as the decode calls (RTP_KV_COMPACT:
