@@ -8,10 +8,12 @@
 //    head (pre-RoPE projection, summary "Approach"; abstract, observation (2)).
 //
 // Attention kernel (flash-attention forward, bf16 in / fp32 accumulate, D = 128):
-//  - a block owns 128 query rows of one head (4 waves x 32 rows) and walks 64-key
-//    tiles of the cache: every key tile for retrieval heads up to the diagonal; only
-//    the sink tile(s) and the window tiles for local heads (tiles outside the mask are
-//    never loaded).  Blocks are ordered heaviest first (retrieval heads, last rows).
+//  - a block has 4 waves of 32 query rows: gcd(G, 4) query heads of one KV head (grouped-
+//    query attention: they read the same keys) times 4 / gcd(G, 4) row slices, so one K/V
+//    tile copied to LDS serves up to four heads.  It walks 64-key tiles of the cache:
+//    every key tile for retrieval heads up to the diagonal; only the sink tile(s) and
+//    the window tiles for local heads (tiles outside the mask are never loaded).  Blocks
+//    are ordered heaviest first (retrieval heads, last rows).
 //  - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K tile from LDS, Q^T held in registers
 //    for the whole loop); the accumulator layout of S^T is exactly the B operand of
 //    O^T = V^T P^T, so P never goes through LDS.
@@ -27,6 +29,7 @@
 //    loop runs two tiles per trip so that LDS buffer indices are constants and the two
 //    S accumulator sets swap roles without register copies.
 #include <cmath>
+#include <numeric>
 #include <type_traits>
 
 #include "rtp_internal.hpp"
@@ -49,7 +52,7 @@ constexpr int PD = 128;               // head dim
 constexpr int RB = 1;                 // 32-row column blocks per wave
 constexpr int NW = RTP_PREFILL_NW;    // waves per block
 constexpr int kOpAhead = 2;           // LDS operand reads in flight ahead of their MFMA
-constexpr int BM = 32 * RB * NW;      // query rows per block
+constexpr int WR = 32 * RB;           // query rows per wave
 constexpr int BN = 64;                // keys per tile
 // LDS tiles are 64 rows x 128 bf16 (256-byte rows, 16 chunks of 16 bytes), unpadded
 // (direct-to-LDS loads fill 1 KB contiguous runs), with the chunk index XOR-swizzled per
@@ -100,8 +103,11 @@ struct PrefArgs {
   int64_t n_cap;
   int n_sinks, window;
   float scale_log2;
-  int nmb;                  // row blocks per head
-  int n_ret_q, n_loc_q;     // retrieval / local query heads
+  int gb;                   // query heads per block (of one KV head): gcd(G, NW)
+  int ngrp;                 // G / gb head groups per KV head
+  int rows;                 // query rows per block: WR * NW / gb
+  int nmb;                  // row blocks per chunk
+  int n_ret, n_loc;         // retrieval / local KV heads
   HeadMap ret, loc;         // rank -> KV head
 };
 
@@ -118,26 +124,30 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  // ---- which head / row block (heaviest first)
+  // ---- which KV head / head group / row block (heaviest first).  The block's waves are
+  // gb query heads of one KV head x NW/gb row slices, so every K/V tile copied to LDS
+  // serves gb heads.
   int idx = blockIdx.x;
   bool retr;
-  int qh;                     // global query head
-  int mb;
-  if (idx < a.n_ret_q * a.nmb) {
+  int kvh, grp, mb;
+  if (idx < a.n_ret * a.ngrp * a.nmb) {
     retr = true;
-    const int i = idx % a.n_ret_q;
-    mb = a.nmb - 1 - idx / a.n_ret_q;
-    qh = a.ret.kv[i / a.G] * a.G + i % a.G;
+    const int per = a.n_ret * a.ngrp, i = idx % per;
+    mb = a.nmb - 1 - idx / per;
+    kvh = a.ret.kv[i / a.ngrp];
+    grp = i % a.ngrp;
   } else {
-    idx -= a.n_ret_q * a.nmb;
+    idx -= a.n_ret * a.ngrp * a.nmb;
     retr = false;
-    const int i = idx % a.n_loc_q;
-    mb = a.nmb - 1 - idx / a.n_loc_q;
-    qh = a.loc.kv[i / a.G] * a.G + i % a.G;
+    const int per = a.n_loc * a.ngrp, i = idx % per;
+    mb = a.nmb - 1 - idx / per;
+    kvh = a.loc.kv[i / a.ngrp];
+    grp = i % a.ngrp;
   }
-  const int kvh = qh / a.G;
-  const int64_t R0 = a.c0 + int64_t(mb) * BM;                  // first row of the block
-  const int64_t Rend = min<int64_t>(R0 + BM, a.c0 + a.C);      // one past the last valid row
+  const int qh = kvh * a.G + grp * a.gb + wave % a.gb;         // this wave's query head
+  const int rslice = wave / a.gb;                              // this wave's row slice
+  const int64_t R0 = a.c0 + int64_t(mb) * a.rows;              // first row of the block
+  const int64_t Rend = min<int64_t>(R0 + a.rows, a.c0 + a.C);  // one past the last valid row
   const int64_t Rl = Rend - 1;                                 // last valid row
 
   // ---- key tiles this block visits
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
   bf16x8_t qop[RB][PD / 16];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    my_row[rb] = R0 + wave * (32 * RB) + rb * 32 + l32;
+    my_row[rb] = R0 + rslice * WR + rb * 32 + l32;
     const int64_t qrow_c = min<int64_t>(my_row[rb] - a.c0, a.C - 1);   // chunk-relative, clamped
 #pragma unroll
     for (int ds = 0; ds < PD / 16; ++ds)
@@ -597,11 +607,14 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
   a.n_sinks = L.n_sinks;
   a.window = L.window;
   a.scale_log2 = sm_scale * kLog2e;
-  a.nmb = (C + BM - 1) / BM;
-  a.n_ret_q = L.n_ret * L.G;
-  a.n_loc_q = L.n_loc * L.G;
+  a.gb = std::gcd(L.G, NW);
+  a.ngrp = L.G / a.gb;
+  a.rows = WR * NW / a.gb;
+  a.nmb = (C + a.rows - 1) / a.rows;
+  a.n_ret = L.n_ret;
+  a.n_loc = L.n_loc;
   a.ret = ret_map(L);
   a.loc = loc_map(L);
-  hipLaunchKernelGGL(k_prefill_attn, dim3(a.nmb * L.Hq), dim3(kPreThreads), 0, s, a);
+  hipLaunchKernelGGL(k_prefill_attn, dim3(a.nmb * L.Hkv * a.ngrp), dim3(kPreThreads), 0, s, a);
   return check_launch("k_prefill_attn");
 }

@@ -118,6 +118,28 @@ def test_prefill_small_all_rows(over):
     _check_kidx(cfg, pi, kp, kidx)
 
 
+@pytest.mark.parametrize("hq,hkv,retr", [
+    (8, 8, (0, 3)),        # one query head per KV head: a block takes 4 row slices of one head
+    (16, 8, (1, 6)),       # two per KV head: 2 heads x 2 row slices
+    (64, 8, (0, 3)),       # eight per KV head: two head groups of 4 per KV head
+])
+def test_prefill_query_group_sizes(hq, hkv, retr):
+    P.require_gpu()
+    cfg = W.scaled_prefill(W.CONFIGS["prefill_32k"], seq_len=700, chunk=256, window=100, n_sinks=4,
+                           rows_per_head=4, n_q_heads=hq, n_kv_heads=hkv, retrieval_kv=retr)
+    pi = W.PrefillInputs(cfg)
+    k, v, kp = pi.full_kv()
+    out, kidx = _run_prefill(cfg, pi, k, v, kp)
+    G = cfg.group
+    for h in sorted({0, 1, G - 1, G, hq // 2 + 1, hq - 1} & set(range(hq))):
+        g = h // G
+        rows = np.arange(cfg.seq_len)
+        q_rows = np.concatenate([pi.q_chunk(c, heads=[h])[:, h] for c in range(cfg.n_chunks)])
+        ref = O.prefill_rows(q_rows, rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
+        P.check_outputs(out[:, h], ref, f"head {h} (G={G})")
+    _check_kidx(cfg, pi, kp, kidx)
+
+
 def test_prefill_32k_sampled_rows():
     P.require_gpu()
     cfg = W.CONFIGS["prefill_32k"]
