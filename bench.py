@@ -565,7 +565,7 @@ def main():
         rooflines["prefill_attn"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                                      "traffic": measured_traffic("prefill_attn"),
-                                     "kernel": "rtp_prefill_attn (k_kidx_proj + k_prefill_attn)",
+                                     "kernel": "rtp_prefill_attn (k_prefill_attn: attention blocks + indexer-key projection blocks)",
                                      "ms_per_chunk": round(pre_ms / pre.cfg.n_chunks, 4)}
     # the dominant kernel of the step is the one that takes the most time
     if rooflines:

@@ -109,9 +109,66 @@ struct PrefArgs {
   int nmb;                  // row blocks per chunk
   int n_ret, n_loc;         // retrieval / local KV heads
   HeadMap ret, loc;         // rank -> KV head
+  int n_attn;               // attention blocks; the blocks after them project indexer keys
+  int n_px;                 // projection blocks per retrieval KV head (64 tokens each)
+  int Hkv, idx;             // KV heads, indexer dim
+  const uint16_t* k_pre;    // [C][Hkv][D] pre-RoPE keys of the chunk
+  const uint16_t* w_k;      // [Hkv_r][D][idx] (head stride w_stride)
+  int64_t w_stride;
+  uint16_t* k_idx;          // [Hkv_r][n_cap][idx]
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+
+// Indexer keys of the chunk: k_idx[r][c0 + t][:] = bf16(k_pre[t][g(r)][:] . W_k_idx[r]).
+// One wave per 16 tokens on v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of
+// k_pre (one 16-byte load per lane and step), B = W^T staged in LDS, one 16-column
+// block per 16 indexer outputs (dims 4 and 8 use one block, zero-padded).
+// These blocks run as the last blocks of the attention grid (block x of 64 tokens, retrieval
+// rank r), in the attention's tail; `lds` is the block's K tile buffer, free in such blocks.
+template <int IDX>
+__device__ __forceinline__ void kidx_proj_block(const PrefArgs& a, int bx, int r, uint16_t* lds) {
+  constexpr int NCB = IDX > 16 ? IDX / 16 : 1;                  // 16-column output blocks
+  const uint16_t* __restrict__ k_pre = a.k_pre;
+  const uint16_t* __restrict__ w_k = a.w_k;
+  uint16_t* __restrict__ k_idx = a.k_idx;
+  const int C = a.C, Hkv = a.Hkv;
+  const int64_t c0 = a.c0, n_cap = a.n_cap, w_stride = a.w_stride;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = a.ret.kv[r];
+  typedef uint16_t wrow_t[PD + 8];
+  wrow_t* s_wt = reinterpret_cast<wrow_t*>(lds);                // W^T: [out][d], 16 * NCB rows
+  for (int i = tid; i < PD * 16 * NCB; i += 256) {
+    const int d = i / (16 * NCB), c = i % (16 * NCB);
+    s_wt[c][d] = c < IDX ? w_k[int64_t(r) * w_stride + d * IDX + c] : uint16_t(0);
+  }
+  __syncthreads();
+  const int t0 = (bx * 4 + wave) * 16;                         // first token of this wave
+  const int row = lane & 15, kq = lane >> 4;
+  const int tok = min(t0 + row, C - 1);
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int st = 0; st < PD / 32; ++st) {
+    const uint4 av = *reinterpret_cast<const uint4*>(k_pre + (int64_t(tok) * Hkv + g) * PD + 32 * st + 8 * kq);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint4 bv = *reinterpret_cast<const uint4*>(&s_wt[cb * 16 + row][32 * st + 8 * kq]);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[cb], 0, 0, 0);
+    }
+  }
+  // D (16 x 16): lane holds output column (lane & 15), token rows 4*(lane>>4) + v
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + 4 * kq + v, col = cb * 16 + row;
+      if (t < C && col < IDX) k_idx[(int64_t(r) * n_cap + c0 + t) * IDX + col] = f32_to_bf16(acc[cb][v]);
+    }
+}
+
 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -123,6 +180,19 @@ typedef __attribute__((address_space(3))) short4_t* lds_s4;
 __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hf = lane >> 5;
+  __shared__ uint16_t s_k[2][BN * KP];
+  __shared__ uint16_t s_v[2][BN * KP];
+
+  if (blockIdx.x >= a.n_attn) {               // indexer-key projection block
+    const int pb = blockIdx.x - a.n_attn, bx = pb % a.n_px, r = pb / a.n_px;
+    switch (a.idx) {
+      case 4: kidx_proj_block<4>(a, bx, r, s_k[0]); break;
+      case 8: kidx_proj_block<8>(a, bx, r, s_k[0]); break;
+      case 16: kidx_proj_block<16>(a, bx, r, s_k[0]); break;
+      default: kidx_proj_block<32>(a, bx, r, s_k[0]); break;
+    }
+    return;
+  }
 
   // ---- which KV head / head group / row block (heaviest first).  The block's waves are
   // gb query heads of one KV head x NW/gb row slices, so every K/V tile copied to LDS
@@ -161,9 +231,6 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
   }
   const int n_tiles = n_sink_t + (kt_last - kt_start + 1);
   auto tile_of = [&](int n) { return n < n_sink_t ? n : kt_start + (n - n_sink_t); };
-
-  __shared__ uint16_t s_k[2][BN * KP];
-  __shared__ uint16_t s_v[2][BN * KP];
 
   const uint16_t* kbase = a.k + int64_t(kvh) * a.n_cap * PD;
   const uint16_t* vbase = a.v + int64_t(kvh) * a.n_cap * PD;
@@ -498,50 +565,6 @@ __global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a
   }
 }
 
-// Indexer keys of the chunk: k_idx[r][c0 + t][:] = bf16(k_pre[t][g(r)][:] . W_k_idx[r]).
-// One wave per 16 tokens on v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of
-// k_pre (one 16-byte load per lane and step), B = W^T staged in LDS, one 16-column
-// block per 16 indexer outputs (dims 4 and 8 use one block, zero-padded).
-template <int IDX>
-__global__ __launch_bounds__(256) void k_kidx_proj(const uint16_t* __restrict__ k_pre,
-                                                   const uint16_t* __restrict__ w_k, int64_t w_stride,
-                                                   uint16_t* __restrict__ k_idx, int64_t c0, int C, int Hkv,
-                                                   int64_t n_cap, HeadMap ret) {
-  constexpr int NCB = IDX > 16 ? IDX / 16 : 1;                  // 16-column output blocks
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = blockIdx.y;
-  const int g = ret.kv[r];
-  __shared__ uint16_t s_wt[16 * NCB][PD + 8];                   // W^T: [out][d]
-  for (int i = tid; i < PD * 16 * NCB; i += 256) {
-    const int d = i / (16 * NCB), c = i % (16 * NCB);
-    s_wt[c][d] = c < IDX ? w_k[int64_t(r) * w_stride + d * IDX + c] : uint16_t(0);
-  }
-  __syncthreads();
-  const int t0 = (blockIdx.x * 4 + wave) * 16;                 // first token of this wave
-  const int row = lane & 15, kq = lane >> 4;
-  const int tok = min(t0 + row, C - 1);
-  f32x4 acc[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int st = 0; st < PD / 32; ++st) {
-    const uint4 av = *reinterpret_cast<const uint4*>(k_pre + (int64_t(tok) * Hkv + g) * PD + 32 * st + 8 * kq);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const uint4 bv = *reinterpret_cast<const uint4*>(&s_wt[cb * 16 + row][32 * st + 8 * kq]);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[cb], 0, 0, 0);
-    }
-  }
-  // D (16 x 16): lane holds output column (lane & 15), token rows 4*(lane>>4) + v
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = t0 + 4 * kq + v, col = cb * 16 + row;
-      if (t < C && col < IDX) k_idx[(int64_t(r) * n_cap + c0 + t) * IDX + col] = f32_to_bf16(acc[cb][v]);
-    }
-}
-
 }  // namespace
 
 namespace rtp {
@@ -579,21 +602,6 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
       (k_pre && !aligned(k_pre, 16)) || (k_idx_cache && !aligned(k_idx_cache, 2)))
     return fail(RTP_EINVAL, "rtp_prefill_attn: tensors must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (L.n_ret > 0) {
-    const dim3 pg((C + 63) / 64, L.n_ret);
-    const HeadMap rm = ret_map(L);
-    switch (L.idx) {
-      case 4: hipLaunchKernelGGL(k_kidx_proj<4>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache, c0,
-                                 C, L.Hkv, L.n_cap, rm); break;
-      case 8: hipLaunchKernelGGL(k_kidx_proj<8>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache, c0,
-                                 C, L.Hkv, L.n_cap, rm); break;
-      case 16: hipLaunchKernelGGL(k_kidx_proj<16>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache,
-                                  c0, C, L.Hkv, L.n_cap, rm); break;
-      default: hipLaunchKernelGGL(k_kidx_proj<32>, pg, dim3(256), 0, s, k_pre, w_k_idx, w_head_stride, k_idx_cache,
-                                  c0, C, L.Hkv, L.n_cap, rm); break;
-    }
-    if ((st = check_launch("k_kidx_proj")) != RTP_OK) return st;
-  }
   PrefArgs a{};
   a.q = q;
   a.k = k_cache;
@@ -615,6 +623,15 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
   a.n_loc = L.n_loc;
   a.ret = ret_map(L);
   a.loc = loc_map(L);
-  hipLaunchKernelGGL(k_prefill_attn, dim3(a.nmb * L.Hkv * a.ngrp), dim3(kPreThreads), 0, s, a);
+  a.n_attn = a.nmb * L.Hkv * a.ngrp;
+  a.n_px = (C + 63) / 64;
+  a.Hkv = L.Hkv;
+  a.idx = L.idx;
+  a.k_pre = k_pre;
+  a.w_k = w_k_idx;
+  a.w_stride = w_head_stride;
+  a.k_idx = k_idx_cache;
+  const int n_proj = L.n_ret > 0 ? a.n_px * L.n_ret : 0;
+  hipLaunchKernelGGL(k_prefill_attn, dim3(a.n_attn + n_proj), dim3(kPreThreads), 0, s, a);
   return check_launch("k_prefill_attn");
 }
