@@ -97,6 +97,25 @@ def check_set(gpu_sel: np.ndarray, info: Dict[str, np.ndarray], p: float, scores
     return False, int(diff.size)
 
 
+def check_prefix(gpu_sel: np.ndarray, scores32: np.ndarray, what: str = ""):
+    """The selected set must be the first |S| tokens of the (score descending, index ascending)
+    order of the very fp32 scores the kernel ranked (-0 and +0 tie).  The mass arithmetic only
+    decides |S|; which tokens fill it, ties included, is exact integer/fp32 comparison work,
+    so this holds bit for bit wherever the mass boundary falls."""
+    sel = np.asarray(gpu_sel, np.int64)
+    if sel.size == 0:
+        return
+    s = np.asarray(scores32, np.float32) + np.float32(0.0)
+    t = s[sel].min()
+    above = np.flatnonzero(s > t)
+    tied = np.flatnonzero(s == t)
+    n_t = sel.size - above.size
+    assert 1 <= n_t <= tied.size, f"{what}: the set is not a prefix of the score order"
+    want = np.sort(np.concatenate([above, tied[:n_t]]))
+    assert np.array_equal(sel, want), f"{what}: the set is not the first {sel.size} tokens of the score order " \
+        f"(ties are taken lowest index first)"
+
+
 class DeviceDecode:
     """Generator inputs of one decode configuration, resident on the GPU."""
 

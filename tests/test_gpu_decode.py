@@ -146,6 +146,7 @@ def _check_rows(scores32, sets, p):
         s64 = scores32[r].astype(np.float64)
         _, info = O.topp_select(s64, p)
         same, _ = P.check_set(sets[r], info, p)
+        P.check_prefix(sets[r], scores32[r], f"row {r}")
         ident += same
     return ident
 
@@ -362,10 +363,12 @@ def test_decode_step_end_to_end(name, p):
     g = rtp.from_device_bf16(out).reshape(B, cfg.n_q_heads, cfg.head_dim)
     cnt = step.sel_count.view(B, R).cpu().numpy()
     sel = step.sel_idx.view(B, R, N).cpu().numpy()
+    gsc = step.scores.view(B, R, -1)[:, :, :N].cpu().numpy()
     identical, sizes = [], []
     for b in range(B):
         for ci in range(R):
             r = ci // G
+            P.check_prefix(sel[b, ci, :cnt[b, ci]], gsc[b, ci], f"row ({b},{ci})")   # on the kernel's own scores
             scale = P.score_scale(x, b, ci, r, N)
             same, _ = P.check_set(sel[b, ci, :cnt[b, ci]], ora["info"][(b, ci)], p, ora["scores"][(b, ci)],
                                   P.FP32_SCORE_SLACK * scale)

@@ -96,6 +96,7 @@ def _check_kidx(cfg, pi, kp, kidx):
     dict(seq_len=640, chunk=192, window=1, n_sinks=0),            # query token only
     dict(seq_len=600, chunk=128, window=70, n_sinks=0),           # no sinks: first rows see few keys
     dict(seq_len=900, chunk=300, window=130, n_sinks=77),         # sinks span two key tiles
+    dict(seq_len=150, chunk=17, window=40, n_sinks=3),            # chunks shorter than one 32-row block
     dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=4),   # indexer dims of the ablation
     dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=8),
     dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=32),
