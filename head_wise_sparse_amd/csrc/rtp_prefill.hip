@@ -23,11 +23,14 @@
 //    (no registers; one scalar base plus a fixed per-lane offset per copy) while the
 //    current tile is computed, and V^T operands are read with the transposing LDS read
 //    (ds_read_b64_tr_b16), so V needs no explicit transpose.
-//  - per tile, the rare branches (boundary mask, reference-max move) come first; the
-//    next tile's QK^T, this tile's exponentials and its PV product then form one
-//    straight-line block that the compiler interleaves on the MFMA and VALU pipes.  The
-//    loop runs two tiles per trip so that LDS buffer indices are constants and the two
-//    S accumulator sets swap roles without register copies.
+//  - per tile, the rare branches (boundary mask, reference-max move) come first; the rest
+//    is 32 MFMA slots pinned in order by scheduling barriers: the next tile's QK^T, each
+//    slot carrying one pair of this tile's exponentials, then this tile's PV product,
+//    carrying the next tile's row max.  The loop runs two tiles per trip so that LDS
+//    buffer indices are constants and the two S accumulator sets swap roles without
+//    register copies.
+//  - the indexer-key projection runs as the last blocks of the same grid (64 tokens x one
+//    retrieval KV head each), so it fills the attention's tail instead of a launch.
 #include <cmath>
 #include <numeric>
 #include <type_traits>
