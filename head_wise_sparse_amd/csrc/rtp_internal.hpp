@@ -116,8 +116,9 @@ rtp_status launch_select(const SelArgs& a, int rows, hipStream_t s);
 // Decode attention (sparse and window share the layout).
 constexpr int kDecThreads = 256;
 constexpr int kDecRange = RTP_SEL_RANGE; // token-index range per block (sparse path)
-constexpr int kWinRange = 256;           // list positions per block (window path) ...
-constexpr int kWinRangeShort = 128;      // ... or half that when the launch then still fits one round
+constexpr int kWinRange = 256;           // list positions per block (window path) when no slice fits ...
+constexpr int kWinRangeShort = 128;      // ... else the shortest multiple of 32 from 128 ...
+constexpr int kWinRangeMax = 512;        // ... to 512 with which the launch fits one round
 constexpr int kDecUnroll = 2;            // cached rows per pipeline stage per lane group (2 stages)
 // Sparse path: blocks per index range (each takes one slice of the range's union list),
 // chosen per call so that the grid is about one round of resident blocks
@@ -128,10 +129,13 @@ inline int dec_sub(int nsplit, int groups) {
   return n < 1 ? 1 : (n > kDecSubMax ? kDecSubMax : n);
 }
 // window slice length for `len` list positions and `groups` (batch x local KV heads),
-// sharing a launch with `other` blocks
+// sharing a launch with `other` blocks: a block walks its slice as a chain of dependent
+// loads, so the shortest slice wins as long as every block still starts in the first
+// round of resident blocks
 inline int win_range(int64_t len, int groups, int other) {
-  const int64_t n_short = (len + kWinRangeShort - 1) / kWinRangeShort * groups;
-  return other + n_short <= kDecBlocksTarget ? kWinRangeShort : kWinRange;
+  for (int wr = kWinRangeShort; wr <= kWinRangeMax; wr += 32)
+    if (other + (len + wr - 1) / wr * groups <= kDecBlocksTarget) return wr;
+  return kWinRange;
 }
 size_t dec_ws_bytes(const Layer& L, int64_t n_ctx, bool sparse);   // partials [rows][slots][D + 4]
 // window slice length of a call (the same for the separate call and the fused step, which
