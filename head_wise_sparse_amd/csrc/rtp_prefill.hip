@@ -49,11 +49,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int PD = 128;               // head dim
-#ifndef RTP_PREFILL_NW
-#define RTP_PREFILL_NW 4
-#endif
 constexpr int RB = 1;                 // 32-row column blocks per wave
-constexpr int NW = RTP_PREFILL_NW;    // waves per block
+constexpr int NW = 4;                 // waves per block (two blocks per CU)
 constexpr int kOpAhead = 2;           // LDS operand reads in flight ahead of their MFMA
 constexpr int WR = 32 * RB;           // query rows per wave
 constexpr int BN = 64;                // keys per tile
@@ -180,7 +177,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t* lds_s4;
 
-__global__ __launch_bounds__(kPreThreads, 8 / NW) void k_prefill_attn(PrefArgs a) {
+__global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hf = lane >> 5;
   __shared__ uint16_t s_k[2][BN * KP];
