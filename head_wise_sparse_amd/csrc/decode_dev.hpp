@@ -128,7 +128,9 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
         // compiler keeps every load in flight instead of waiting inside a branch
         const int k = lo[t] + u * kDecThreads + tid;
         const int v = sr[k < hi[t] ? k : 0];
-        pos[t][u] = (k < hi[t]) ? v - j0 : -1;
+        // an index outside [0, n_ctx) (a malformed list from the caller) is dropped, so no
+        // cache row at or past n_ctx is ever read
+        pos[t][u] = (k < hi[t] && v >= 0 && v < a.n_ctx) ? v - j0 : -1;
       }
     }
 #pragma unroll

@@ -312,18 +312,20 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
   // Tile copies.  Wave w's i-th copy fills physical chunks (NW*i + w)*64 .. +63 of the
   // tile, i.e. rows 4*NW*i + crow (crow = 4w + lane/16); the swizzled chunk a lane fetches
   // does not depend on i, so a copy is one scalar base (the tile's first row, + NW KB per
-  // i) plus a fixed per-lane byte offset.  Only a tile that runs past the cache's last row
-  // takes the clamped path (its rows beyond n_cap - 1 repeat the last row; their scores
-  // are masked).
+  // i) plus a fixed per-lane byte offset.  Only a tile that runs past the chunk's last row
+  // (rows from c0 + C on need not hold valid data yet) takes the clamped path: its rows
+  // from there on repeat the last valid row, so they are finite; their scores are masked
+  // and their probabilities are exactly 0.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int crow = 4 * wave + (lane >> 4);
   const uint32_t koff = uint32_t(crow * PD + (((lane & 15) ^ (crow & 15)) << 3)) * 2u;
   const uint32_t voff = uint32_t(crow * PD + (((lane & 15) ^ ((crow & 3) << 2)) << 3)) * 2u;
   static_assert(KLD * NWV * 64 == KCH && NWV == NW, "copy layout");
+  const int64_t kv_end = a.c0 + a.C;          // cache rows below this are valid (<= n_cap)
   auto copy_tile = [&](const uint16_t* base, int kt, uint32_t off, uint16_t* lds_tile, bool is_k) {
     const int64_t k0 = int64_t(kt) * BN;
     const uint32_t lds0 = lds_addr(lds_tile) + uint32_t(wave_u) * 1024u;
-    if (k0 + BN <= a.n_cap) {
+    if (k0 + BN <= kv_end) {
       const char* g0 = reinterpret_cast<const char*>(base + k0 * PD);
 #pragma unroll
       for (int i = 0; i < KLD; ++i) g2lds_16s(g0 + 1024 * NW * i, off, lds0 + 1024u * NW * i);
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
       for (int i = 0; i < KLD; ++i) {
         const int row = 4 * NW * i + crow;
         const int c = is_k ? ((lane & 15) ^ (crow & 15)) : ((lane & 15) ^ ((crow & 3) << 2));
-        const int64_t kr = min<int64_t>(k0 + row, a.n_cap - 1);
+        const int64_t kr = min<int64_t>(k0 + row, kv_end - 1);
         g2lds_16(base + kr * PD + c * 8, lds0 + 1024u * NW * i);
       }
     }

@@ -191,7 +191,9 @@ rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx, const floa
  *
  *   q        bf16 [B][Hq][D]  post-RoPE queries
  *   k_cache, v_cache bf16 [B][Hkv][n_cap][D]
- *   sel_idx, sel_count  as written by rtp_topp_select (indices < n_ctx, increasing)
+ *   sel_idx, sel_count  as written by rtp_topp_select (indices < n_ctx, increasing);
+ *            an entry outside [0, n_ctx) is ignored, so no cache row at or past n_ctx
+ *            is read whatever the lists hold
  *   sel_starts  the range index rtp_topp_select wrote for the same sets, or NULL
  *            (then it is rebuilt from sel_idx in the workspace)
  *   out      bf16 [B][Hq][D]; only retrieval heads' rows are written.  A row

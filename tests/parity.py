@@ -59,6 +59,7 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 def check_outputs(gpu_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     g = O.bf16_to_f64(gpu_bits).reshape(ref.shape)
+    assert np.isfinite(g).all(), f"{what}: {int((~np.isfinite(g)).sum())} non-finite outputs"
     err = np.abs(g - ref)
     allow = OUT_ATOL + 0.5 * bf16_ulp(ref)
     bad = err > allow

@@ -265,6 +265,35 @@ def test_sparse_decode_on_oracle_sets(name, over):
     assert np.all(g[:, loc] == 0), "local-head rows must not be written"
 
 
+def test_sparse_decode_ignores_indices_past_the_context():
+    """Lists holding entries at or past n_ctx (a malformed caller list) make the call read no
+    cache row there: the result is bit-identical to that of the clean lists.  The cache holds
+    exactly n_ctx rows and the last index range runs past them."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=2, n_ctx=5000)
+    cfg = x.cfg
+    N, B, G = cfg.n_ctx, cfg.batch, cfg.group
+    R = cfg.n_kv_r * G
+    L = P.layer_for(cfg)
+    rng = np.random.default_rng(3)
+    clean, bogus = {}, {}
+    for b in range(B):
+        for ci in range(R):
+            s_ = np.unique(np.concatenate([rng.choice(N, 300, replace=False), [N - 1]]))
+            clean[(b, ci)] = s_
+            bogus[(b, ci)] = np.concatenate([s_, [N, N + 50, 5119]]) if (b + ci) % 2 == 0 else s_
+    outs = []
+    for sets in (clean, bogus):
+        sel, cnt = _sel_tensors(sets, B, R, N)
+        out = torch.zeros(B * cfg.n_q_heads * cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+        rtp.rtp_sparse_decode_attn(L, N, d.q, d.k, d.v, sel, cnt, None, 1 / math.sqrt(cfg.head_dim), out,
+                                   rtp.workspace(L, N, rtp.CALL_SPARSE_DECODE))
+        torch.cuda.synchronize()
+        outs.append(rtp.from_device_bf16(out))
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_sparse_decode_special_sets():
     """Empty set -> zeros; one token -> that V row; every token -> dense attention;
     overlapping random sets inside a GQA group."""

@@ -141,6 +141,43 @@ def test_prefill_query_group_sizes(hq, hkv, retr):
     _check_kidx(cfg, pi, kp, kidx)
 
 
+@pytest.mark.parametrize("retr", [(0, 3), (0, 1, 2, 3, 4, 5, 6, 7)])
+def test_prefill_ignores_rows_past_the_chunk(retr):
+    """Cache rows at or past c0 + C are not valid yet (the contract): fill them with NaN and
+    the chunk's outputs must still match the oracle (a key tile that crosses the chunk's end
+    must not let those rows into the sums, not even as 0 * NaN)."""
+    P.require_gpu()
+    import torch
+    cfg = W.scaled_prefill(W.CONFIGS["prefill_32k"], seq_len=700, chunk=300, window=100, n_sinks=4,
+                           rows_per_head=4, retrieval_kv=retr)
+    pi = W.PrefillInputs(cfg)
+    k, v, kp = pi.full_kv()
+    T, Hq, D, G = cfg.seq_len, cfg.n_q_heads, cfg.head_dim, cfg.group
+    L = rtp.Layer(1, Hq, cfg.n_kv_heads, D, T, cfg.kv_role.tolist(), cfg.n_sinks, cfg.window, idx_dim=cfg.idx_dim)
+    I = cfg.idx_dim
+    w = P.dev(pi.w_k_idx)
+    kidx = torch.zeros(cfg.n_kv_r * T * I, dtype=torch.bfloat16, device="cuda")
+    ws = rtp.workspace(L, cfg.chunk, rtp.CALL_PREFILL)
+    nan = np.uint16(0x7FC0)
+    for c in range(cfg.n_chunks):
+        c0, c1 = pi.chunk_bounds(c)
+        kn, vn = k.copy(), v.copy()
+        kn[:, c1:] = nan
+        vn[:, c1:] = nan
+        q = P.dev(pi.q_chunk(c))
+        o = torch.empty((c1 - c0) * Hq * D, dtype=torch.bfloat16, device="cuda")
+        rtp.rtp_prefill_attn(L, c0, c1 - c0, q, P.dev(kn), P.dev(vn), P.dev(kp[c0:c1]), w, D * I, kidx,
+                             1 / math.sqrt(D), o, ws)
+        torch.cuda.synchronize()
+        ob = rtp.from_device_bf16(o).reshape(c1 - c0, Hq, D)
+        for h in (0, 1, G, Hq - 1):
+            g = h // G
+            rows = np.arange(c0, c1)
+            ref = O.prefill_rows(pi.q_chunk(c, heads=[h])[:, h], rows, k[g], v[g], bool(cfg.kv_role[g]),
+                                 cfg.n_sinks, cfg.window)
+            P.check_outputs(ob[:, h], ref, f"chunk {c} head {h}")
+
+
 def test_prefill_32k_sampled_rows():
     P.require_gpu()
     cfg = W.CONFIGS["prefill_32k"]
