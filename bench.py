@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0
 # changes the figure no longer describes the kernel and `traffic` is reported as null.
 COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
 MEASURED_KIB = {
-    "prefill_attn": {"src": ("rtp_prefill.hip", "3348dd74dd941082"),
-                     "fetch": 211555.2, "write": 41325.4},
-    "sparse_decode": {"src": ("decode_dev.hpp", "a902b732dd649f6d"),
-                      "fetch": 172605.7 + 1086.5, "write": 2176.2 + 8.0},
+    "prefill_attn": {"src": ("rtp_prefill.hip", "a6a49f69ede1f05d"),
+                     "fetch": 211534.9, "write": 41345.1},
+    "sparse_decode": {"src": ("decode_dev.hpp", "1d2d2b66f5ec8523"),
+                      "fetch": 172604.6 + 1086.5, "write": 2176.2 + 8.0},
 }
 
 
