@@ -97,6 +97,7 @@ def _check_kidx(cfg, pi, kp, kidx):
     dict(seq_len=600, chunk=128, window=70, n_sinks=0),           # no sinks: first rows see few keys
     dict(seq_len=900, chunk=300, window=130, n_sinks=77),         # sinks span two key tiles
     dict(seq_len=150, chunk=17, window=40, n_sinks=3),            # chunks shorter than one 32-row block
+    dict(seq_len=40, chunk=1, window=9, n_sinks=2),               # one row per chunk
     dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=4),   # indexer dims of the ablation
     dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=8),
     dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=32),
@@ -174,6 +175,29 @@ def test_prefill_ignores_rows_past_the_chunk(retr):
             g = h // G
             rows = np.arange(c0, c1)
             ref = O.prefill_rows(pi.q_chunk(c, heads=[h])[:, h], rows, k[g], v[g], bool(cfg.kv_role[g]),
+                                 cfg.n_sinks, cfg.window)
+            P.check_outputs(ob[:, h], ref, f"chunk {c} head {h}")
+
+
+def test_prefill_all_local_heads():
+    """No retrieval head: no indexer-key work, the indexer pointers may be NULL."""
+    P.require_gpu()
+    import torch
+    cfg = W.scaled_prefill(W.CONFIGS["prefill_32k"], seq_len=600, chunk=256, window=70, n_sinks=5, rows_per_head=4)
+    pi = W.PrefillInputs(cfg)
+    k, v, _ = pi.full_kv()
+    T, Hq, D, G = cfg.seq_len, cfg.n_q_heads, cfg.head_dim, cfg.group
+    L = rtp.Layer(1, Hq, cfg.n_kv_heads, D, T, [0] * cfg.n_kv_heads, cfg.n_sinks, cfg.window, idx_dim=cfg.idx_dim)
+    ws = rtp.workspace(L, cfg.chunk, rtp.CALL_PREFILL)
+    kd, vd = P.dev(k), P.dev(v)
+    for c in range(cfg.n_chunks):
+        c0, c1 = pi.chunk_bounds(c)
+        o = torch.empty((c1 - c0) * Hq * D, dtype=torch.bfloat16, device="cuda")
+        rtp.rtp_prefill_attn(L, c0, c1 - c0, P.dev(pi.q_chunk(c)), kd, vd, None, None, 0, None, 1 / math.sqrt(D), o, ws)
+        torch.cuda.synchronize()
+        ob = rtp.from_device_bf16(o).reshape(c1 - c0, Hq, D)
+        for h in (0, G + 1, Hq - 1):
+            ref = O.prefill_rows(pi.q_chunk(c, heads=[h])[:, h], np.arange(c0, c1), k[h // G], v[h // G], False,
                                  cfg.n_sinks, cfg.window)
             P.check_outputs(ob[:, h], ref, f"chunk {c} head {h}")
 
