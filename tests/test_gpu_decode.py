@@ -413,6 +413,32 @@ def test_decode_step_end_to_end(name, p):
     assert sum(identical) >= 0.9 * len(identical)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_step_ignores_rows_past_the_context(fused):
+    """Cache rows at or past n_ctx (K, V and indexer keys) hold NaN: the step reads none of
+    them, so every output is bit-identical to the run on zero-filled rows."""
+    P.require_gpu()
+    torch = _torch()
+    cfg = W.scaled_decode(W.CONFIGS["decode_b8_32k"], batch=2, n_ctx=5000)
+    cap = 5000 + 700
+    x = W.make_decode_inputs(cfg, n_cap=cap)
+    L = P.layer_for(cfg, n_cap=cap)
+    B, R = cfg.batch, cfg.n_kv_r * cfg.group
+    res = []
+    for poison in (False, True):
+        if poison:
+            nan = np.uint16(0x7FC0)
+            x.k[:, :, cfg.n_ctx:] = nan
+            x.v[:, :, cfg.n_ctx:] = nan
+            x.k_idx[:, :, cfg.n_ctx:] = nan
+        d = P.DeviceDecode(x)
+        step = rtp.DecodeStep(L, cfg.n_ctx, cfg.top_p, fused=fused)
+        step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+        torch.cuda.synchronize()
+        res.append(_step_outputs(step, B, R, cfg.n_ctx))
+    _assert_same(res[0], res[1], "NaN past n_ctx")
+
+
 def test_decode_step_is_deterministic():
     P.require_gpu()
     torch = _torch()
