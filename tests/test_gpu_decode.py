@@ -439,6 +439,42 @@ def test_decode_step_ignores_rows_past_the_context(fused):
     _assert_same(res[0], res[1], "NaN past n_ctx")
 
 
+@pytest.mark.parametrize("head_dim,group", [(64, 1), (64, 2), (64, 4), (64, 8), (128, 1), (128, 2), (128, 8)])
+def test_decode_step_shapes(head_dim, group):
+    """Every (head_dim, group size) the decode kernels are built for: the fused step against
+    the oracle, and bit-identical to the separate calls."""
+    P.require_gpu()
+    torch = _torch()
+    over = dict(head_dim=head_dim, batch=2, n_ctx=6000, n_q_heads=8 * group)
+    x, d = _inputs("decode_b8_32k", **over)
+    cfg = x.cfg
+    N, B, G = cfg.n_ctx, cfg.batch, cfg.group
+    R = cfg.n_kv_r * G
+    L = P.layer_for(cfg)
+    res = []
+    for fused in (False, True):
+        step = rtp.DecodeStep(L, N, cfg.top_p, fused=fused)
+        step.run(d.q_pre, d.q, d.k, d.v, d.k_idx, d.w_q_idx)
+        torch.cuda.synchronize()
+        res.append(_step_outputs(step, B, R, N))
+    _assert_same(res[0], res[1], f"head_dim {head_dim}, G {group}")
+    ora = O.decode_step(x.q_pre, x.q, x.k, x.v, x.k_idx, x.w_q_idx, x.kv_role, N, cfg.top_p, cfg.n_sinks, cfg.window)
+    g = res[1]["out"].reshape(B, cfg.n_q_heads, cfg.head_dim)
+    same = 0
+    for b in range(B):
+        for ci in range(R):
+            r = ci // G
+            ok, _ = P.check_set(res[1]["sets"][b * R + ci], ora["info"][(b, ci)], cfg.top_p, ora["scores"][(b, ci)],
+                                P.FP32_SCORE_SLACK * P.score_scale(x, b, ci, r, N))
+            h = cfg.retrieval_kv[r] * G + ci % G
+            if ok:
+                P.check_outputs(g[b, h][None], ora["out"][b, h][None], f"retrieval row ({b},{h})")
+            same += ok
+    loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
+    P.check_outputs(g[:, loc], ora["out"][:, loc], "local rows")
+    assert same >= 0.9 * B * R
+
+
 def test_decode_step_is_deterministic():
     P.require_gpu()
     torch = _torch()
