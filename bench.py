@@ -562,6 +562,21 @@ def main():
         tflops = fl["total"] / (pre_ms * 1e-3) / 1e12
         res["prefill"] = {"ms": round(pre_ms, 3), "tflops": round(tflops, 1),
                           "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "flops": fl}
+        # the dense bf16 MFMA rate this chip sustains (4 independent 32x32x16 chains per
+        # wave, 2 waves per SIMD: its clock under an MFMA load), the ceiling the prefill's
+        # rate is read against; the roofline peak stays 2.5 PFLOP/s
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            rtp.rtp_mfma_probe(20000, sink)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        pfl = sum(rtp.rtp_mfma_probe(100000, sink) for _ in range(3))
+        b.record()
+        torch.cuda.synchronize()
+        probe_tf = pfl / (a.elapsed_time(b) * 1e-3) / 1e12
+        res["prefill"]["mfma_probe_TFLOPs"] = round(probe_tf, 1)
+        res["prefill"]["frac_of_mfma_probe"] = round(tflops / probe_tf, 4)
         rooflines["prefill_attn"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                                      "traffic": measured_traffic("prefill_attn"),

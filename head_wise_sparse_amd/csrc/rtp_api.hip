@@ -209,7 +209,48 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;      // keeps the loads; almost never stores
 }
+
+// Dense MFMA throughput: every wave runs 4 independent v_mfma_f32_32x32x16_bf16 chains
+// from register operands (2 waves per SIMD), the shape and dtype of the prefill's MFMAs.
+typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256, 2) void k_mfma_probe(uint32_t iters, float* __restrict__ sink) {
+  probe_f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+  probe_bf16x8 x, y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = (__bf16)(1e-3f * float(threadIdx.x + e));
+    y[e] = (__bf16)(1e-3f * float(e + 1));
+  }
+  for (uint32_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc[j], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[j][v];
+  if (s == 1.2345e-30f) sink[0] = s;          // keeps the work; almost never stores
+}
 }  // namespace
+
+extern "C" rtp_status rtp_mfma_probe(uint32_t iters, float* sink, double* flops, void* stream) {
+  if (!sink || !flops) return fail(RTP_EINVAL, "rtp_mfma_probe: NULL sink or flops");
+  if (iters < 1 || iters > (1u << 24)) return fail(RTP_EINVAL, "rtp_mfma_probe: iters must be in [1, 2^24]");
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      ncu < 1)
+    return fail(RTP_EDEVICE, "rtp_mfma_probe: cannot read the compute-unit count");
+  const int blocks = 2 * ncu;                   // 8 waves per CU: 2 per SIMD
+  *flops = double(blocks) * 4.0 * double(iters) * 4.0 * 32.0 * 32.0 * 16.0 * 2.0;
+  hipLaunchKernelGGL(k_mfma_probe, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), iters, sink);
+  return check_launch("k_mfma_probe");
+}
 
 extern "C" rtp_status rtp_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes < 16) return fail(RTP_EINVAL, "rtp_hbm_read_probe: NULL buffer or fewer than 16 bytes");

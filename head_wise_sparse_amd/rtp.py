@@ -25,7 +25,7 @@ KV_FULL, KV_COMPACT = 0, 1
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
             "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_append_token",
-            "rtp_hbm_read_probe", "rtp_status_string", "rtp_last_error", "rtp_version"]
+            "rtp_hbm_read_probe", "rtp_mfma_probe", "rtp_status_string", "rtp_last_error", "rtp_version"]
 
 
 class RtpError(RuntimeError):
@@ -70,6 +70,7 @@ def load() -> C.CDLL:
         "rtp_append_token": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, C.c_int64, _P, _P, _P, _P, _P, _P]),
         "rtp_topk_select": (C.c_int, [D, C.c_int64, _P, C.c_int64, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_hbm_read_probe": (C.c_int, [_P, C.c_size_t, _P, _P]),
+        "rtp_mfma_probe": (C.c_int, [C.c_uint32, _P, C.POINTER(C.c_double), _P]),
         "rtp_status_string": (C.c_char_p, [C.c_int]),
         "rtp_last_error": (C.c_char_p, []),
         "rtp_version": (C.c_char_p, []),
@@ -227,6 +228,13 @@ def rtp_append_token(layer: Layer, pos: int, k_new, v_new, k_pre, w_k_idx, w_hea
 
 def rtp_hbm_read_probe(buf, sink, stream=None):
     _check(load().rtp_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def rtp_mfma_probe(iters: int, sink, stream=None) -> float:
+    """Enqueue the MFMA throughput probe; returns the launch's flop count."""
+    fl = C.c_double(0.0)
+    _check(load().rtp_mfma_probe(int(iters), _ptr(sink), C.byref(fl), _stream(stream)))
+    return fl.value
 
 
 def rtp_version() -> str:

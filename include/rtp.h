@@ -311,6 +311,17 @@ rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos,
  */
 rtp_status rtp_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * rtp_mfma_probe -- diagnostic: every wave of 2 blocks per compute unit (2 waves per
+ * SIMD) runs `iters` trips of 4 independent v_mfma_f32_32x32x16_bf16 chains from
+ * register operands (the prefill's MFMA shape); *flops (HOST) receives the launch's
+ * flop count, sink is a device word that is almost never written.  Timing it gives
+ * the dense bf16 MFMA rate the chip sustains (its clock under such a load), the
+ * reference against which the prefill's MFMA rate is read; it is not part of the method.
+ * iters in [1, 2^24].
+ */
+rtp_status rtp_mfma_probe(uint32_t iters, float* sink, double* flops, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* rtp_status_string(rtp_status s);
 

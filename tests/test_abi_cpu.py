@@ -166,6 +166,15 @@ def test_call_validation():
                                 1 << 30, None) == rtp.RTP_EINVAL                # C >= 1
 
 
+def test_probe_validation():
+    lib = rtp.load()
+    fl = C.c_double(0.0)
+    assert lib.rtp_mfma_probe(10, None, C.byref(fl), None) == rtp.RTP_EINVAL
+    assert lib.rtp_mfma_probe(0, C.c_void_p(16), C.byref(fl), None) == rtp.RTP_EINVAL
+    assert lib.rtp_mfma_probe((1 << 24) + 1, C.c_void_p(16), C.byref(fl), None) == rtp.RTP_EINVAL
+    assert lib.rtp_hbm_read_probe(None, 64, C.c_void_p(16), None) == rtp.RTP_EINVAL
+
+
 def test_binding_raises_with_message():
     L = _layer(head_dim=96)
     with pytest.raises(rtp.RtpError, match="RTP_EUNSUPPORTED: head_dim"):
