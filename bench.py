@@ -203,10 +203,16 @@ class DecodeBench:
         local = 4 * D * n_local * B * n_loc_kv
         gathered = 4 * D * union
         qo = 2 * 2 * D * B * cfg.n_q_heads
+        groups = B * cfg.n_kv_r
         return {"kidx": kidx, "local_kv": local, "gathered_kv_union": gathered, "q_out": qo,
                 "total": kidx + local + gathered + qo, "union_tokens": union, "per_head_tokens": per_head,
                 "sel_min": int(cnt.min()), "sel_median": int(np.median(cnt)), "sel_mean": float(cnt.mean()),
-                "sel_max": int(cnt.max())}
+                "sel_max": int(cnt.max()),
+                # compute sparsity (summary, "Experimental setup", metrics): share of the context a
+                # retrieval head does not attend to, per query head and per GQA group's union
+                "compute_sparsity": {"per_head_mean": round(1.0 - float(cnt.mean()) / N, 4),
+                                     "per_head_min": round(1.0 - float(cnt.max()) / N, 4),
+                                     "gqa_union_mean": round(1.0 - union / (groups * N), 4)}}
 
 
 # ----------------------------------------------------------------------------- long generation
@@ -322,24 +328,86 @@ class PrefillBench:
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(dec: DecodeBench):
-    """The fp64 oracle, single-threaded, on one batch entry of the 128K decode step
-    (all 32 heads), scaled by the batch size to a whole step."""
+def host_identity():
+    """CPU model of this host and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(dec: DecodeBench, prefill: bool = True):
+    """The fp64 oracle, single-threaded, on a bounded sample of each workload.
+
+    Decode: each batch entry of the 128K step once (all 32 heads), the time per entry
+    scaled by the batch size to a whole step.  Prefill (32K in 4K chunks): the indexer-key
+    projection of the whole sequence plus the seeded sample rows of every head, measured;
+    the time per sampled row times the 32768 x 32 rows of the pass is reported as an
+    extrapolation."""
     from threadpoolctl import threadpool_limits
     from oracle import rtp_oracle as O
     x, cfg = dec.x, dec.cfg
+    host = host_identity()
     with threadpool_limits(limits=1):
-        reps, t0 = 0, time.time()
-        while True:
+        t0 = time.time()
+        for b in range(cfg.batch):
             O.decode_step(x.q_pre, x.q, x.k, x.v, x.k_idx, x.w_q_idx, x.kv_role, cfg.n_ctx, cfg.top_p, cfg.n_sinks,
-                          cfg.window, batch_rows=[reps % cfg.batch])
-            reps += 1
-            if time.time() - t0 > 10.0 or reps >= 8:
-                break
-        per_row = (time.time() - t0) / reps
-    return {"value": per_row * cfg.batch * 1e6, "unit": "us/step/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} batch entr{'y' if reps == 1 else 'ies'} of the 128K decode step (all 32 heads, "
-                      f"p=0.95), fp64 numpy on 1 thread, scaled by batch {cfg.batch}"}
+                          cfg.window, batch_rows=[b])
+        per_entry = (time.time() - t0) / cfg.batch
+    res = {"value": round(per_entry * cfg.batch * 1e6, 1), "unit": "us/step/layer", "cores": 1, "kind": "oracle",
+           "sample": f"each of the {cfg.batch} batch entries of the 128K decode step once (all 32 heads, p=0.95), "
+                     f"fp64 numpy on 1 thread: the whole step, measured",
+           **host}
+    if prefill:
+        res["prefill"] = cpu_baseline_prefill()
+    return res
+
+
+def cpu_baseline_prefill(max_rows_per_head: int = 64):
+    """The oracle's prefill leg (see cpu_baseline)."""
+    from threadpoolctl import threadpool_limits
+    from head_wise_sparse_amd import workloads as W
+    from oracle import rtp_oracle as O
+    cfg = W.CONFIGS["prefill_32k"]
+    pi = W.PrefillInputs(cfg)
+    k, v, kp = pi.full_kv()
+    G = cfg.group
+    rows_of = {h: pi.sample_rows(h)[:max_rows_per_head] for h in range(cfg.n_q_heads)}
+    qrows = {}
+    for h, rows in rows_of.items():
+        chunks = {}
+        for r in rows:
+            c = int(r) // cfg.chunk
+            if c not in chunks:
+                chunks[c] = pi.q_chunk(c, heads=[h])
+        qrows[h] = np.stack([chunks[int(r) // cfg.chunk][int(r) % cfg.chunk, h] for r in rows])
+    with threadpool_limits(limits=1):
+        t0 = time.time()
+        O.prefill_kidx(kp, pi.w_k_idx, cfg.kv_role)
+        t_proj = time.time() - t0
+        t1 = time.time()
+        n_rows = 0
+        for h, rows in rows_of.items():
+            g = h // G
+            O.prefill_rows(qrows[h], rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
+            n_rows += len(rows)
+        t_rows = time.time() - t1
+    per_row = t_rows / n_rows
+    total_rows = cfg.seq_len * cfg.n_q_heads
+    return {"measured_s": round(t_proj + t_rows, 3), "projection_s": round(t_proj, 3),
+            "sampled_rows": n_rows, "rows_s": round(t_rows, 3),
+            "extrapolated_ms_per_pass": round((t_proj + per_row * total_rows) * 1e3, 1),
+            "extrapolation": f"time per sampled row x {cfg.seq_len} rows x {cfg.n_q_heads} heads + the measured "
+                             "projection (an estimate, not a measurement)",
+            "sample": f"32K prefill (4K chunks): indexer-key projection of all {cfg.seq_len} tokens and "
+                      f"{max_rows_per_head} seeded query rows of each of the {cfg.n_q_heads} heads, fp64 numpy on "
+                      "1 thread", "cores": 1}
 
 
 def report_configs(args):
@@ -588,7 +656,7 @@ def main():
         res["roofline"] = rooflines[dom]
         res["rooflines"] = rooflines
     if dec and not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(dec)
+        res["cpu_baseline"] = cpu_baseline(dec, prefill=pre is not None)
     res["wall_s_timed"] = round(wall, 3)
     print(json.dumps(res))
 

@@ -55,6 +55,20 @@ constexpr int score_items(int idx) { return idx <= 16 ? kScoreItems : kScoreItem
 constexpr int score_tile(int idx) { return kScoreThreads * score_items(idx); }
 size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
 
+// Top-p mass is summed in u64 fixed point with F fraction bits (the row max weighs 2^F):
+// F = 42 up to 2^20 tokens, then one bit fewer per doubling of the context, so that a row
+// of n_ctx weights (each <= 2^F) sums below 2^63.  Rounding moves each weight by at most
+// 2^-(F+1) of the max weight, so the whole row's mass by at most n_ctx * 2^-(F+1) of it:
+// 2^-23 at 2^20 tokens, 2^-15 at 2^24.  Top-p is refused above kTopPMaxCtx tokens, where
+// that bound would pass 1e-4.
+constexpr int64_t kTopPMaxCtx = int64_t(1) << 24;
+inline int mass_frac_bits(int64_t n_ctx) {
+  int c = 0;
+  while ((int64_t(1) << c) < n_ctx) ++c;                        // ceil(log2(n_ctx))
+  return 62 - c < 42 ? 62 - c : 42;
+}
+inline float mass_wscale(int64_t n_ctx) { return float(int64_t(1) << mass_frac_bits(n_ctx)); }
+
 // Top-p selection (four launches; the workspace is zero before and after a call).
 constexpr int kSelThreads = 256;
 constexpr int kSelItems = 16;
@@ -96,6 +110,7 @@ struct SelArgs {
   float* row_max_out;            // with score_part: row statistics written by the first pass
   float* row_sum_out;
   float top_p;
+  float wscale;                  // 2^F of the fixed-point mass (mass_wscale(n_ctx); set by launch_select)
   int by_count;                  // static top-k: bins weigh their token counts, the target is k_target
   int64_t k_target;
   int n_ctx;
@@ -187,10 +202,12 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// Fixed-point softmax weight of a score: round(exp(s - m) * 2^42), exp argument clamped to <= 0.
-__device__ __forceinline__ uint64_t fixed_weight(float s, float m) {
+// Fixed-point softmax weight of a score: round(exp(s - m) * 2^F), exp argument clamped to
+// <= 0, with wscale = 2^F (F from mass_frac_bits: every weight is <= 2^F and a row of n_ctx
+// of them sums below 2^63).
+__device__ __forceinline__ uint64_t fixed_weight(float s, float m, float wscale) {
   float w = __expf(fminf(s - m, 0.0f));
-  return (uint64_t)__builtin_rintf(w * 4398046511104.0f);   // 2^42; w*2^42 < 2^43 fits a float
+  return (uint64_t)__builtin_rintf(w * wscale);              // w * 2^F <= 2^42 is exact in float range
 }
 
 template <typename T>

@@ -9,8 +9,9 @@
 // t the threshold key and r a tie count.  The search is O(N) and takes four launches:
 //
 //   hist<0>   histogram of key bits [31:21] over the whole row.  Each bin carries the
-//             token count and the softmax mass exp(s - max) in 2^-42 fixed point (u64:
-//             exact sums, independent of order, bit-reproducible).  Bins are built in
+//             token count and the softmax mass exp(s - max) in u64 fixed point (2^-42
+//             up to 2^20 tokens, see mass_frac_bits: exact sums, independent of order,
+//             bit-reproducible).  Bins are built in
 //             LDS per block and added to the row's histogram with global atomics, with a
 //             64-bin coarse summary (32 fine bins each) beside it.
 //   hist<1,2> the same on key bits [20:10] and [9:0], only for tokens whose higher
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
     const bool match = (j < a.n_ctx) && (LEVEL == 0 || (key >> PSHIFT) == prefix);
     if (match) {
       const uint32_t d = (key >> SHIFT) & uint32_t(NB - 1);
-      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m));
+      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m, a.wscale));
       atomicAdd(&h_c[d], 1u);
     }
     if constexpr (LEVEL == 2) n_above += uint32_t((j < a.n_ctx) && (key >> PSHIFT) > prefix);
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     if (lane == 0) {
       // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
       s_t = o.prefix;
-      const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(o.prefix), a.R.state[row].ref_max);
+      const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(o.prefix), a.R.state[row].ref_max, a.wscale);
       const uint64_t rem = o.target - o.above;
       uint64_t r = (w == 0) ? o.tied : (rem + w - 1) / w;
       if (r < 1) r = 1;
@@ -606,6 +607,8 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   if (n_ctx < 1 || n_ctx > L.n_cap)
     return fail(RTP_EINVAL, "n_ctx must be in [1, n_cap=%lld] (got %lld)", (long long)L.n_cap, (long long)n_ctx);
   if (!(top_p > 0.0f)) return fail(RTP_EINVAL, "top_p must be > 0 (got %g)", double(top_p));
+  if (top_p < 1.0f && n_ctx > kTopPMaxCtx)
+    return fail(RTP_EUNSUPPORTED, "rtp_topp_select: top_p < 1 needs n_ctx <= 2^24 (got %lld)", (long long)n_ctx);
   if (L.n_ret == 0) return ok();
   if (!scores || !row_max || !sel_idx || !sel_count) return fail(RTP_EINVAL, "rtp_topp_select: NULL tensor pointer");
   if (!aligned(scores, 16) || !aligned(sel_idx, 16))
@@ -684,6 +687,7 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
   }
   // tile size: 16 scores per thread, or 32 when that keeps a pass to one round of blocks
   SelArgs b = a;
+  b.wscale = mass_wscale(a.n_ctx);
   const int64_t nblk16 = (int64_t(a.n_ctx) + kSelTile - 1) / kSelTile;
   b.items = nblk16 * rows > kDecBlocksTarget ? kSelItemsLong : kSelItems;
   b.nblk = int((int64_t(a.n_ctx) + kSelThreads * b.items - 1) / (kSelThreads * b.items));

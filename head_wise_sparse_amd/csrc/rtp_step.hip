@@ -150,6 +150,8 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
                   (long long)w_head_stride);
     if (!std::isfinite(idx_scale)) return fail(RTP_EINVAL, "idx_scale must be finite");
     if (!(top_p > 0.0f)) return fail(RTP_EINVAL, "top_p must be > 0 (got %g)", double(top_p));
+    if (top_p < 1.0f && n_ctx > kTopPMaxCtx)
+      return fail(RTP_EUNSUPPORTED, "rtp_decode_step: top_p < 1 needs n_ctx <= 2^24 (got %lld)", (long long)n_ctx);
     if (!aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(q_pre, 16) || !aligned(w_q_idx, 16) ||
         !aligned(sel_idx, 16))
       return fail(RTP_EINVAL, "rtp_decode_step: tensors must be 16-byte aligned");

@@ -76,6 +76,10 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
     const uint16_t* src = w_q + int64_t(r * G + t) * w_stride + off * 8;
     __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(s_w + i * kScoreThreads + wave * 64), 16, 0, 0);
   }
+  // The wait below (vmcnt(NK)) relies on every direct-to-LDS copy being issued before the
+  // NK key loads: this barrier keeps the compiler from moving any key load above it.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   // this tile's keys: thread tid takes tokens base + it*256 + tid (coalesced 2*IDX-byte rows)
   const int64_t base = int64_t(blk) * TILE;
   const uint16_t* kp = k_idx + int64_t(grp) * n_cap * IDX;

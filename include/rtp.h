@@ -12,8 +12,8 @@
  *   - retrieval heads pick tokens with a 16-dimensional pre-RoPE indexer and a
  *     query-adaptive top-p threshold over the indexer's softmax mass (abstract,
  *     observations (2) and (3); summary, "Approach"), then attend over the
- *     gathered K/V of that set (abstract: "lightweight token indexer for sparse
- *     attention");
+ *     gathered K/V of that set only (abstract: a small indexer picks the tokens
+ *     that sparse attention reads);
  *   - during prefill retrieval heads stay dense (summary, "Limitations").
  *
  * Conventions shared by every call
@@ -143,9 +143,12 @@ rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ctx,
  * With pi_j = exp(s_j - row_max) / row_sum, tokens are ranked by score (higher
  * first; equal scores: lower index first) and the set is the shortest prefix of
  * that ranking whose mass reaches top_p.  top_p >= 1 keeps all n_ctx tokens.
- * The mass is accumulated in 2^-42 fixed point (order independent, so results
- * are bit-reproducible); a token whose rank sits within ~1e-6 of the p boundary
- * may differ from an exact computation.
+ * The mass is accumulated in u64 fixed point: the row max weighs 2^F with F = 42 up
+ * to 2^20 tokens and one bit less per doubling beyond (the row total stays below
+ * 2^63).  Sums are exact and order independent, so results are bit-reproducible; a
+ * token whose rank sits within n_ctx * 2^-(F+1) of the p boundary (~1e-7 at 1M tokens)
+ * may differ from an exact computation.  top_p < 1 with n_ctx > 2^24 returns
+ * RTP_EUNSUPPORTED (the bound would pass 1e-4 of the mass).
  *
  *   scores   fp32 [B][Hq_r][n_cap]  (j < n_ctx read), row_max/row_sum fp32 [B][Hq_r]
  *            (row_sum is accepted for interface symmetry; the fixed-point total is used)

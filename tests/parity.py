@@ -138,3 +138,21 @@ def score_scale(x, b: int, ci: int, r: int, n_ctx: int) -> np.ndarray:
     g = x.cfg.retrieval_kv[r]
     qi = O.indexer_query(O.bf16_to_f64(x.q_pre[b, g * G + ci % G]), O.bf16_to_f64(x.w_q_idx[ci]))
     return np.abs(O.bf16_to_f64(x.k_idx[b, r, :n_ctx])) @ np.abs(qi)
+
+
+def check_retrieval_row(g_row: np.ndarray, x, b: int, h: int, gpu_sel: np.ndarray, n_ctx: int, same: bool,
+                        ora_out_row: np.ndarray, what: str = ""):
+    """Output of one retrieval query row.  When the GPU set equals the oracle's, against the
+    oracle's output; otherwise against the oracle's attention over the GPU's own set (the set
+    itself is judged by check_set), so that every row's gather and merge are checked."""
+    if same:
+        return check_outputs(g_row[None], ora_out_row[None], what)
+    G = x.cfg.group
+    D = x.cfg.head_dim
+    sel = np.asarray(gpu_sel, np.int64)
+    if sel.size == 0:
+        assert np.all(O.bf16_to_f64(g_row) == 0), f"{what}: an empty set must give a zero row"
+        return 0.0, 0.0
+    ref = O.attend(O.bf16_to_f64(x.q[b, h]), O.bf16_to_f64(x.k[b, h // G, :n_ctx]),
+                   O.bf16_to_f64(x.v[b, h // G, :n_ctx]), sel, 1 / math.sqrt(D))
+    return check_outputs(g_row[None], ref[None], what + " (over the GPU's set)")

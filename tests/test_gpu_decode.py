@@ -402,8 +402,8 @@ def test_decode_step_end_to_end(name, p):
             same, _ = P.check_set(sel[b, ci, :cnt[b, ci]], ora["info"][(b, ci)], p, ora["scores"][(b, ci)],
                                   P.FP32_SCORE_SLACK * scale)
             h = cfg.retrieval_kv[r] * G + ci % G
-            if same:
-                P.check_outputs(g[b, h][None], ora["out"][b, h][None], f"retrieval row ({b},{h})")
+            P.check_retrieval_row(g[b, h], x, b, h, sel[b, ci, :cnt[b, ci]], N, same, ora["out"][b, h],
+                                  f"retrieval row ({b},{h})")
             identical.append(same)
             sizes.append(int(cnt[b, ci]))
     loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
@@ -467,8 +467,8 @@ def test_decode_step_shapes(head_dim, group):
             ok, _ = P.check_set(res[1]["sets"][b * R + ci], ora["info"][(b, ci)], cfg.top_p, ora["scores"][(b, ci)],
                                 P.FP32_SCORE_SLACK * P.score_scale(x, b, ci, r, N))
             h = cfg.retrieval_kv[r] * G + ci % G
-            if ok:
-                P.check_outputs(g[b, h][None], ora["out"][b, h][None], f"retrieval row ({b},{h})")
+            P.check_retrieval_row(g[b, h], x, b, h, res[1]["sets"][b * R + ci], N, ok, ora["out"][b, h],
+                                  f"retrieval row ({b},{h})")
             same += ok
     loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
     P.check_outputs(g[:, loc], ora["out"][:, loc], "local rows")
@@ -808,8 +808,8 @@ def test_decode_step_other_indexer_dims(idx_dim):
             same, _ = P.check_set(sel[b, ci, :cnt[b, ci]], ora["info"][(b, ci)], cfg.top_p, ora["scores"][(b, ci)],
                                   P.FP32_SCORE_SLACK * P.score_scale(x, b, ci, r, N))
             h = cfg.retrieval_kv[r] * G + ci % G
-            if same:
-                P.check_outputs(g[b, h][None], ora["out"][b, h][None], f"row ({b},{h})")
+            P.check_retrieval_row(g[b, h], x, b, h, sel[b, ci, :cnt[b, ci]], N, same, ora["out"][b, h],
+                                  f"row ({b},{h})")
             same_all += same
     assert same_all >= 0.9 * B * R
     loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]

@@ -319,6 +319,20 @@ def test_recall_is_one_for_full_set():
     assert 0.0 < r < 1.0
 
 
+def test_recall_hand_worked_three_keys():
+    """Recall by hand: q = (2 ln 2, 0), keys (1,0), (0,1), (-1,0), sm_scale 1/2 give logits
+    ln 2, 0, -ln 2, so softmax weights 2 : 1 : 1/2 of a total 7/2.  The first key holds 4/7 of
+    the mass, the first and third 5/7.  With the scale left out (1 instead of 1/2) the weights
+    would be 4 : 1 : 1/4 and the first key would hold 16/21, so the scale is pinned."""
+    q = np.array([2.0 * math.log(2.0), 0.0])
+    k = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0]])
+    assert abs(O.attention_recall(q, k, None, 3, np.array([0]), 0.5) - 4.0 / 7.0) < 1e-12
+    assert abs(O.attention_recall(q, k, None, 3, np.array([0, 2]), 0.5) - 5.0 / 7.0) < 1e-12
+    assert abs(O.attention_recall(q, k, None, 3, np.array([1]), 0.5) - 2.0 / 7.0) < 1e-12
+    # only the first n_ctx keys count: with n_ctx = 2 the third key is outside the context
+    assert abs(O.attention_recall(q, k, None, 2, np.array([0]), 0.5) - 2.0 / 3.0) < 1e-12
+
+
 # ----------------------------------------------------------------------------- static top-k
 def _ranks_before(s, i, j):
     """Token i ranks before token j: higher score, or equal score and lower index."""
