@@ -151,6 +151,12 @@ def test_call_validation():
             == rtp.RTP_EINVAL
     assert lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, None, FAKE, 64, None) \
         == rtp.RTP_EWORKSPACE
+    # top-p mass is fixed point sized from the context: refused above 2^24 tokens (p < 1 only)
+    Lbig = _layer(batch=1, n_cap=(1 << 24) + 1)
+    assert lib.rtp_topp_select(Lbig.desc, (1 << 24) + 1, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, None, FAKE, 1 << 40,
+                               None) == rtp.RTP_EUNSUPPORTED
+    assert "2^24" in lib.rtp_last_error().decode()
+    assert _call_step(Lbig, n_ctx=(1 << 24) + 1, ws_bytes=1 << 40) == rtp.RTP_EUNSUPPORTED
     assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, None, FAKE, None, 0.1, FAKE, FAKE, 1 << 30,
                                       None) == rtp.RTP_EINVAL
     assert lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, math.inf, FAKE, FAKE,

@@ -229,6 +229,23 @@ def test_topp_select_edge_cases(case):
             assert s.tolist() == [int(np.flatnonzero(s32[r] == s32[r].max())[0])]
 
 
+def test_topp_select_flat_row_at_largest_context():
+    """A flat row (every score equal) at 2^24 tokens, the longest context top-p accepts: all
+    weights equal the row max's, so the row total is n_ctx times the largest weight -- the
+    case where a fixed-point total with too many fraction bits would wrap -- and the set is
+    exactly the first ceil(p * n_ctx) tokens (ties are taken lowest index first)."""
+    P.require_gpu()
+    n = 1 << 24
+    L = rtp.Layer(2, 1, 1, 64, n, [1], 0, 1)
+    s32 = np.zeros((2, n), np.float32)
+    s32[1] = 3.25
+    for p in (0.5, 0.999):
+        sets = _run_select(L, n, s32, p)
+        k = math.ceil(p * n)
+        for s in sets:
+            assert s.size == k and s[0] == 0 and s[-1] == k - 1 and np.all(np.diff(s) == 1)
+
+
 # ----------------------------------------------------------------------------- sparse decode
 def _sel_tensors(sets, B, R, cap):
     torch = _torch()
