@@ -7,7 +7,8 @@
 //  * the chunk's 16-dim indexer keys, bf16(k_pre . W_k_idx), for every retrieval KV
 //    head (pre-RoPE projection, summary "Approach"; abstract, observation (2)).
 //
-// Attention kernel (flash-attention forward, bf16 in / fp32 accumulate, D = 128):
+// Attention kernel (flash-attention forward, bf16 in / fp32 accumulate, D = 64 or 128,
+// one instantiation each):
 //  - a block has 4 waves of 32 query rows: gcd(G, 4) query heads of one KV head (grouped-
 //    query attention: they read the same keys) times 4 / gcd(G, 4) row slices, so one K/V
 //    tile copied to LDS serves up to four heads.  It walks 64-key tiles of the cache:
@@ -48,22 +49,31 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int PD = 128;               // head dim
 constexpr int RB = 1;                 // 32-row column blocks per wave
 constexpr int NW = 4;                 // waves per block (two blocks per CU)
 constexpr int kOpAhead = 2;           // LDS operand reads in flight ahead of their MFMA
 constexpr int WR = 32 * RB;           // query rows per wave
 constexpr int BN = 64;                // keys per tile
-// LDS tiles are 64 rows x 128 bf16 (256-byte rows, 16 chunks of 16 bytes), unpadded
+// LDS tiles are 64 rows x PD bf16 (2*PD-byte rows of PD/8 chunks of 16 bytes), unpadded
 // (direct-to-LDS loads fill 1 KB contiguous runs), with the chunk index XOR-swizzled per
-// row, differently for K and V:
-//  - K is read as MFMA A operands: 16 consecutive rows, one chunk each -> c ^ (r & 15)
-//    puts them in 16 different chunk slots;
-//  - V is read with the transposing read: per wave, rows 4h .. 4h+3 (h = 0, 1) x 4 chunks
-//    -> c ^ 4*(r & 3) spreads each row's 4 chunks over a different quarter of the row.
-constexpr int KP = PD;
-__device__ __forceinline__ int swz_k(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }
-__device__ __forceinline__ int swz_v(int r, int c) { return r * 128 + ((c ^ ((r & 3) << 2)) << 3); }
+// row, differently for K and V, so that the 16 (ds_read_b128) or 32 (ds_read_b64_tr_b16)
+// lanes the LDS serves together touch 256 distinct bytes:
+//  - K is read as MFMA A operands: 16 consecutive rows, one chunk each.  PD = 128
+//    (256-byte rows): c ^ (r & 15) puts them in 16 different chunk slots; PD = 64
+//    (128-byte rows, two per 256 bytes): c ^ ((r >> 1) & 7) gives the 8 rows of each parity
+//    8 different slots.
+//  - V is read with the transposing read: per wave, rows 4h .. 4h+3 (h = 0, 1) x 4 chunks.
+//    PD = 128: c ^ 4*(r & 3) spreads each row's 4 chunks over a different quarter of the
+//    row; PD = 64: c ^ 4*((r >> 1) & 1) puts rows 4h and 4h+2 (same half of 256 bytes) in
+//    different halves of their rows.
+template <int PD>
+__device__ __forceinline__ int swz_xk(int r) { return PD == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int PD>
+__device__ __forceinline__ int swz_xv(int r) { return PD == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+template <int PD>
+__device__ __forceinline__ int swz_k(int r, int c) { return r * PD + ((c ^ swz_xk<PD>(r)) << 3); }
+template <int PD>
+__device__ __forceinline__ int swz_v(int r, int c) { return r * PD + ((c ^ swz_xv<PD>(r)) << 3); }
 
 // 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i writes at the
 // wave-uniform LDS byte address `lds` + 16*i.  Issued from inline asm so that the
@@ -127,7 +137,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin
 // block per 16 indexer outputs (dims 4 and 8 use one block, zero-padded).
 // These blocks run as the last blocks of the attention grid (block x of 64 tokens, retrieval
 // rank r), in the attention's tail; `lds` is the block's K tile buffer, free in such blocks.
-template <int IDX>
+template <int IDX, int PD>
 __device__ __forceinline__ void kidx_proj_block(const PrefArgs& a, int bx, int r, uint16_t* lds) {
   constexpr int NCB = IDX > 16 ? IDX / 16 : 1;                  // 16-column output blocks
   const uint16_t* __restrict__ k_pre = a.k_pre;
@@ -177,19 +187,21 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t* lds_s4;
 
+template <int PD>
 __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
+  static_assert(PD == 64 || PD == 128, "head dims");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hf = lane >> 5;
-  __shared__ uint16_t s_k[2][BN * KP];
-  __shared__ uint16_t s_v[2][BN * KP];
+  __shared__ uint16_t s_k[2][BN * PD];
+  __shared__ uint16_t s_v[2][BN * PD];
 
   if (blockIdx.x >= a.n_attn) {               // indexer-key projection block
     const int pb = blockIdx.x - a.n_attn, bx = pb % a.n_px, r = pb / a.n_px;
     switch (a.idx) {
-      case 4: kidx_proj_block<4>(a, bx, r, s_k[0]); break;
-      case 8: kidx_proj_block<8>(a, bx, r, s_k[0]); break;
-      case 16: kidx_proj_block<16>(a, bx, r, s_k[0]); break;
-      default: kidx_proj_block<32>(a, bx, r, s_k[0]); break;
+      case 4: kidx_proj_block<4, PD>(a, bx, r, s_k[0]); break;
+      case 8: kidx_proj_block<8, PD>(a, bx, r, s_k[0]); break;
+      case 16: kidx_proj_block<16, PD>(a, bx, r, s_k[0]); break;
+      default: kidx_proj_block<32, PD>(a, bx, r, s_k[0]); break;
     }
     return;
   }
@@ -264,8 +276,8 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
     short4_t h0, h1;
     const int d = 32 * db + 16 * tr_dsub + 4 * (tr_r & 3);
     const int key0 = 16 * ks + 4 * hf + (tr_r >> 2);
-    h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&s_v[buf][swz_v(key0, d >> 3) + (d & 7)]));
-    h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&s_v[buf][swz_v(key0 + 8, d >> 3) + (d & 7)]));
+    h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&s_v[buf][swz_v<PD>(key0, d >> 3) + (d & 7)]));
+    h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&s_v[buf][swz_v<PD>(key0 + 8, d >> 3) + (d & 7)]));
     short8_t r8;
     r8[0] = h0[0]; r8[1] = h0[1]; r8[2] = h0[2]; r8[3] = h0[3];
     r8[4] = h1[0]; r8[5] = h1[1]; r8[6] = h1[2]; r8[7] = h1[3];
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ds = 0; ds < PD / 16; ++ds) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][swz_k(kb * 32 + l32, 2 * ds + hf)]);
+        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][swz_k<PD>(kb * 32 + l32, 2 * ds + hf)]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sa[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[rb][ds], sa[rb][kb], 0, 0, 0);
@@ -310,16 +322,21 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
   };
 
   // Tile copies.  Wave w's i-th copy fills physical chunks (NW*i + w)*64 .. +63 of the
-  // tile, i.e. rows 4*NW*i + crow (crow = 4w + lane/16); the swizzled chunk a lane fetches
-  // does not depend on i, so a copy is one scalar base (the tile's first row, + NW KB per
-  // i) plus a fixed per-lane byte offset.  Only a tile that runs past the chunk's last row
-  // (rows from c0 + C on need not hold valid data yet) takes the clamped path: its rows
-  // from there on repeat the last valid row, so they are finite; their scores are masked
-  // and their probabilities are exactly 0.
+  // tile, i.e. the RPC rows RPC*NW*i + crow (crow = RPC*w + lane/CPR, RPC = 1 KB / row
+  // bytes, CPR chunks per row); the swizzled chunk a lane fetches does not depend on i, so
+  // a copy is one scalar base (the tile's first row, + NW KB per i) plus a fixed per-lane
+  // byte offset.  Only a tile that runs past the chunk's last row (rows from c0 + C on
+  // need not hold valid data yet) takes the clamped path: its rows from there on repeat
+  // the last valid row, so they are finite; their scores are masked and their
+  // probabilities are exactly 0.
+  constexpr int CPR = PD / 8;                                 // 16-byte chunks per row
+  constexpr int RPC = 64 / CPR;                               // rows per 1 KB wave copy
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int crow = 4 * wave + (lane >> 4);
-  const uint32_t koff = uint32_t(crow * PD + (((lane & 15) ^ (crow & 15)) << 3)) * 2u;
-  const uint32_t voff = uint32_t(crow * PD + (((lane & 15) ^ ((crow & 3) << 2)) << 3)) * 2u;
+  const int crow = RPC * wave + lane / CPR;
+  const int cslot = lane % CPR;
+  // the XOR terms depend only on crow: RPC*NW*i is a multiple of 16 (PD = 128) or 32 (PD = 64)
+  const uint32_t koff = uint32_t(crow * PD + ((cslot ^ swz_xk<PD>(crow)) << 3)) * 2u;
+  const uint32_t voff = uint32_t(crow * PD + ((cslot ^ swz_xv<PD>(crow)) << 3)) * 2u;
   static_assert(KLD * NWV * 64 == KCH && NWV == NW, "copy layout");
   const int64_t kv_end = a.c0 + a.C;          // cache rows below this are valid (<= n_cap)
   auto copy_tile = [&](const uint16_t* base, int kt, uint32_t off, uint16_t* lds_tile, bool is_k) {
@@ -332,8 +349,8 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < KLD; ++i) {
-        const int row = 4 * NW * i + crow;
-        const int c = is_k ? ((lane & 15) ^ (crow & 15)) : ((lane & 15) ^ ((crow & 3) << 2));
+        const int row = RPC * NW * i + crow;
+        const int c = is_k ? (cslot ^ swz_xk<PD>(crow)) : (cslot ^ swz_xv<PD>(crow));
         const int64_t kr = min<int64_t>(k0 + row, kv_end - 1);
         g2lds_16(base + kr * PD + c * 8, lds0 + 1024u * NW * i);
       }
@@ -412,22 +429,31 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
 
     // ---- straight-line part: QK of the next tile, softmax and PV of this one
     if constexpr (HAS_NEXT) {
-      // 32 MFMA slots, pinned in this order by scheduling barriers: QK^T(n+1) in slots
-      // 0..15 (alternating the two 32-key chains), each carrying one pair of this tile's
-      // exponentials; PV(n) in slots 16..31, which also carry the next tile's row max (its
-      // chains finished by then).  K and V^T operands are read kOpAhead slots ahead; left
-      // to itself the compiler reads each operand one MFMA before its use.
+      // 2*NQK MFMA slots (32 at PD = 128, 16 at PD = 64), pinned in this order by scheduling
+      // barriers: QK^T(n+1) in slots 0..NQK-1 (alternating the two 32-key chains), each
+      // carrying 16/NQK pairs of this tile's exponentials; PV(n) in the next NQK slots,
+      // which also carry the next tile's row max (its chains finished by then).  K and V^T
+      // operands are read kOpAhead slots ahead; left to itself the compiler reads each
+      // operand one MFMA before its use.
       static_assert(RB == 1, "slot schedule assumes one row block per wave");
       constexpr int KB1 = 1 - B;
-      bf16x8_t kop[16], vop[16];
+      constexpr int NQK = PD / 8;                 // QK^T MFMAs per tile: 2 chains x PD/16
+      constexpr int NDB = PD / 32;                // 32-dim output blocks
+      constexpr int NPV = 4 * NDB;                // PV MFMAs per tile: 4 key steps x NDB
+      constexpr int EPS = 16 / NQK;               // exponential pairs per QK slot
+      constexpr int T0 = PD == 128 ? 2 : 1;       // first PV slot folding chain 0 into the row max
+      constexpr int T1 = NPV / 2;                 // first PV slot folding chain 1
+      constexpr int VPP = 16 / (NPV - T1);        // values folded per slot
+      static_assert(NPV == NQK && EPS * NQK == 16 && VPP * (NPV - T1) == 16, "slot schedule");
+      bf16x8_t kop[NQK], vop[NPV];
       uint32_t pk[2][8];
       float psum = 0.0f;
       const float nm = -m_run[0];
       auto kread = [&](int s) {
         const int kbp = s & 1, ds = s >> 1;
-        kop[s] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_k[KB1][swz_k(kbp * 32 + l32, 2 * ds + hf)]));
+        kop[s] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_k[KB1][swz_k<PD>(kbp * 32 + l32, 2 * ds + hf)]));
       };
-      auto vread = [&](int p) { vop[p] = vt_operand(B, p & 3, p >> 2); };
+      auto vread = [&](int p) { vop[p] = vt_operand(B, p % NDB, p / NDB); };
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -436,34 +462,40 @@ __global__ __launch_bounds__(kPreThreads, 2) void k_prefill_attn(PrefArgs a) {
       for (int s = 0; s < kOpAhead; ++s) kread(s);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
+      for (int s = 0; s < NQK; ++s) {
         nxt[0][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[0][s >> 1], nxt[0][s & 1], 0, 0, 0);
-        if (s + kOpAhead < 16) kread(s + kOpAhead);
-        if (s >= 16 - kOpAhead) vread(s - (16 - kOpAhead));
-        {
-          const int kb = s >> 3, v = 2 * (s & 7);
+        if (s + kOpAhead < NQK) kread(s + kOpAhead);
+        if (s >= NQK - kOpAhead) vread(s - (NQK - kOpAhead));
+#pragma unroll
+        for (int j = 0; j < EPS; ++j) {
+          const int e = s * EPS + j, kb = e >> 3, v = 2 * (e & 7);
           const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[0][kb][v], a.scale_log2, nm));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[0][kb][v + 1], a.scale_log2, nm));
-          pk[kb][s & 7] = pack_bf16x2(p0, p1);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb][s & 7]),
+          pk[kb][e & 7] = pack_bf16x2(p0, p1);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb][e & 7]),
                                                  __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // PV slots; the next tile's row max rides along (its S chains finished in slots 14/15)
+      // PV slots; the next tile's row max rides along (its S chains finished in the last
+      // two QK slots)
       float tm0 = -INFINITY, tm1 = -INFINITY;
 #pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        const int ks = p >> 2, db = p & 3, kb = ks >> 1, half = ks & 1;
-        if (p + kOpAhead < 16) vread(p + kOpAhead);
+      for (int p = 0; p < NPV; ++p) {
+        const int ks = p / NDB, db = p % NDB, kb = ks >> 1, half = ks & 1;
+        if (p + kOpAhead < NPV) vread(p + kOpAhead);
         const uint4 pb = make_uint4(pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2], pk[kb][4 * half + 3]);
         oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[p], as_bf16x8(pb), oacc[0][db], 0, 0, 0);
-        if (p >= 2 && p < 10) {
-          tm0 = fmaxf(fmaxf(tm0, nxt[0][0][2 * (p - 2)]), nxt[0][0][2 * (p - 2) + 1]);
+        if (p >= T0 && p < T0 + 16 / VPP) {
+#pragma unroll
+          for (int j = 0; j < VPP; j += 2)
+            tm0 = fmaxf(fmaxf(tm0, nxt[0][0][VPP * (p - T0) + j]), nxt[0][0][VPP * (p - T0) + j + 1]);
           asm volatile("" : "+v"(tm0));          // keep this partial max in its slot
         }
-        if (p >= 8) {
-          tm1 = fmaxf(fmaxf(tm1, nxt[0][1][2 * (p - 8)]), nxt[0][1][2 * (p - 8) + 1]);
+        if (p >= T1) {
+#pragma unroll
+          for (int j = 0; j < VPP; j += 2)
+            tm1 = fmaxf(fmaxf(tm1, nxt[0][1][VPP * (p - T1) + j]), nxt[0][1][VPP * (p - T1) + j + 1]);
           asm volatile("" : "+v"(tm1));
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -591,7 +623,7 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
   if (c0 < 0 || c0 + C > L.n_cap)
     return fail(RTP_EINVAL, "rtp_prefill_attn: need 0 <= c0 and c0 + C <= n_cap (c0=%lld, C=%d, n_cap=%lld)",
                 (long long)c0, C, (long long)L.n_cap);
-  if (L.D != PD) return fail(RTP_EUNSUPPORTED, "rtp_prefill_attn: head_dim must be 128 (got %d)", L.D);
+
   if (L.kv_layout != RTP_KV_FULL)
     return fail(RTP_EUNSUPPORTED, "rtp_prefill_attn: the chunk needs the full cache layout (RTP_KV_FULL)");
   if (!q || !k_cache || !v_cache || !out) return fail(RTP_EINVAL, "rtp_prefill_attn: NULL tensor pointer");
@@ -634,6 +666,9 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
   a.w_stride = w_head_stride;
   a.k_idx = k_idx_cache;
   const int n_proj = L.n_ret > 0 ? a.n_px * L.n_ret : 0;
-  hipLaunchKernelGGL(k_prefill_attn, dim3(a.n_attn + n_proj), dim3(kPreThreads), 0, s, a);
+  if (L.D == 128)
+    hipLaunchKernelGGL(k_prefill_attn<128>, dim3(a.n_attn + n_proj), dim3(kPreThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_prefill_attn<64>, dim3(a.n_attn + n_proj), dim3(kPreThreads), 0, s, a);
   return check_launch("k_prefill_attn");
 }

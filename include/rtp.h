@@ -240,7 +240,8 @@ rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n_ctx,
  *   w_k_idx  bf16 [Hkv_r][D][I]; head r starts at r*w_head_stride (0 = shared)
  *   k_idx_cache bf16 [Hkv_r][n_cap][I]: rows [c0, c0+C) are written
  *   out      bf16 [C][Hq][D]
- * Requires c0 >= 0, C >= 1, c0 + C <= n_cap, head_dim == 128.
+ * Requires c0 >= 0, C >= 1, c0 + C <= n_cap; head_dim 64 or 128 (each has its own
+ * kernel instantiation: tile layout and MFMA schedule).
  */
 rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, int32_t C,
                             const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,

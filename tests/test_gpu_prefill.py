@@ -142,6 +142,33 @@ def test_prefill_query_group_sizes(hq, hkv, retr):
     _check_kidx(cfg, pi, kp, kidx)
 
 
+@pytest.mark.parametrize("over", [
+    dict(seq_len=700, chunk=256, window=100, n_sinks=4),                       # G = 4, ragged chunks
+    dict(seq_len=900, chunk=300, window=130, n_sinks=77),                      # sinks span two key tiles
+    dict(seq_len=40, chunk=1, window=9, n_sinks=2),                            # one row per chunk
+    dict(seq_len=513, chunk=513, window=4096, n_sinks=4),                      # window covers everything
+    dict(seq_len=600, chunk=200, window=70, n_sinks=3, n_q_heads=8),           # G = 1
+    dict(seq_len=600, chunk=200, window=70, n_sinks=3, n_q_heads=16),          # G = 2
+    dict(seq_len=520, chunk=260, window=100, n_sinks=4, idx_dim=32),           # two indexer column blocks
+])
+def test_prefill_head_dim_64(over):
+    """Head dimension 64 (its own tile layout and slot schedule): every row of several heads
+    of each kind, and the indexer keys."""
+    P.require_gpu()
+    cfg = W.scaled_prefill(W.CONFIGS["prefill_32k"], rows_per_head=4, head_dim=64, **over)
+    pi = W.PrefillInputs(cfg)
+    k, v, kp = pi.full_kv()
+    out, kidx = _run_prefill(cfg, pi, k, v, kp)
+    G, Hq = cfg.group, cfg.n_q_heads
+    for h in sorted({0, 1, G - 1, G, 3 * G, Hq // 2 + 1, Hq - 1} & set(range(Hq))):
+        g = h // G
+        rows = np.arange(cfg.seq_len)
+        q_rows = np.concatenate([pi.q_chunk(c, heads=[h])[:, h] for c in range(cfg.n_chunks)])
+        ref = O.prefill_rows(q_rows, rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
+        P.check_outputs(out[:, h], ref, f"head {h} (D=64, G={G})")
+    _check_kidx(cfg, pi, kp, kidx)
+
+
 @pytest.mark.parametrize("retr", [(0, 3), (0, 1, 2, 3, 4, 5, 6, 7)])
 def test_prefill_ignores_rows_past_the_chunk(retr):
     """Cache rows at or past c0 + C are not valid yet (the contract): fill them with NaN and
