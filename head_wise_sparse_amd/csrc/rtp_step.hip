@@ -13,7 +13,9 @@
 //   7. one merge launch for the split partials of both head kinds (preceded, when a
 //      retrieval row has more than 128 split partials, by a launch that combines
 //      them 32 at a time).
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "score_dev.hpp"
 #include "decode_dev.hpp"
@@ -117,14 +119,25 @@ namespace rtp {
 size_t step_ws_bytes(const Layer& L, int64_t n_ctx) { return step_layout(L, n_ctx).total; }
 }  // namespace rtp
 
-extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
-                                      const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
-                                      float idx_scale, const uint16_t* q, const uint16_t* k_cache,
-                                      const uint16_t* v_cache, const uint16_t* k_loc, const uint16_t* v_loc,
-                                      float top_p, float sm_scale, float* scores,
-                                      float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
-                                      int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
-                                      void* stream) {
+namespace {
+
+// Zero-fill of n 16-byte words (a kernel rather than a memset node, so that a captured
+// graph replays it faithfully).
+__global__ __launch_bounds__(256) void k_step_clear(uint4* __restrict__ p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += size_t(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The whole step; `clear_sel`: zero the selection region first (the allocation-free entry
+// point, whose scratch keeps whatever the last call on the device left there).
+rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
+                            const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
+                            float idx_scale, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const uint16_t* k_loc, const uint16_t* v_loc,
+                            float top_p, float sm_scale, float* scores,
+                            float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
+                            int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
+                            void* stream, bool clear_sel) {
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;
@@ -166,6 +179,12 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   const int n = int(n_ctx);
+  if (clear_sel && L.n_ret && top_p < 1.0f) {
+    const size_t n16 = sel_layout(L).total / 16;            // the region is a multiple of 256 bytes
+    const unsigned nb = unsigned(std::min<size_t>((n16 + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_step_clear, dim3(nb), dim3(256), 0, s, reinterpret_cast<uint4*>(w + lay.sel), n16);
+    if ((st = check_launch("k_step_clear")) != RTP_OK) return st;
+  }
 
   // ---- launch 1: scoring blocks + local heads' split-K blocks
   ScoreArgs sa{};
@@ -277,4 +296,79 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
   else
     hipLaunchKernelGGL(k_step_merge<64>, dim3(mrows), dim3(256), 0, s, ms, rs, mw);
   return check_launch("k_step_merge");
+}
+
+}  // namespace
+
+extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
+                                      const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
+                                      float idx_scale, const uint16_t* q, const uint16_t* k_cache,
+                                      const uint16_t* v_cache, const uint16_t* k_loc, const uint16_t* v_loc,
+                                      float top_p, float sm_scale, float* scores,
+                                      float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
+                                      int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return decode_step_impl(desc, n_ctx, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,
+                          v_loc, top_p, sm_scale, scores, row_max, row_sum, sel_idx, sel_count, sel_starts, out, ws,
+                          ws_bytes, stream, false);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// The decode step's scratch in a file-scope device array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy (at its own address) until the process
+// ends.  Host code never passes the array's name to a kernel: its device address is looked
+// up once per device and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+rtp_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(RTP_EDEVICE, "rtp_decode_step_noalloc: cannot read the current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RTP_EDEVICE, "rtp_decode_step_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" size_t rtp_decode_step_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" rtp_status rtp_decode_step_noalloc(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q_pre,
+                                              const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
+                                              float idx_scale, const uint16_t* q, const uint16_t* k_cache,
+                                              const uint16_t* v_cache, const uint16_t* k_loc, const uint16_t* v_loc,
+                                              float top_p, float sm_scale, float* scores, float* row_max,
+                                              float* row_sum, int32_t* sel_idx, int32_t* sel_count,
+                                              int32_t* sel_starts, uint16_t* out, void* stream) {
+  Layer L;
+  rtp_status st = check_desc(desc, &L);
+  if (st != RTP_OK) return st;
+  if (n_ctx < 1 || n_ctx > L.n_cap)
+    return fail(RTP_EINVAL, "rtp_decode_step_noalloc: n_ctx must be in [1, n_cap=%lld] (got %lld)",
+                (long long)L.n_cap, (long long)n_ctx);
+  const size_t need = step_ws_bytes(L, n_ctx);
+  if (need > kScratchBytes)
+    return fail(RTP_EUNSUPPORTED,
+                "rtp_decode_step_noalloc: this layer and context need %zu bytes of scratch; the library holds %zu "
+                "(use rtp_decode_step with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != RTP_OK) return st;
+  return decode_step_impl(desc, n_ctx, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,
+                          v_loc, top_p, sm_scale, scores, row_max, row_sum, sel_idx, sel_count, sel_starts, out, ws,
+                          kScratchBytes, stream, true);
 }

@@ -25,7 +25,8 @@ KV_FULL, KV_COMPACT = 0, 1
 
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
             "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_append_token",
-            "rtp_hbm_read_probe", "rtp_mfma_probe", "rtp_status_string", "rtp_last_error", "rtp_version"]
+            "rtp_hbm_read_probe", "rtp_mfma_probe", "rtp_status_string", "rtp_last_error", "rtp_version",
+            "rtp_decode_step_noalloc", "rtp_decode_step_noalloc_max_bytes"]
 
 
 class RtpError(RuntimeError):
@@ -67,6 +68,9 @@ def load() -> C.CDLL:
                                        _P, _P, C.c_size_t, _P]),
         "rtp_decode_step": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, _P, _P,
                                       C.c_float, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_decode_step_noalloc": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, _P, _P,
+                                              C.c_float, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "rtp_decode_step_noalloc_max_bytes": (C.c_size_t, []),
         "rtp_append_token": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, C.c_int64, _P, _P, _P, _P, _P, _P]),
         "rtp_topk_select": (C.c_int, [D, C.c_int64, _P, C.c_int64, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_hbm_read_probe": (C.c_int, [_P, C.c_size_t, _P, _P]),
@@ -217,6 +221,20 @@ def rtp_decode_step(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_stride: int
                                   _ptr(v_loc), float(top_p), float(sm_scale), _ptr(scores), _ptr(row_max),
                                   _ptr(row_sum), _ptr(sel_idx), _ptr(sel_count), _ptr(sel_starts), _ptr(out), p, n,
                                   _stream(stream)))
+
+
+def rtp_decode_step_noalloc(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_stride: int, k_idx, idx_scale: float,
+                            q, k_cache, v_cache, k_loc, v_loc, top_p: float, sm_scale: float, scores, row_max,
+                            row_sum, sel_idx, sel_count, sel_starts, out, stream=None):
+    _check(load().rtp_decode_step_noalloc(layer.desc, int(n_ctx), _ptr(q_pre), _ptr(w_q_idx), int(w_head_stride),
+                                          _ptr(k_idx), float(idx_scale), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(k_loc), _ptr(v_loc), float(top_p), float(sm_scale), _ptr(scores),
+                                          _ptr(row_max), _ptr(row_sum), _ptr(sel_idx), _ptr(sel_count),
+                                          _ptr(sel_starts), _ptr(out), _stream(stream)))
+
+
+def rtp_decode_step_noalloc_max_bytes() -> int:
+    return int(load().rtp_decode_step_noalloc_max_bytes())
 
 
 def rtp_append_token(layer: Layer, pos: int, k_new, v_new, k_pre, w_k_idx, w_head_stride: int, k_cache, v_cache,

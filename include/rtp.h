@@ -286,6 +286,32 @@ rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * rtp_decode_step_noalloc -- rtp_decode_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches, arguments and results bit for bit, with the workspace
+ * replaced by a scratch array the library holds on each GPU it runs on
+ * (rtp_decode_step_noalloc_max_bytes() bytes, 64 MiB, kept until the process ends).
+ * It calls no allocating routine: the array's device address is looked up on the first
+ * call on a device, and every call zero-fills the part the step needs zero with a kernel
+ * (no memset node).
+ *   - A layer and context whose workspace (rtp_workspace_bytes(desc, n_ctx,
+ *     RTP_CALL_DECODE_STEP)) exceeds the array returns RTP_EUNSUPPORTED, nothing enqueued.
+ *   - All calls on one GPU share its array: calls whose execution overlaps (other
+ *     streams, other threads, other graphs replaying) race and give wrong results; the
+ *     caller serialises them.
+ */
+size_t rtp_decode_step_noalloc_max_bytes(void);
+rtp_status rtp_decode_step_noalloc(const rtp_layer_desc* desc, int64_t n_ctx,
+                                   const uint16_t* q_pre, const uint16_t* w_q_idx, int64_t w_head_stride,
+                                   const uint16_t* k_idx, float idx_scale,
+                                   const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                   const uint16_t* k_loc, const uint16_t* v_loc,
+                                   float top_p, float sm_scale,
+                                   float* scores, float* row_max, float* row_sum,
+                                   int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts,
+                                   uint16_t* out, void* stream);
+
+/*
  * rtp_append_token -- store the token at position `pos` (the next one; decode then
  * runs with n_ctx = pos + 1) in every cache of the layout: its post-RoPE key and
  * value for every head, and for retrieval heads its indexer key
