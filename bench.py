@@ -269,6 +269,32 @@ class GenBench:
             self.step.run(self.q_pre, self.q, self.kr, self.vr, self.kidx, self.w_q, n_ctx=pos + 1, k_loc=self.kl,
                           v_loc=self.vl)
 
+    def capture(self):
+        """One HIP graph of [rtp_append_token_dev, rtp_decode_step_dev]: the context length is
+        the device state {pos, n_ctx} that every replay advances by one token.  The replays
+        append the same new-token vectors at successive positions (the work per token does
+        not depend on their values)."""
+        torch, rtp, D = self.torch, self.rtp, self.cfg.head_dim
+        self.gen = torch.tensor([self.n0, self.n0], dtype=torch.int64, device="cuda")
+        self.knew, self.vnew, self.kpnew = self.k_new[0].clone(), self.v_new[0].clone(), self.k_pre[0].clone()
+
+        def pair():
+            rtp.rtp_append_token_dev(self.L, self.gen, self.knew, self.vnew, self.kpnew, self.w_k, D * 16, self.kr,
+                                     self.vr, self.kidx, self.kl, self.vl)
+            self.step.run_dev(self.gen, self.q_pre, self.q, self.kr, self.vr, self.kidx, self.w_q, k_loc=self.kl,
+                              v_loc=self.vl)
+        pair()
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            pair()
+        torch.cuda.synchronize()
+
+    def run_graph(self):
+        self.gen.fill_(self.n0)
+        for _ in range(self.T):
+            self.graph.replay()
+
 
 # ----------------------------------------------------------------------------- prefill
 class PrefillBench:
@@ -410,6 +436,40 @@ def cpu_baseline_prefill(max_rows_per_head: int = 64):
                       "1 thread", "cores": 1}
 
 
+def selection_rows(args):
+    """rtp_topp_select alone on two 1M-token score rows: a peaked row (scores N(0, 3^2)) and a
+    near-flat one (5 + 1e-3 N(0,1)), where many tokens share the threshold's upper key bits and
+    every selection tile holds more distinct candidates than its record keeps."""
+    import torch
+    from head_wise_sparse_amd import rtp
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    n = 1 << 20
+    rng = np.random.default_rng(3)
+    rows = {"peaked": (rng.standard_normal(n) * 3).astype(np.float32),
+            "near_flat": (5 + rng.standard_normal(n) * 1e-3).astype(np.float32)}
+    L = rtp.Layer(1, 1, 1, 128, n, [1], 0, 1)
+    out = {}
+    for name, r in rows.items():
+        sc = torch.from_numpy(r).cuda()
+        m = torch.tensor([float(r.max())], device="cuda")
+        z = torch.tensor([float(np.exp(r.astype(np.float64) - r.max()).sum())], device="cuda")
+        sel = torch.empty(n, dtype=torch.int32, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        ws = rtp.workspace(L, n, rtp.CALL_TOPP_SELECT)
+        for _ in range(3):
+            rtp.rtp_topp_select(L, n, sc, m, z, 0.95, sel, cnt, None, ws)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(args.steps):
+            rtp.rtp_topp_select(L, n, sc, m, z, 0.95, sel, cnt, None, ws)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = {"us_per_call": round(a.elapsed_time(b) / args.steps * 1e3, 2), "selected": int(cnt.item())}
+        log(f"selection 1M {name}: {out[name]}")
+    return out
+
+
 def report_configs(args):
     """Per-config timings (not the headline line): the fused decode step of every decode
     workload at its p, and the chunked prefill of both prefill workloads."""
@@ -441,6 +501,7 @@ def report_configs(args):
         log(f"{name}: {us:.1f} us/step")
         del dec
         torch.cuda.empty_cache()
+    out["selection_rows"] = selection_rows(args)
     for name, qd, passes in (("prefill_32k", 0, args.steps), ("prefill_1m", 4, 2)):
         pre = PrefillBench(name, qd)
         pre.run()
@@ -609,6 +670,8 @@ def main():
         del buf
     if dec and args.gen_steps > 0:
         gen = GenBench(dec, args.gen_steps)
+        gen.capture()
+        gen.run_graph()                      # warm-up of the graph path
         gen.run()                            # warm-up (re-appending the same tokens is idempotent)
         torch.cuda.synchronize()
         a, b = ev(), ev()
@@ -617,11 +680,23 @@ def main():
         b.record()
         torch.cuda.synchronize()
         us_tok = a.elapsed_time(b) / gen.T * 1e3
+        a, b = ev(), ev()
+        a.record()
+        gen.run_graph()
+        b.record()
+        torch.cuda.synchronize()
+        us_tok_graph = a.elapsed_time(b) / gen.T * 1e3
+        gen.run()                            # restore the generated tokens' cache rows
+        torch.cuda.synchronize()
         res["generation"] = {
             "workload": f"{gen.T} tokens generated from {gen.n0} to {gen.n0 + gen.T}, batch {dec.cfg.batch}, "
                         "compact KV (retrieval heads: whole history; local heads: sinks + window ring), "
-                        "append + fused decode step per token, launched eagerly",
+                        "append + fused decode step per token",
             "us_per_token_per_layer": round(us_tok, 2),
+            "launch": "eager (host context length per token)",
+            "graph_us_per_token_per_layer": round(us_tok_graph, 2),
+            "graph": "one captured graph of rtp_append_token_dev + rtp_decode_step_dev replayed per token "
+                     "(context length in device memory)",
             "kv_bytes_full_layout": gen.full_bytes, "kv_bytes_compact_layout": gen.compact_bytes,
             "memory_sparsity": round(1 - gen.compact_bytes / gen.full_bytes, 4)}
         del gen

@@ -45,10 +45,13 @@ struct DecArgs {
   const int32_t* sel_idx;     // sparse only
   const int32_t* starts;      // sparse only: [rows][nsplit + 1]
   float* part;                // [rows][nsplit * nsub][D + 4]: accumulator, max, sum (16-byte rows)
-  int n_ctx;
+  int n_ctx;                  // the context (device-length step: its bound n_max)
+  const int64_t* live;        // device-length step: the context's device word, else null
+  int n_sinks, window;        // window path: the layer's sinks and window (live list bounds)
   int64_t n_cap;
   int Hq, Hkv;
-  int nsplit;                 // sparse: index ranges (row stride of `starts` is nsplit + 1); window: slices
+  int nsplit;                 // sparse: index ranges of n_ctx (row stride of `starts` is nsplit + 1);
+                              // window: slices of the bound's list (the partials' row stride)
   int nsub;                   // sparse: blocks per range, each taking one slice of its union list
   int wrange;                 // window: list positions per block
   float scale_log2;           // sm_scale * log2(e)
@@ -80,6 +83,17 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
   const int lg = wave * TPW + lane / LPT;
   const int li = lane % LPT;
   const int b = grp / a.map.n, rr = grp % a.map.n, g = a.map.kv[rr];
+  // the live context: its length, and (window path) its sink + window list.  Slices and
+  // ranges past it write empty partials, which add exact zeros in the merge.
+  const int n_ctx = live_ctx(a.live, a.n_ctx);
+  int s_end = a.s_end, w_start = a.w_start, list_len = a.list_len, ring_off = a.ring_off;
+  if (!SPARSE && a.live) {
+    s_end = min(a.n_sinks, n_ctx);
+    w_start = max(n_ctx - a.window, s_end);
+    list_len = s_end + (n_ctx - w_start);
+    ring_off = (a.ring_w > 0 && w_start >= a.ring_s) ? (w_start - a.ring_s) % a.ring_w : 0;
+  }
+  const int nsplit_live = SPARSE ? (n_ctx + RANGE - 1) / RANGE : a.nsplit;
   const int64_t head_off = (int64_t(b) * a.cache_heads + (a.by_rank ? rr : g)) * a.cache_rows * D + li * 8;
   const uint16_t* kb = a.k + head_off;
   const uint16_t* vb = a.v + head_off;
@@ -114,9 +128,9 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
 #pragma unroll
     for (int t = 0; t < G; ++t) {
       const int64_t so = int64_t(grp * G + t) * (a.nsplit + 1) + split;
-      // clamped: the range index may come from the caller
-      hi[t] = min(max(a.starts[so + 1], 0), a.n_ctx);
-      lo[t] = min(max(a.starts[so], 0), hi[t]);
+      // clamped: the range index may come from the caller; a range past the live context is empty
+      hi[t] = split < nsplit_live ? min(max(a.starts[so + 1], 0), n_ctx) : 0;
+      lo[t] = split < nsplit_live ? min(max(a.starts[so], 0), hi[t]) : 0;
     }
     int pos[G][SP];
 #pragma unroll
@@ -130,7 +144,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
         const int v = sr[k < hi[t] ? k : 0];
         // an index outside [0, n_ctx) (a malformed list from the caller) is dropped, so no
         // cache row at or past n_ctx is ever read
-        pos[t][u] = (k < hi[t] && v >= 0 && v < a.n_ctx) ? v - j0 : -1;
+        pos[t][u] = (k < hi[t] && v >= 0 && v < n_ctx) ? v - j0 : -1;
       }
     }
 #pragma unroll
@@ -185,7 +199,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
     }
   } else {
     p0 = split * a.wrange;
-    U = min(a.wrange, a.list_len - p0);
+    U = min(a.wrange, list_len - p0);
   }
 
   float m[G], l[G], acc[G][8];
@@ -204,13 +218,13 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
     } else {
       mask = (1u << G) - 1u;
       const int p = p0 + e;
-      if (p < a.s_end) return int64_t(p);
+      if (p < s_end) return int64_t(p);
       if (a.ring_w > 0) {                      // window token w_start + (p - s_end) in the ring
-        int t = a.ring_off + (p - a.s_end);    // < 2 * ring_w: the window holds at most ring_w tokens
+        int t = ring_off + (p - s_end);        // < 2 * ring_w: the window holds at most ring_w tokens
         if (t >= a.ring_w) t -= a.ring_w;
         return int64_t(a.ring_s) + t;
       }
-      return int64_t(a.w_start) + (p - a.s_end);
+      return int64_t(w_start) + (p - s_end);
     }
   };
 

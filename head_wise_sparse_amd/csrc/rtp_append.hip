@@ -16,6 +16,8 @@ namespace {
 
 struct AppendArgs {
   int64_t pos;
+  int64_t* gen;                // device-length variant: {pos, n_ctx} (pos read here, n_ctx = pos + 1 written)
+  int64_t n_sinks, window;
   const uint16_t* k_new;       // [B][Hkv][D]
   const uint16_t* v_new;
   const uint16_t* k_pre;       // [B][Hkv][D]
@@ -40,16 +42,23 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
   const bool ret = a.role[g];
   const int r = a.rank[g];
   const int64_t src = (int64_t(b) * a.Hkv + g) * a.D;
+  int64_t pos = a.pos, loc_row = a.loc_row;
+  if (a.gen) {               // the position from the generation state; the next decode sees pos + 1
+    pos = a.gen[0];
+    if (g == 0 && b == 0 && lane == 0) a.gen[1] = pos + 1 < 1 ? 1 : (pos + 1 > a.n_cap ? a.n_cap : pos + 1);
+    if (pos < 0 || pos >= a.n_cap) return;                 // outside the cache: nothing is written
+    loc_row = pos < a.n_sinks ? pos : a.n_sinks + (pos - a.n_sinks) % a.window;
+  }
   uint16_t *kd, *vd;
   if (!a.compact) {
-    kd = a.k_ret + ((int64_t(b) * a.Hkv + g) * a.n_cap + a.pos) * a.D;
-    vd = a.v_ret + ((int64_t(b) * a.Hkv + g) * a.n_cap + a.pos) * a.D;
+    kd = a.k_ret + ((int64_t(b) * a.Hkv + g) * a.n_cap + pos) * a.D;
+    vd = a.v_ret + ((int64_t(b) * a.Hkv + g) * a.n_cap + pos) * a.D;
   } else if (ret) {
-    kd = a.k_ret + ((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.D;
-    vd = a.v_ret + ((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.D;
+    kd = a.k_ret + ((int64_t(b) * a.n_ret + r) * a.n_cap + pos) * a.D;
+    vd = a.v_ret + ((int64_t(b) * a.n_ret + r) * a.n_cap + pos) * a.D;
   } else {
-    kd = a.k_loc + ((int64_t(b) * a.n_loc + r) * a.ring_rows + a.loc_row) * a.D;
-    vd = a.v_loc + ((int64_t(b) * a.n_loc + r) * a.ring_rows + a.loc_row) * a.D;
+    kd = a.k_loc + ((int64_t(b) * a.n_loc + r) * a.ring_rows + loc_row) * a.D;
+    vd = a.v_loc + ((int64_t(b) * a.n_loc + r) * a.ring_rows + loc_row) * a.D;
   }
   const int nv = a.D / 8;                  // 16-byte pieces per row
   if (lane < nv) {
@@ -75,21 +84,25 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
   float acc = 0.0f;
   for (int d = part; d < a.D; d += lpo) acc = fmaf(bf16_to_f32(kp[d]), bf16_to_f32(w[d * a.idx + c]), acc);
   for (int o = 1; o < lpo; o <<= 1) acc += __shfl_xor(acc, o, 64);
-  if (part == 0) a.k_idx[((int64_t(b) * a.n_ret + r) * a.n_cap + a.pos) * a.idx + c] = f32_to_bf16(acc);
+  if (part == 0) a.k_idx[((int64_t(b) * a.n_ret + r) * a.n_cap + pos) * a.idx + c] = f32_to_bf16(acc);
 }
 
 }  // namespace
 
-extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, const uint16_t* k_new,
-                                       const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx,
-                                       int64_t w_head_stride, uint16_t* k_cache, uint16_t* v_cache,
-                                       uint16_t* k_idx_cache, uint16_t* k_loc, uint16_t* v_loc, void* stream) {
+namespace {
+
+rtp_status append_impl(const rtp_layer_desc* desc, int64_t pos, int64_t* gen, const uint16_t* k_new,
+                       const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx, int64_t w_head_stride,
+                       uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache, uint16_t* k_loc,
+                       uint16_t* v_loc, void* stream) {
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;
-  if (pos < 0 || pos >= L.n_cap)
+  if (!gen && (pos < 0 || pos >= L.n_cap))
     return fail(RTP_EINVAL, "rtp_append_token: pos must be in [0, n_cap=%lld) (got %lld)", (long long)L.n_cap,
                 (long long)pos);
+  if (gen && !aligned(gen, 8))
+    return fail(RTP_EINVAL, "rtp_append_token_dev: the generation state must be 8-byte aligned");
   const bool compact = L.kv_layout == RTP_KV_COMPACT;
   if (!k_new || !v_new) return fail(RTP_EINVAL, "rtp_append_token: NULL tensor pointer");
   if ((L.n_ret || !compact) && (!k_cache || !v_cache)) return fail(RTP_EINVAL, "rtp_append_token: NULL cache");
@@ -103,6 +116,9 @@ extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, 
     return fail(RTP_EINVAL, "rtp_append_token: tensors must be 16-byte aligned");
   AppendArgs a{};
   a.pos = pos;
+  a.gen = gen;
+  a.n_sinks = L.n_sinks;
+  a.window = L.window;
   a.k_new = k_new;
   a.v_new = v_new;
   a.k_pre = k_pre;
@@ -122,7 +138,7 @@ extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, 
   a.compact = compact;
   const int64_t S = L.n_sinks, W = L.window;
   a.ring_rows = S + W;
-  a.loc_row = pos < S ? pos : S + (pos - S) % W;
+  a.loc_row = gen ? 0 : (pos < S ? pos : S + (pos - S) % W);
   for (int i = 0; i < L.n_ret; ++i) {
     a.rank[L.ret_kv[i]] = i;
     a.role[L.ret_kv[i]] = 1;
@@ -134,4 +150,23 @@ extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(k_append, dim3(L.Hkv, L.B), dim3(64), 0, s, a);
   return check_launch("k_append");
+}
+
+}  // namespace
+
+extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, const uint16_t* k_new,
+                                       const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx,
+                                       int64_t w_head_stride, uint16_t* k_cache, uint16_t* v_cache,
+                                       uint16_t* k_idx_cache, uint16_t* k_loc, uint16_t* v_loc, void* stream) {
+  return append_impl(desc, pos, nullptr, k_new, v_new, k_pre, w_k_idx, w_head_stride, k_cache, v_cache, k_idx_cache,
+                     k_loc, v_loc, stream);
+}
+
+extern "C" rtp_status rtp_append_token_dev(const rtp_layer_desc* desc, int64_t* gen, const uint16_t* k_new,
+                                           const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx,
+                                           int64_t w_head_stride, uint16_t* k_cache, uint16_t* v_cache,
+                                           uint16_t* k_idx_cache, uint16_t* k_loc, uint16_t* v_loc, void* stream) {
+  if (!gen) return fail(RTP_EINVAL, "rtp_append_token_dev: NULL generation state");
+  return append_impl(desc, 0, gen, k_new, v_new, k_pre, w_k_idx, w_head_stride, k_cache, v_cache, k_idx_cache, k_loc,
+                     v_loc, stream);
 }

@@ -62,12 +62,22 @@ size_t score_ws_bytes(const Layer& L, int64_t n_ctx);
 // 2^-23 at 2^20 tokens, 2^-15 at 2^24.  Top-p is refused above kTopPMaxCtx tokens, where
 // that bound would pass 1e-4.
 constexpr int64_t kTopPMaxCtx = int64_t(1) << 24;
-inline int mass_frac_bits(int64_t n_ctx) {
+__host__ __device__ inline int mass_frac_bits(int64_t n_ctx) {
   int c = 0;
   while ((int64_t(1) << c) < n_ctx) ++c;                        // ceil(log2(n_ctx))
   return 62 - c < 42 ? 62 - c : 42;
 }
-inline float mass_wscale(int64_t n_ctx) { return float(int64_t(1) << mass_frac_bits(n_ctx)); }
+__host__ __device__ inline float mass_wscale(int64_t n_ctx) { return float(int64_t(1) << mass_frac_bits(n_ctx)); }
+
+// Context length of a launch.  The calls take it from the host (live == null); the
+// device-length step reads it from a device word written by an earlier launch (live),
+// clamped to [1, n_max], where n_max is the host bound every stride and grid is sized
+// for.  With live == null the length is n_max itself, so both paths share the kernels.
+__device__ __forceinline__ int live_ctx(const int64_t* live, int n_max) {
+  if (!live) return n_max;
+  const int64_t v = *live;
+  return int(v < 1 ? 1 : (v > n_max ? int64_t(n_max) : v));
+}
 
 // Top-p selection (four launches; the workspace is zero before and after a call).
 constexpr int kSelThreads = 256;
@@ -110,10 +120,10 @@ struct SelArgs {
   float* row_max_out;            // with score_part: row statistics written by the first pass
   float* row_sum_out;
   float top_p;
-  float wscale;                  // 2^F of the fixed-point mass (mass_wscale(n_ctx); set by launch_select)
   int by_count;                  // static top-k: bins weigh their token counts, the target is k_target
   int64_t k_target;
-  int n_ctx;
+  int n_ctx;                     // the context (device-length step: its bound n_max)
+  const int64_t* live;           // device-length step: the context's device word, else null
   int64_t n_cap;
   int nblk;                      // selection tiles per row (from n_ctx; set by launch_select)
   int items;                     // scores per thread per tile (kSelItems or kSelItemsLong; set by launch_select)
@@ -121,7 +131,7 @@ struct SelArgs {
   int32_t* sel_idx;
   int32_t* sel_count;
   int32_t* starts;               // [rows][nsplit + 1] range index of the selected lists, or null
-  int nsplit;
+  int nsplit;                    // ranges of n_ctx (row stride of starts: nsplit + 1)
   SelRows R;
 };
 SelRows sel_rows(void* ws, const SelLayout& lay);

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_indexer_score(ScoreArgs A) {
 // One wave per score row: combine the per-block partials into (row_max, row_sum).
 __global__ __launch_bounds__(64) void k_score_finalize(const float2* __restrict__ part, int nblk,
                                                        float* __restrict__ row_max, float* __restrict__ row_sum) {
-  score_finalize_row(part, nblk, row_max, row_sum, blockIdx.x);
+  score_finalize_row(part, nblk, nblk, row_max, row_sum, blockIdx.x);
 }
 
 template <int G, int D, int IDX>
@@ -80,8 +80,8 @@ extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ct
   const dim3 grid(nblk, L.B * L.n_ret);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws);
-  const ScoreArgs A{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, int(n_ctx), L.n_cap, L.Hq,
-                    ret_map(L), nblk};
+  const ScoreArgs A{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, int(n_ctx), nullptr, L.n_cap,
+                    L.Hq, ret_map(L), nblk};
   bool launched = false;
   switch (L.idx) {
     case 4: launched = dispatch_score<4>(L, grid, s, A); break;

@@ -220,17 +220,18 @@ __device__ __forceinline__ void clear_level(const SelRows& R, int row, int level
 
 // Row max (and, by the first block, the row statistics) from the scoring's per-block
 // (max, sum of exp) partials.
-__device__ float row_max_from_partials(const SelArgs& a, int row, int blk, int tid, float* s_red) {
+__device__ float row_max_from_partials(const SelArgs& a, int row, int blk, int tid, float* s_red, int n_ctx) {
   const float2* p = a.score_part + int64_t(row) * a.score_nblk;
+  const int nb = (n_ctx + kScoreTile - 1) / kScoreTile;        // partials of the live context
   float m = -INFINITY;
-  for (int i = tid; i < a.score_nblk; i += kSelThreads) m = fmaxf(m, p[i].x);
+  for (int i = tid; i < nb; i += kSelThreads) m = fmaxf(m, p[i].x);
   m = wave_max(m);
   if ((tid & 63) == 0) s_red[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   // the row statistics, by the same one-wave reduction as rtp_indexer_score's
   if (blk == 0 && a.row_max_out && tid < 64)
-    score_finalize_row(a.score_part, a.score_nblk, a.row_max_out, a.row_sum_out, row);
+    score_finalize_row(a.score_part, a.score_nblk, nb, a.row_max_out, a.row_sum_out, row);
   return m;
 }
 
@@ -247,6 +248,10 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   __shared__ uint32_t s_prefix;
   __shared__ float s_red[kSelThreads / 64];
   __shared__ uint32_t s_na[kSelThreads / 64], s_np, s_pair[kRecPairs];   // level 2: tile record
+  const int n_ctx = live_ctx(a.live, a.n_ctx);
+  const int nblk = int((int64_t(n_ctx) + TILE - 1) / TILE);       // tiles of the live context
+  if (blk >= nblk) return;
+  const float wscale = mass_wscale(n_ctx);
 
   // scores of the tile: unconditional loads (index clamped), validity kept aside
   const float* sp = a.scores + int64_t(row) * a.n_cap;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
-    sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
+    sv[it] = sp[j < n_ctx ? j : n_ctx - 1];
   }
   for (int i = tid; i < NB; i += kSelThreads) {
     h_m[i] = 0;
@@ -264,12 +269,12 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   if (LEVEL == 2 && tid == 0) s_np = 0;
   float m = 0.0f;                                   // unused by the static top-k rule
   if constexpr (LEVEL == 0) {
-    if (!a.by_count) m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red) : a.row_max[row];
+    if (!a.by_count) m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red, n_ctx) : a.row_max[row];
     if (blk == 0 && tid == 0) a.R.state[row].ref_max = m;
   } else {
     m = a.R.state[row].ref_max;                      // written by the level-0 launch
   }
-  if constexpr (LEVEL == 2) clear_level(a.R, row, 0, blk, a.nblk);   // read last by hist<1>
+  if constexpr (LEVEL == 2) clear_level(a.R, row, 0, blk, nblk);   // read last by hist<1>
   if (LEVEL > 0 && tid < 64) {
     Resolved in{};
     if (LEVEL == 2) {
@@ -298,13 +303,13 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
     const uint32_t key = score_key(sv[it]);
-    const bool match = (j < a.n_ctx) && (LEVEL == 0 || (key >> PSHIFT) == prefix);
+    const bool match = (j < n_ctx) && (LEVEL == 0 || (key >> PSHIFT) == prefix);
     if (match) {
       const uint32_t d = (key >> SHIFT) & uint32_t(NB - 1);
-      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m, a.wscale));
+      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m, wscale));
       atomicAdd(&h_c[d], 1u);
     }
-    if constexpr (LEVEL == 2) n_above += uint32_t((j < a.n_ctx) && (key >> PSHIFT) > prefix);
+    if constexpr (LEVEL == 2) n_above += uint32_t((j < n_ctx) && (key >> PSHIFT) > prefix);
   }
   if constexpr (LEVEL == 2) {
     n_above = wave_sum(n_above);
@@ -371,6 +376,11 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   __shared__ uint32_t s_pa, s_pe, s_heavy, s_last;
   __shared__ uint32_t s_ra[NW], s_re[NW];
   __shared__ uint32_t s_heavy_list[kMaxHeavy];
+  const int n_ctx = live_ctx(a.live, a.n_ctx);
+  const int nblk = int((int64_t(n_ctx) + TILE - 1) / TILE);       // tiles of the live context
+  if (tile >= nblk) return;
+  const int nsplit = (n_ctx + kDecRange - 1) / kDecRange;         // ranges of the live context
+  const float wscale = mass_wscale(n_ctx);
   uint32_t* ctr = a.R.ctr + 2 * int64_t(row);
   const uint4* rec = a.R.tilerec + int64_t(row) * a.rec_stride;
   const float* sp = a.scores + int64_t(row) * a.n_cap;
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
-    sv[it] = sp[j < a.n_ctx ? j : a.n_ctx - 1];
+    sv[it] = sp[j < n_ctx ? j : n_ctx - 1];
   }
   uint4 rec0 = make_uint4(0u, 0u, 0u, 0u);           // records of the first 64 earlier tiles
   if (wave == 1 && lane < tile) rec0 = rec[lane];
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     if (lane == 0) {
       // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
       s_t = o.prefix;
-      const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(o.prefix), a.R.state[row].ref_max, a.wscale);
+      const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(o.prefix), a.R.state[row].ref_max, wscale);
       const uint64_t rem = o.target - o.above;
       uint64_t r = (w == 0) ? o.tied : (rem + w - 1) / w;
       if (r < 1) r = 1;
@@ -403,12 +413,12 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
       if (tile == 0) {
         const uint32_t cnt = o.cnt_above + uint32_t(r);
         a.sel_count[row] = int32_t(cnt);
-        if (a.starts) a.starts[int64_t(row) * (a.nsplit + 1) + a.nsplit] = int32_t(cnt);
+        if (a.starts) a.starts[int64_t(row) * (a.nsplit + 1) + nsplit] = int32_t(cnt);
       }
     }
   }
   __syncthreads();
-  clear_level(a.R, row, 1, tile, a.nblk);             // read last by hist<2>
+  clear_level(a.R, row, 1, tile, nblk);             // read last by hist<2>
   const uint32_t t = s_t, r = s_r;
   // ---- tokens of earlier tiles with key > t (pa) and key == t (pe), from their records;
   // tiles whose record overflowed ("heavy") are listed and counted from their scores
@@ -452,7 +462,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
     const uint32_t key = score_key(sv[it]);
-    const bool above = (j < a.n_ctx) && key > t, tied = (j < a.n_ctx) && key == t;
+    const bool above = (j < n_ctx) && key > t, tied = (j < n_ctx) && key == t;
     fa |= uint32_t(above) << it;
     fe |= uint32_t(tied) << it;
     const uint64_t ba = __ballot(above), be = __ballot(tied);
@@ -547,7 +557,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     if (a.starts && it % IT_PER_RANGE == 0 && tid == 0) {
       // first token of a decode range: the number of selected tokens before it
       const int64_t q = (base + it * kSelThreads) / kDecRange;
-      if (q < a.nsplit) a.starts[int64_t(row) * (a.nsplit + 1) + q] = int32_t(ca + (ce < r ? ce : r));
+      if (q < nsplit) a.starts[int64_t(row) * (a.nsplit + 1) + q] = int32_t(ca + (ce < r ? ce : r));
     }
     const bool above = (fa >> it) & 1u, tied = (fe >> it) & 1u;
     const uint32_t a_before = ca + __popcll(__ballot(above) & lt);
@@ -557,10 +567,10 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   }
   // the last block of the row to be counted clears what this launch read: every other
   // block has finished its reads of the tile records, the level-2 histogram and the state
-  if (tid == 0) s_last = (done_before == uint32_t(a.nblk - 1));
+  if (tid == 0) s_last = (done_before == uint32_t(nblk - 1));
   __syncthreads();
   if (s_last) {
-    for (int i = tid; i < a.nblk; i += kSelThreads) a.R.tilerec[int64_t(row) * a.rec_stride + i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < nblk; i += kSelThreads) a.R.tilerec[int64_t(row) * a.rec_stride + i] = make_uint4(0u, 0u, 0u, 0u);
     uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
     if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
     clear_level(a.R, row, 2, 0, 1);
@@ -572,14 +582,17 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
 }
 
 // top_p >= 1: every token, in order.
-__global__ __launch_bounds__(256) void k_sel_all(int n_ctx, int64_t n_cap, int32_t* __restrict__ sel_idx,
-                                                 int32_t* __restrict__ sel_count, int32_t* __restrict__ starts,
-                                                 int nsplit) {
+// (nsplit: the range index's row stride - 1; live: the device-length step's context word)
+__global__ __launch_bounds__(256) void k_sel_all(int n_max, const int64_t* live, int64_t n_cap,
+                                                 int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
+                                                 int32_t* __restrict__ starts, int nsplit) {
   const int row = blockIdx.y;
+  const int n_ctx = live_ctx(live, n_max);
+  const int nl = (n_ctx + kDecRange - 1) / kDecRange;
   const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (j < n_ctx) sel_idx[int64_t(row) * n_cap + j] = int32_t(j);
   if (j == 0) sel_count[row] = n_ctx;
-  if (starts && j <= nsplit) starts[int64_t(row) * (nsplit + 1) + j] = int32_t(j == nsplit ? n_ctx : j * kDecRange);
+  if (starts && j <= nl) starts[int64_t(row) * (nsplit + 1) + j] = int32_t(j == nl ? n_ctx : j * kDecRange);
 }
 
 }  // namespace
@@ -622,7 +635,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   const int nsplit = int((n_ctx + kDecRange - 1) / kDecRange);
   if (top_p >= 1.0f) {
     hipLaunchKernelGGL(k_sel_all, dim3(unsigned((n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, int(n_ctx),
-                       L.n_cap, sel_idx, sel_count, sel_starts, nsplit);
+                       nullptr, L.n_cap, sel_idx, sel_count, sel_starts, nsplit);
     return check_launch("k_sel_all");
   }
   SelArgs a{};
@@ -682,12 +695,11 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
   const SelArgs& a = a0;
   if (a.top_p >= 1.0f) {
     hipLaunchKernelGGL(k_sel_all, dim3(unsigned((a.n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, a.n_ctx,
-                       a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
+                       a.live, a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
     return check_launch("k_sel_all");
   }
   // tile size: 16 scores per thread, or 32 when that keeps a pass to one round of blocks
   SelArgs b = a;
-  b.wscale = mass_wscale(a.n_ctx);
   const int64_t nblk16 = (int64_t(a.n_ctx) + kSelTile - 1) / kSelTile;
   b.items = nblk16 * rows > kDecBlocksTarget ? kSelItemsLong : kSelItems;
   b.nblk = int((int64_t(a.n_ctx) + kSelThreads * b.items - 1) / (kSelThreads * b.items));

@@ -46,16 +46,21 @@ __global__ __launch_bounds__(256) void k_step_merge_pre(MergeArgs ms, float* par
   merge_pre_chunk<D>(ms, part2, nchunks, blockIdx.y, blockIdx.x);
 }
 
+// gen: the device-length step's state {pos, n_ctx}; the last launch of the step moves pos
+// to n_ctx (no launch of the step reads pos), so the next append writes the next token.
 template <int D>
-__global__ __launch_bounds__(256) void k_step_merge(MergeArgs ms, int rows_s, MergeArgs mw) {
+__global__ __launch_bounds__(256) void k_step_merge(MergeArgs ms, int rows_s, MergeArgs mw, int64_t* gen) {
   const int i = blockIdx.x;
   if (i < rows_s) merge_row<D>(ms, i);
   else merge_row<D>(mw, i - rows_s);
+  if (gen && i == 0 && threadIdx.x == 0) gen[0] = gen[1];
 }
 
-__global__ __launch_bounds__(64) void k_step_finalize(const float2* __restrict__ part, int nblk,
-                                                      float* __restrict__ row_max, float* __restrict__ row_sum) {
-  score_finalize_row(part, nblk, row_max, row_sum, blockIdx.x);
+__global__ __launch_bounds__(64) void k_step_finalize(const float2* __restrict__ part, int stride, int n_max,
+                                                      const int64_t* live, float* __restrict__ row_max,
+                                                      float* __restrict__ row_sum) {
+  const int n = live_ctx(live, n_max);
+  score_finalize_row(part, stride, (n + kScoreTile - 1) / kScoreTile, row_max, row_sum, blockIdx.x);
 }
 
 struct StepLayout {
@@ -137,7 +142,10 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
                             float top_p, float sm_scale, float* scores,
                             float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
                             int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
-                            void* stream, bool clear_sel) {
+                            void* stream, bool clear_sel, int64_t* gen = nullptr) {
+  // gen (device-length step): n_ctx is the bound every grid and stride is sized for, and
+  // the live length is gen[1]
+  const int64_t* live = gen ? gen + 1 : nullptr;
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;
@@ -193,7 +201,7 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     score_gx = int((n_ctx + kScoreTile - 1) / kScoreTile);
     n_score = score_gx * L.B * L.n_ret;
     sa = ScoreArgs{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, reinterpret_cast<float2*>(w + lay.score),
-                   n, L.n_cap, L.Hq, ret_map(L), score_gx};
+                   n, live, L.n_cap, L.Hq, ret_map(L), score_gx};
   }
   DecArgs wa{};
   int win_gx = 1, n_win = 0;
@@ -209,6 +217,9 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     wa.v = v_cache;
     wa.part = reinterpret_cast<float*>(w + lay.window);
     wa.n_ctx = n;
+    wa.live = live;
+    wa.n_sinks = L.n_sinks;
+    wa.window = L.window;
     wa.n_cap = L.n_cap;
     wa.Hq = L.Hq;
     wa.Hkv = L.Hkv;
@@ -241,6 +252,7 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     a.row_sum_out = row_sum;
     a.top_p = top_p;
     a.n_ctx = n;
+    a.live = live;
     a.n_cap = L.n_cap;
       a.rec_stride = sl.nblk_max;
     a.sel_idx = sel_idx;
@@ -249,7 +261,8 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     a.nsplit = nsplit;
     a.R = sel_rows(w + lay.sel, sl);
     if (top_p >= 1.0f) {           // no radix pass runs: reduce the partials here
-      hipLaunchKernelGGL(k_step_finalize, dim3(rows_s), dim3(64), 0, s, sa.part, score_gx, row_max, row_sum);
+      hipLaunchKernelGGL(k_step_finalize, dim3(rows_s), dim3(64), 0, s, sa.part, score_gx, n, live, row_max,
+                         row_sum);
       if ((st = check_launch("k_step_finalize")) != RTP_OK) return st;
     }
     if ((st = launch_select(a, rows_s, s)) != RTP_OK) return st;
@@ -263,6 +276,7 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     da.starts = starts;
     da.part = reinterpret_cast<float*>(w + lay.sparse);
     da.n_ctx = n;
+    da.live = live;
     da.n_cap = L.n_cap;
     da.Hq = L.Hq;
     da.Hkv = L.Hkv;
@@ -292,9 +306,9 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
   const unsigned mrows = unsigned((L.n_ret ? rows_s : 0) + (L.n_loc ? rows_w : 0));
   const int rs = L.n_ret ? rows_s : 0;
   if (L.D == 128)
-    hipLaunchKernelGGL(k_step_merge<128>, dim3(mrows), dim3(256), 0, s, ms, rs, mw);
+    hipLaunchKernelGGL(k_step_merge<128>, dim3(mrows), dim3(256), 0, s, ms, rs, mw, gen);
   else
-    hipLaunchKernelGGL(k_step_merge<64>, dim3(mrows), dim3(256), 0, s, ms, rs, mw);
+    hipLaunchKernelGGL(k_step_merge<64>, dim3(mrows), dim3(256), 0, s, ms, rs, mw, gen);
   return check_launch("k_step_merge");
 }
 
@@ -311,6 +325,22 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
   return decode_step_impl(desc, n_ctx, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,
                           v_loc, top_p, sm_scale, scores, row_max, row_sum, sel_idx, sel_count, sel_starts, out, ws,
                           ws_bytes, stream, false);
+}
+
+// ---------------------------------------------------------------- device-length variant
+extern "C" rtp_status rtp_decode_step_dev(const rtp_layer_desc* desc, int64_t n_max, int64_t* gen,
+                                          const uint16_t* q_pre, const uint16_t* w_q_idx, int64_t w_head_stride,
+                                          const uint16_t* k_idx, float idx_scale, const uint16_t* q,
+                                          const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_loc,
+                                          const uint16_t* v_loc, float top_p, float sm_scale, float* scores,
+                                          float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
+                                          int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  if (!gen) return fail(RTP_EINVAL, "rtp_decode_step_dev: NULL generation state");
+  if (!aligned(gen, 8)) return fail(RTP_EINVAL, "rtp_decode_step_dev: the generation state must be 8-byte aligned");
+  return decode_step_impl(desc, n_max, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,
+                          v_loc, top_p, sm_scale, scores, row_max, row_sum, sel_idx, sel_count, sel_starts, out, ws,
+                          ws_bytes, stream, false, gen);
 }
 
 // ---------------------------------------------------------------- allocation-free variant

@@ -17,11 +17,12 @@ struct ScoreArgs {
   float idx_scale;
   float* scores;               // [B][Hq_r][n_cap]
   float2* part;                // [B][Hq_r][nblk] per-block (max, sum of exp)
-  int n_ctx;
+  int n_ctx;                   // the context (device-length step: its bound)
+  const int64_t* live;         // device-length step: the context's device word, else null
   int64_t n_cap;
   int Hq;
   HeadMap map;
-  int nblk;
+  int nblk;                    // tiles of n_ctx: the row stride of `part`
 };
 
 // One block of the indexer scoring: token tile `blk` of group `grp` (= b * n_ret + r),
@@ -38,7 +39,8 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
   const float idx_scale = A.idx_scale;
   float* __restrict__ scores = A.scores;
   float2* __restrict__ part = A.part;
-  const int n_ctx = A.n_ctx;
+  const int n_ctx = live_ctx(A.live, A.n_ctx);
+  if (int64_t(blk) * TILE >= n_ctx) return;              // a tile past the live context
   const int64_t n_cap = A.n_cap;
   const int Hq = A.Hq;
   const HeadMap& map = A.map;
@@ -194,12 +196,13 @@ __device__ __forceinline__ void score_block(const ScoreArgs& A, int blk, int grp
   }
 }
 
-// One wave: combine the per-block partials of score row `row` into (row_max, row_sum).
-__device__ __forceinline__ void score_finalize_row(const float2* __restrict__ part, int nblk,
+// One wave: combine the first nblk per-block partials of score row `row` (rows `stride`
+// apart) into (row_max, row_sum).
+__device__ __forceinline__ void score_finalize_row(const float2* __restrict__ part, int stride, int nblk,
                                                    float* __restrict__ row_max, float* __restrict__ row_sum,
                                                    int row) {
   const int lane = threadIdx.x & 63;
-  const float2* p = part + int64_t(row) * nblk;
+  const float2* p = part + int64_t(row) * stride;
   float m = -INFINITY;
   for (int i = lane; i < nblk; i += 64) m = fmaxf(m, p[i].x);
   m = wave_max(m);

@@ -26,7 +26,8 @@ KV_FULL, KV_COMPACT = 0, 1
 EXPORTED = ["rtp_workspace_bytes", "rtp_indexer_score", "rtp_topp_select", "rtp_sparse_decode_attn",
             "rtp_window_sink_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_topk_select", "rtp_append_token",
             "rtp_hbm_read_probe", "rtp_mfma_probe", "rtp_status_string", "rtp_last_error", "rtp_version",
-            "rtp_decode_step_noalloc", "rtp_decode_step_noalloc_max_bytes"]
+            "rtp_decode_step_noalloc", "rtp_decode_step_noalloc_max_bytes", "rtp_append_token_dev",
+            "rtp_decode_step_dev"]
 
 
 class RtpError(RuntimeError):
@@ -71,6 +72,9 @@ def load() -> C.CDLL:
         "rtp_decode_step_noalloc": (C.c_int, [D, C.c_int64, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, _P, _P,
                                               C.c_float, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
         "rtp_decode_step_noalloc_max_bytes": (C.c_size_t, []),
+        "rtp_decode_step_dev": (C.c_int, [D, C.c_int64, _P, _P, _P, C.c_int64, _P, C.c_float, _P, _P, _P, _P, _P,
+                                          C.c_float, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+        "rtp_append_token_dev": (C.c_int, [D, _P, _P, _P, _P, _P, C.c_int64, _P, _P, _P, _P, _P, _P]),
         "rtp_append_token": (C.c_int, [D, C.c_int64, _P, _P, _P, _P, C.c_int64, _P, _P, _P, _P, _P, _P]),
         "rtp_topk_select": (C.c_int, [D, C.c_int64, _P, C.c_int64, _P, _P, _P, _P, C.c_size_t, _P]),
         "rtp_hbm_read_probe": (C.c_int, [_P, C.c_size_t, _P, _P]),
@@ -233,6 +237,24 @@ def rtp_decode_step_noalloc(layer: Layer, n_ctx: int, q_pre, w_q_idx, w_head_str
                                           _ptr(sel_starts), _ptr(out), _stream(stream)))
 
 
+def rtp_decode_step_dev(layer: Layer, n_max: int, gen, q_pre, w_q_idx, w_head_stride: int, k_idx, idx_scale: float,
+                        q, k_cache, v_cache, k_loc, v_loc, top_p: float, sm_scale: float, scores, row_max, row_sum,
+                        sel_idx, sel_count, sel_starts, out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(load().rtp_decode_step_dev(layer.desc, int(n_max), _ptr(gen), _ptr(q_pre), _ptr(w_q_idx),
+                                      int(w_head_stride), _ptr(k_idx), float(idx_scale), _ptr(q), _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(k_loc), _ptr(v_loc), float(top_p), float(sm_scale),
+                                      _ptr(scores), _ptr(row_max), _ptr(row_sum), _ptr(sel_idx), _ptr(sel_count),
+                                      _ptr(sel_starts), _ptr(out), p, n, _stream(stream)))
+
+
+def rtp_append_token_dev(layer: Layer, gen, k_new, v_new, k_pre, w_k_idx, w_head_stride: int, k_cache, v_cache,
+                         k_idx_cache, k_loc=None, v_loc=None, stream=None):
+    _check(load().rtp_append_token_dev(layer.desc, _ptr(gen), _ptr(k_new), _ptr(v_new), _ptr(k_pre), _ptr(w_k_idx),
+                                       int(w_head_stride), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache),
+                                       _ptr(k_loc), _ptr(v_loc), _stream(stream)))
+
+
 def rtp_decode_step_noalloc_max_bytes() -> int:
     return int(load().rtp_decode_step_noalloc_max_bytes())
 
@@ -321,4 +343,17 @@ class DecodeStep:
         compact = L.kv_layout == KV_COMPACT
         rtp_window_sink_attn(L, n, q, k_loc if compact else k_cache, v_loc if compact else v_cache, self.sm_scale,
                              self.out, self.ws[CALL_WINDOW_SINK], stream)
+        return self.out
+
+    def run_dev(self, gen, q_pre, q, k_cache, v_cache, k_idx, w_q_idx, w_head_stride: Optional[int] = None,
+                stream=None, k_loc=None, v_loc=None):
+        """The fused step with the context length read from the device state `gen` (int64
+        {pos, n_ctx}); grids and strides are sized for this object's n_ctx (the bound)."""
+        L = self.layer
+        if w_head_stride is None:
+            w_head_stride = L.head_dim * L.idx_dim
+        rtp_decode_step_dev(L, self.n_ctx, gen, q_pre, w_q_idx, w_head_stride, k_idx, self.idx_scale, q, k_cache,
+                            v_cache, k_loc, v_loc, self.top_p, self.sm_scale, self.scores, self.row_max,
+                            self.row_sum, self.sel_idx, self.sel_count, self.sel_starts, self.out,
+                            self.ws[CALL_DECODE_STEP], stream)
         return self.out

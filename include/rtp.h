@@ -286,6 +286,46 @@ rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Growing-context generation with the context length on the device, so that one
+ * captured HIP graph of [rtp_append_token_dev, rtp_decode_step_dev] serves every new
+ * token (a long generation grows the retrieval heads' context by one token per step;
+ * abstract: full KV kept for retrieval heads; summary, "Experimental setup": long
+ * reasoning outputs).
+ *
+ * gen: int64_t[2] in DEVICE memory, {pos, n_ctx}, 8-byte aligned, caller-owned:
+ *   rtp_append_token_dev stores the token at position gen[0] exactly as
+ *   rtp_append_token(pos = gen[0]) does and sets gen[1] = gen[0] + 1 (clamped to
+ *   [1, n_cap]; a position outside [0, n_cap) writes nothing);
+ *   rtp_decode_step_dev computes exactly what rtp_decode_step computes for
+ *   n_ctx = gen[1] (clamped to [1, n_max]) and, in its last launch, sets
+ *   gen[0] = gen[1].
+ * A replay of the pair therefore appends the next token and decodes over it.  The
+ * caller writes the new token's k/v/k_pre into the same buffers before each replay.
+ *
+ * rtp_decode_step_dev: n_max is the longest context the call will see (the grids,
+ * strides and workspace are sized for it: rtp_workspace_bytes(desc, n_max,
+ * RTP_CALL_DECODE_STEP)); the other arguments are rtp_decode_step's.  sel_starts rows
+ * are n_max's (row stride ceil(n_max / RTP_SEL_RANGE) + 1; entry ceil(n_ctx /
+ * RTP_SEL_RANGE) holds the count).  Where the layout of the split partials differs
+ * between n_max and n_ctx (window lists shorter than the window, or selection tiles of
+ * another size), the outputs can differ from rtp_decode_step's in rounding only.
+ */
+rtp_status rtp_append_token_dev(const rtp_layer_desc* desc, int64_t* gen,
+                                const uint16_t* k_new, const uint16_t* v_new, const uint16_t* k_pre,
+                                const uint16_t* w_k_idx, int64_t w_head_stride,
+                                uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache,
+                                uint16_t* k_loc, uint16_t* v_loc, void* stream);
+rtp_status rtp_decode_step_dev(const rtp_layer_desc* desc, int64_t n_max, int64_t* gen,
+                               const uint16_t* q_pre, const uint16_t* w_q_idx, int64_t w_head_stride,
+                               const uint16_t* k_idx, float idx_scale,
+                               const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                               const uint16_t* k_loc, const uint16_t* v_loc,
+                               float top_p, float sm_scale,
+                               float* scores, float* row_max, float* row_sum,
+                               int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts,
+                               uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * rtp_decode_step_noalloc -- rtp_decode_step for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same launches, arguments and results bit for bit, with the workspace

@@ -831,3 +831,113 @@ def test_decode_step_other_indexer_dims(idx_dim):
     assert same_all >= 0.9 * B * R
     loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
     P.check_outputs(g[:, loc], ora["out"][:, loc], "local rows")
+
+
+# ----------------------------------------------------------------------------- long generation (device length)
+def _check_step_against_oracle(x, cfg, n, k_full, v_full, kidx, out_bits, sel, cnt, gsc, p, what):
+    """Every row of a decode step at context n against the oracle on the given caches."""
+    B, G = cfg.batch, cfg.group
+    R = cfg.n_kv_r * G
+    ora = O.decode_step(x.q_pre, x.q, k_full, v_full, kidx, x.w_q_idx, x.kv_role, n, p, cfg.n_sinks, cfg.window)
+    ob = np.asarray(out_bits).reshape(B, cfg.n_q_heads, cfg.head_dim)
+    xs = type("X", (), {})()
+    xs.cfg, xs.q, xs.k, xs.v = cfg, x.q, k_full, v_full
+    same_all = 0
+    for b in range(B):
+        for ci in range(R):
+            r = ci // G
+            s_g = sel[b, ci, :cnt[b, ci]]
+            P.check_prefix(s_g, gsc[b, ci, :n], f"{what} row ({b},{ci})")
+            qi = O.indexer_query(O.bf16_to_f64(x.q_pre[b, cfg.retrieval_kv[r] * G + ci % G]),
+                                 O.bf16_to_f64(x.w_q_idx[ci]))
+            scale = np.abs(O.bf16_to_f64(kidx[b, r, :n])) @ np.abs(qi)
+            same, _ = P.check_set(s_g, ora["info"][(b, ci)], p, ora["scores"][(b, ci)], P.FP32_SCORE_SLACK * scale)
+            h = cfg.retrieval_kv[r] * G + ci % G
+            P.check_retrieval_row(ob[b, h], xs, b, h, s_g, n, same, ora["out"][b, h], f"{what} retrieval row ({b},{h})")
+            same_all += same
+    loc = [gg * G + t for gg in range(cfg.n_kv_heads) if not x.kv_role[gg] for t in range(G)]
+    P.check_outputs(ob[:, loc], ora["out"][:, loc], f"{what} local rows")
+    return same_all
+
+
+@pytest.mark.parametrize("layout", [rtp.KV_COMPACT, rtp.KV_FULL])
+def test_generation_graph_with_device_length(layout):
+    """Long generation (NEXT-3): [rtp_append_token_dev, rtp_decode_step_dev] captured once in a
+    HIP graph and replayed for 10 tokens.  The context length lives in the device state
+    {pos, n_ctx}, which every replay advances; after every replay, every retrieval and local
+    row is checked against the oracle on the grown caches, and the appended indexer key
+    against the exact projection."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=2, n_ctx=6000, window=512)
+    cfg = x.cfg
+    B, R, D, Hkv, G = cfg.batch, cfg.n_kv_r * cfg.group, cfg.head_dim, cfg.n_kv_heads, cfg.group
+    T = 10
+    n0 = cfg.n_ctx - T
+    p = 0.95
+    rng = np.random.default_rng(21)
+    k_pre_new = W.f32_to_bf16_bits(rng.standard_normal((T, B, Hkv, D)).astype(np.float32))
+    k_full, v_full = x.k.copy(), x.v.copy()
+    k_full[:, :, n0:] = 0
+    v_full[:, :, n0:] = 0
+    kidx = x.k_idx.copy()
+    kidx[:, :, n0:] = 0
+    dev = lambda a: rtp.to_device_bf16(np.ascontiguousarray(a))
+    L = _layer_kind(cfg, layout)
+    if layout == rtp.KV_COMPACT:
+        xc = type("X", (), {})()
+        xc.cfg, xc.k, xc.v, xc.kv_role = cfg, k_full, v_full, x.kv_role
+        kc, vc, kl, vl = _compact_caches(xc, n0)
+    else:
+        kc, vc, kl, vl = dev(k_full), dev(v_full), None, None
+    kidx_d = dev(kidx)
+    w_k = dev(x.w_k_idx)
+    step = rtp.DecodeStep(L, cfg.n_ctx, p)                      # grids and strides for the bound n0 + T
+    gen = torch.tensor([n0, n0], dtype=torch.int64, device="cuda")
+    knew = torch.empty(B * Hkv * D, dtype=torch.bfloat16, device="cuda")
+    vnew, kpre = torch.empty_like(knew), torch.empty_like(knew)
+
+    def fill(t):
+        knew.copy_(dev(x.k[:, :, n0 + t]).view(-1))
+        vnew.copy_(dev(x.v[:, :, n0 + t]).view(-1))
+        kpre.copy_(dev(k_pre_new[t]).view(-1))
+
+    def pair():
+        rtp.rtp_append_token_dev(L, gen, knew, vnew, kpre, w_k, D * 16, kc, vc, kidx_d, kl, vl)
+        step.run_dev(gen, d.q_pre, d.q, kc, vc, kidx_d, d.w_q_idx, k_loc=kl, v_loc=vl)
+
+    fill(0)
+    pair()                                                      # eager run of token 0 (re-appended below)
+    torch.cuda.synchronize()
+    gen.copy_(torch.tensor([n0, n0], dtype=torch.int64))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pair()
+    torch.cuda.synchronize()
+    ret = [gg for gg in range(Hkv) if x.kv_role[gg]]
+    identical = 0
+    for t in range(T):
+        fill(t)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        n = n0 + t + 1
+        assert gen.cpu().tolist() == [n, n], f"state after token {t}: {gen.cpu().tolist()}"
+        k_full[:, :, n - 1] = x.k[:, :, n - 1]
+        v_full[:, :, n - 1] = x.v[:, :, n - 1]
+        gi = rtp.from_device_bf16(kidx_d).reshape(B, cfg.n_kv_r, -1, 16)[:, :, n - 1]
+        for b in range(B):
+            for r, gg in enumerate(ret):
+                a = O.bf16_to_f64(k_pre_new[t, b, gg])
+                wr = O.bf16_to_f64(x.w_k_idx[r])
+                exact = a @ wr
+                allow = P.bf16_ulp(exact) + 1e-6 * (np.abs(a) @ np.abs(wr))
+                assert np.all(np.abs(O.bf16_to_f64(gi[b, r]) - exact) <= allow)
+        kidx[:, :, n - 1] = gi
+        cnt = step.sel_count.view(B, R).cpu().numpy()
+        sel = step.sel_idx.view(B, R, -1).cpu().numpy()
+        gsc = step.scores.view(B, R, -1).cpu().numpy()
+        assert np.all((cnt >= 1) & (cnt <= n)), f"token {t}: counts {cnt}"
+        identical += _check_step_against_oracle(x, cfg, n, k_full, v_full, kidx, rtp.from_device_bf16(step.out), sel,
+                                                cnt, gsc, p, f"token {t}")
+    assert identical >= 0.9 * T * B * R
