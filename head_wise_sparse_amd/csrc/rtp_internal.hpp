@@ -86,6 +86,7 @@ constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per bl
 constexpr int kSelItemsLong = 32;                                // ... or twice that when a pass would
                                                                  // otherwise take more than one round of blocks
 constexpr int kBins = 2048;                                     // 11-bit digits (last level 10 bits)
+constexpr int kTabDigits = 1024;                                // last-level digits (10 bits)
 struct SelLevelState {           // what is known after resolving one level's digit
   uint32_t prefix;               // key bits resolved so far
   uint32_t cnt_above;            // tokens strictly above the prefix
@@ -99,7 +100,7 @@ struct SelRowState {             // one per score row, lives in the workspace
 };
 static_assert(sizeof(SelRowState) == 56, "row state layout");
 struct SelLayout {                // depends on the layer only (n_cap), not on n_ctx: the
-  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, tilerec, total;
+  size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, tilerec, tiletab, total;
   int nblk_max;                   // zero-filled region stays in place while n_ctx grows
 };
 SelLayout sel_layout(const Layer& L);
@@ -111,6 +112,8 @@ struct SelRows {                 // device views of the selection workspace
   SelRowState* state;            // [rows]
   uint32_t* ctr;                 // [rows][2]       compaction: [1] blocks done ([0] unused, kept zero)
   uint4* tilerec;                // [rows][nblk]    per tile: counts against the level-1 prefix (hist<2>)
+  uint16_t* tiletab;             // [rows][nblk][kTabDigits] tiles whose record overflowed: candidates
+                                 //                 with low digit >= d (hist<2>), zero otherwise
 };
 struct SelArgs {
   const float* scores;           // [rows][n_cap]

@@ -23,22 +23,23 @@
 //             hist<2> also leaves one record per tile: how many of its tokens lie above
 //             the 22-bit prefix (certainly selected) and, for up to kRecPairs distinct
 //             low 10-bit digits among the tokens that share it (candidates), the digit
-//             and its count.
+//             and its count; a tile with more such digits than that, its table.
 //   compact   resolves the last digit (t is now the full key), the tie count r in
 //             closed form (tied tokens carry equal weight), and writes the selected
 //             indices in increasing order.  A tile's output offset comes from the
 //             records of the earlier tiles (written by the previous launch: no waiting
 //             on other blocks): tokens above the prefix, plus candidates above t, plus
 //             at most r ties.  Candidates share 22 key bits with t, so a tile holds few
-//             distinct ones (exact ties collapse into one pair); only for a tile with
-//             more distinct candidates than its record keeps does the block count them
-//             again from that tile's scores.
+//             distinct ones (exact ties collapse into one pair).  A tile with more
+//             distinct candidates than its record keeps ("heavy") also left a table of
+//             its candidate counts at or above each low digit, and the block reads the
+//             two entries at t from it: O(1) per earlier tile whatever the scores.
 //             It also writes the range index of every list when asked for.
 // The workspace is all zero when a call starts and when it ends: each launch clears
 // what earlier launches left and nobody reads any more (hist<2> the level-0
 // histogram, compact the level-1 histogram), and the last compaction block of a row
-// to finish clears the rest of that row (level-2 histogram, tile records, row state
-// and counters).
+// to finish clears the rest of that row (level-2 histogram, tile records and the
+// heavy tiles' tables, row state and counters).
 #include <cmath>
 
 #include "rtp_internal.hpp"
@@ -52,7 +53,6 @@ namespace {
 constexpr int kCoarse = 64;          // coarse bins of levels 0/1 (32 at level 2)
 constexpr int kFinePer = 32;         // fine bins under one coarse bin
 constexpr int kRecPairs = 3;         // (digit, count) pairs a tile record holds (one per 32-bit word)
-constexpr int kMaxHeavy = 256;       // heavy earlier tiles a compaction block recounts one by one
 
 __device__ __forceinline__ uint64_t ld_rlx(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   __shared__ uint32_t s_prefix;
   __shared__ float s_red[kSelThreads / 64];
   __shared__ uint32_t s_na[kSelThreads / 64], s_np, s_pair[kRecPairs];   // level 2: tile record
+  __shared__ uint32_t s_wt[kSelThreads / 64];                               // level 2: heavy-tile table
   const int n_ctx = live_ctx(a.live, a.n_ctx);
   const int nblk = int((int64_t(n_ctx) + TILE - 1) / TILE);       // tiles of the live context
   if (blk >= nblk) return;
@@ -341,6 +342,22 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
       for (int k = 0; k < kRecPairs; ++k) pw[k] = uint32_t(k) < np ? s_pair[k] : 0u;
       a.R.tilerec[int64_t(row) * a.rec_stride + blk] = make_uint4(na | (np << 16), pw[0], pw[1], pw[2]);
     }
+    if (s_np > uint32_t(kRecPairs)) {
+      // The record cannot hold this tile's candidates: leave their counts at or above every
+      // low digit d (inclusive suffix sums of the tile's level-2 counts, < 2^16 per tile),
+      // from which the compaction reads the two it needs once the threshold digit is known.
+      // Thread tid owns digits 4 tid .. 4 tid + 3; higher threads hold higher digits.
+      const uint32_t c0 = h_c[4 * tid], c1 = h_c[4 * tid + 1], c2 = h_c[4 * tid + 2], c3 = h_c[4 * tid + 3];
+      const uint32_t own = c0 + c1 + c2 + c3;
+      const uint32_t in_wave = wave_suffix_incl<uint32_t>(own, lane);   // own + higher lanes of the wave
+      if (lane == 0) s_wt[tid / 64] = in_wave;
+      __syncthreads();
+      uint32_t hi = in_wave - own;                                   // digits above this thread's four
+      for (int w = tid / 64 + 1; w < kSelThreads / 64; ++w) hi += s_wt[w];
+      const uint32_t s3 = hi + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
+      uint2* tab = reinterpret_cast<uint2*>(a.R.tiletab + (int64_t(row) * a.rec_stride + blk) * kTabDigits);
+      tab[tid] = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
+    }
   }
   // coarse summary: thread c < NB/32 sums its 32 fine bins, starting at a different
   // one per thread so that the lanes of a wave read different LDS banks
@@ -373,9 +390,8 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   static_assert(ITEMS * NW % 64 == 0 && ITEMS <= 32, "one wave scans the per-(item, wave) counts");
   __shared__ uint32_t s_t, s_r;
   __shared__ uint32_t s_wa[ITEMS * NW], s_we[ITEMS * NW];   // counts, then exclusive prefixes
-  __shared__ uint32_t s_pa, s_pe, s_heavy, s_last;
-  __shared__ uint32_t s_ra[NW], s_re[NW];
-  __shared__ uint32_t s_heavy_list[kMaxHeavy];
+  __shared__ uint32_t s_pa, s_pe, s_last, s_nh;
+  __shared__ uint32_t s_hl[kSelThreads];
   const int n_ctx = live_ctx(a.live, a.n_ctx);
   const int nblk = int((int64_t(n_ctx) + TILE - 1) / TILE);       // tiles of the live context
   if (tile >= nblk) return;
@@ -420,18 +436,23 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   __syncthreads();
   clear_level(a.R, row, 1, tile, nblk);             // read last by hist<2>
   const uint32_t t = s_t, r = s_r;
-  // ---- tokens of earlier tiles with key > t (pa) and key == t (pe), from their records;
-  // tiles whose record overflowed ("heavy") are listed and counted from their scores
+  // ---- tokens of earlier tiles with key > t (pa) and key == t (pe), from their records,
+  // or, for a tile whose record overflowed ("heavy"), from two entries of its table
+  const uint16_t* tab = a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits;
   if (wave == 1) {
     const uint32_t tl = t & 1023u;
-    uint32_t ca = 0, ce = 0, nh = 0;
+    uint32_t ca = 0, ce = 0;
     for (int c = 0; c < tile; c += 64) {
       const int i = c + lane;
       const uint4 q = (c == 0) ? rec0 : (i < tile ? rec[i] : make_uint4(0u, 0u, 0u, 0u));
       const uint32_t np = q.x >> 16;
       ca += q.x & 0xFFFFu;
-      const bool heavy = np > uint32_t(kRecPairs);
-      if (!heavy) {
+      if (np > uint32_t(kRecPairs)) {
+        const uint16_t* ti = tab + int64_t(i) * kTabDigits;
+        const uint32_t ge = ti[tl], gt = tl < 1023u ? uint32_t(ti[tl + 1]) : 0u;   // digit >= tl, > tl
+        ca += gt;
+        ce += ge - gt;
+      } else {
         const uint32_t pw[kRecPairs] = {q.y, q.z, q.w};
 #pragma unroll
         for (int k = 0; k < kRecPairs; ++k) {
@@ -440,19 +461,12 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
           ce += dig == tl ? cnt : 0u;
         }
       }
-      const uint64_t hb = __ballot(heavy);
-      if (heavy) {
-        const uint32_t slot = nh + __popcll(hb & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        if (slot < uint32_t(kMaxHeavy)) s_heavy_list[slot] = uint32_t(i);
-      }
-      nh += __popcll(hb);
     }
     ca = wave_sum(ca);
     ce = wave_sum(ce);
     if (lane == 0) {
       s_pa = ca;
       s_pe = ce;
-      s_heavy = nh;
     }
   }
   // this thread's tokens above t / tied with t, one bit per item (ballots are taken again
@@ -472,48 +486,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     }
   }
   __syncthreads();
-  const uint32_t nheavy = s_heavy;
-  if (nheavy) {
-    // candidates of the heavy tiles (all earlier tiles when there are too many of them)
-    const bool listed = nheavy <= uint32_t(kMaxHeavy);
-    const int nt = listed ? int(nheavy) : tile;
-    uint32_t ga = 0, ge = 0;
-    for (int h = 0; h < nt; ++h) {
-      const int64_t tb = int64_t(listed ? s_heavy_list[h] : h) * TILE;
-#pragma unroll 4
-      for (int k = tid; k < TILE; k += kSelThreads) {
-        const uint32_t key = score_key(sp[tb + k]);          // earlier tiles are full: tb + k < base
-        const bool cand = (key >> 10) == (t >> 10);
-        ga += uint32_t(cand && key > t);
-        ge += uint32_t(key == t);
-      }
-    }
-    ga = wave_sum(ga);
-    ge = wave_sum(ge);
-    if (lane == 0) {
-      s_ra[wave] = ga;
-      s_re[wave] = ge;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t ga_all = 0, ge_all = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        ga_all += s_ra[w];
-        ge_all += s_re[w];
-      }
-      if (listed) {                 // the records already gave the light tiles' candidates
-        s_pa += ga_all;
-        s_pe += ge_all;
-      } else {                      // recounted every earlier tile: keep only the above-prefix sum
-        uint32_t na = 0;
-        for (int i = 0; i < tile; ++i) na += rec[i].x & 0xFFFFu;
-        s_pa = na + ga_all;
-        s_pe = ge_all;
-      }
-    }
-  }
-  // This block reads no more of the tile records, the level-2 histogram or the row state:
+  // This block reads no more of the tile records and tables, the level-2 histogram or the row state:
   // count it as done now, and learn whether it was the last one only at the end.
   uint32_t done_before = 0;
   if (tid == 0) done_before = atomicAdd(ctr + 1, 1u);
@@ -570,7 +543,25 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   if (tid == 0) s_last = (done_before == uint32_t(nblk - 1));
   __syncthreads();
   if (s_last) {
-    for (int i = tid; i < nblk; i += kSelThreads) a.R.tilerec[int64_t(row) * a.rec_stride + i] = make_uint4(0u, 0u, 0u, 0u);
+    // tile records, and the tables of the heavy tiles among them (kTabDigits / 8 16-byte
+    // stores each), a round of kSelThreads tiles at a time
+    uint4* rrow = a.R.tilerec + int64_t(row) * a.rec_stride;
+    uint4* trow = reinterpret_cast<uint4*>(a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits);
+    constexpr int kTab16 = kTabDigits * int(sizeof(uint16_t)) / 16;
+    for (int c0 = 0; c0 < nblk; c0 += kSelThreads) {
+      if (tid == 0) s_nh = 0;
+      __syncthreads();
+      const int i = c0 + tid;
+      if (i < nblk) {
+        if ((rrow[i].x >> 16) > uint32_t(kRecPairs)) s_hl[atomicAdd(&s_nh, 1u)] = uint32_t(i);
+        rrow[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      __syncthreads();
+      const int nh = int(s_nh);
+      for (int k = tid; k < nh * kTab16; k += kSelThreads)
+        trow[int64_t(s_hl[k / kTab16]) * kTab16 + k % kTab16] = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+    }
     uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
     if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
     clear_level(a.R, row, 2, 0, 1);
@@ -604,7 +595,7 @@ SelRows sel_rows(void* ws, const SelLayout& lay) {
   return SelRows{reinterpret_cast<uint64_t*>(w + lay.hist_mass), reinterpret_cast<uint32_t*>(w + lay.hist_cnt),
                  reinterpret_cast<uint64_t*>(w + lay.coarse_mass), reinterpret_cast<uint32_t*>(w + lay.coarse_cnt),
                  reinterpret_cast<SelRowState*>(w + lay.state), reinterpret_cast<uint32_t*>(w + lay.ctr),
-                 reinterpret_cast<uint4*>(w + lay.tilerec)};
+                 reinterpret_cast<uint4*>(w + lay.tilerec), reinterpret_cast<uint16_t*>(w + lay.tiletab)};
 }
 
 }  // namespace rtp

@@ -188,7 +188,9 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
   char* w = static_cast<char*>(ws);
   const int n = int(n_ctx);
   if (clear_sel && L.n_ret && top_p < 1.0f) {
-    const size_t n16 = sel_layout(L).total / 16;            // the region is a multiple of 256 bytes
+    // up to the heavy-tile tables, which a call writes before it reads them (offsets are
+    // multiples of 256 bytes)
+    const size_t n16 = sel_layout(L).tiletab / 16;
     const unsigned nb = unsigned(std::min<size_t>((n16 + 255) / 256, 1024));
     hipLaunchKernelGGL(k_step_clear, dim3(nb), dim3(256), 0, s, reinterpret_cast<uint4*>(w + lay.sel), n16);
     if ((st = check_launch("k_step_clear")) != RTP_OK) return st;

@@ -162,8 +162,9 @@ rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ctx,
  *            given, rtp_sparse_decode_attn can take it instead of rebuilding it.
  * The row_max values are the reference of every weight exp(s - row_max): pass the
  * row maxima rtp_indexer_score wrote (a smaller value saturates weights at 1).
- * The workspace holds the radix histograms, row states, counters and per-tile
- * records of the search; see the zero-fill rule above.
+ * The workspace holds the radix histograms, row states, counters, per-tile
+ * records and per-tile digit tables of the search (rtp_workspace_bytes grows by
+ * 0.5 byte per token of n_cap per row for the tables); see the zero-fill rule above.
  */
 rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
                            const float* scores, const float* row_max, const float* row_sum,

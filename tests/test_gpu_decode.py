@@ -202,8 +202,9 @@ def _edge_rows():
             ulps = rng.integers(0, 4, per)
             c[:, pos] = (np.float32(1.0).view(np.uint32) + ulps.astype(np.uint32)).view(np.float32)
         yield name, c, 0.5
-    # a narrow spread over more than 256 tiles: every tile holds many distinct candidates,
-    # so late tiles recount all earlier tiles instead of a list of the heavy ones
+    # a narrow spread over more than 256 tiles: every tile holds many distinct candidates
+    # (a heavy tile, counted from its table), and the last compaction block clears the
+    # tables in two rounds of 256 tiles
     yield "narrow_many_heavy_tiles", (5 + rng.standard_normal((1, 4096 * 268 + 100)) * 1e-3).astype(np.float32), 0.9
     # enough rows x tiles that the passes use 8192-token tiles: plain, tied and narrow rows,
     # ragged tail
