@@ -4,6 +4,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <cstdlib>
+
 #include "rtp_internal.hpp"
 
 namespace rtp {
@@ -21,6 +23,12 @@ rtp_status fail(rtp_status s, const char* fmt, ...) {
 rtp_status ok() {
   g_err[0] = '\0';
   return RTP_OK;
+}
+
+rtp_status enqueue_gate(const char* who) {
+  const char* e = getenv("RTP_FAULT_INJECT");
+  if (e && *e) return fail(RTP_EDEVICE, "%s: injected device failure (RTP_FAULT_INJECT=%s)", who, e);
+  return ok();
 }
 
 rtp_status check_launch(const char* what) {
@@ -244,6 +252,8 @@ __global__ __launch_bounds__(256, 2) void k_mfma_probe(uint32_t iters, float* __
 extern "C" rtp_status rtp_mfma_probe(uint32_t iters, float* sink, double* flops, void* stream) {
   if (!sink || !flops) return fail(RTP_EINVAL, "rtp_mfma_probe: NULL sink or flops");
   if (iters < 1 || iters > (1u << 24)) return fail(RTP_EINVAL, "rtp_mfma_probe: iters must be in [1, 2^24]");
+  rtp_status st = enqueue_gate("rtp_mfma_probe");
+  if (st != RTP_OK) return st;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       ncu < 1)
@@ -257,6 +267,8 @@ extern "C" rtp_status rtp_mfma_probe(uint32_t iters, float* sink, double* flops,
 extern "C" rtp_status rtp_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes < 16) return fail(RTP_EINVAL, "rtp_hbm_read_probe: NULL buffer or fewer than 16 bytes");
   if (!aligned(buf, 16)) return fail(RTP_EINVAL, "rtp_hbm_read_probe: buffer must be 16-byte aligned");
+  rtp_status st = enqueue_gate("rtp_hbm_read_probe");
+  if (st != RTP_OK) return st;
   hipLaunchKernelGGL(k_read_probe, dim3(2048), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(buf), bytes / 16, sink);
   return check_launch("k_read_probe");

@@ -147,6 +147,7 @@ rtp_status append_impl(const rtp_layer_desc* desc, int64_t pos, int64_t* gen, co
     a.rank[L.loc_kv[i]] = i;
     a.role[L.loc_kv[i]] = 0;
   }
+  if ((st = enqueue_gate("rtp_append_token")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(k_append, dim3(L.Hkv, L.B), dim3(64), 0, s, a);
   return check_launch("k_append");

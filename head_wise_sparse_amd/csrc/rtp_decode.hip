@@ -135,6 +135,7 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(RTP_EWORKSPACE, "rtp_sparse_decode_attn: workspace needs %zu bytes, 256-aligned (got %zu)", need,
                 ws_bytes);
+  if ((st = enqueue_gate("rtp_sparse_decode_attn")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int nsplit = int((n_ctx + kDecRange - 1) / kDecRange);
   const int rows = L.B * L.n_ret * L.G;
@@ -181,6 +182,7 @@ extern "C" rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(RTP_EWORKSPACE, "rtp_window_sink_attn: workspace needs %zu bytes, 256-aligned (got %zu)", need,
                 ws_bytes);
+  if ((st = enqueue_gate("rtp_window_sink_attn")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t s_end = std::min<int64_t>(L.n_sinks, n_ctx);
   const int64_t w_start = std::max<int64_t>(n_ctx - L.window, s_end);

@@ -19,6 +19,10 @@ rtp_status fail(rtp_status s, const char* fmt, ...) __attribute__((format(printf
 rtp_status ok();
 // Map a HIP error from a launch to RTP_EDEVICE (records the message).
 rtp_status check_launch(const char* what);
+// Called by every entry point where it would first touch the device, after its host
+// checks: RTP_EDEVICE ("injected") when the environment sets RTP_FAULT_INJECT to a
+// non-empty value, so that callers' device-error paths can be exercised without a GPU.
+rtp_status enqueue_gate(const char* who);
 
 // Head bookkeeping derived from a validated descriptor.
 struct Layer {

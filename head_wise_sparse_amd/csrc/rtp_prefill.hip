@@ -635,6 +635,7 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       (k_pre && !aligned(k_pre, 16)) || (k_idx_cache && !aligned(k_idx_cache, 2)))
     return fail(RTP_EINVAL, "rtp_prefill_attn: tensors must be 16-byte aligned");
+  if ((st = enqueue_gate("rtp_prefill_attn")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   PrefArgs a{};
   a.q = q;

@@ -78,6 +78,7 @@ extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ct
 
   const int nblk = int((n_ctx + score_tile(L.idx) - 1) / score_tile(L.idx));
   const dim3 grid(nblk, L.B * L.n_ret);
+  if ((st = enqueue_gate("rtp_indexer_score")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws);
   const ScoreArgs A{q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, scores, part, int(n_ctx), nullptr, L.n_cap,

@@ -618,6 +618,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   if (!aligned(scores, 16) || !aligned(sel_idx, 16))
     return fail(RTP_EINVAL, "rtp_topp_select: tensors must be 16-byte aligned");
   const int rows = L.B * L.n_ret * L.G;
+  if ((st = enqueue_gate("rtp_topp_select")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const SelLayout lay = sel_layout(L);
   if (top_p < 1.0f && (!ws || ws_bytes < lay.total || !aligned(ws, 256)))
@@ -658,6 +659,7 @@ extern "C" rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx,
   if (!aligned(scores, 16) || !aligned(sel_idx, 16))
     return fail(RTP_EINVAL, "rtp_topk_select: tensors must be 16-byte aligned");
   const int rows = L.B * L.n_ret * L.G;
+  if ((st = enqueue_gate("rtp_topk_select")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const SelLayout lay = sel_layout(L);
   if (k < n_ctx && (!ws || ws_bytes < lay.total || !aligned(ws, 256)))

@@ -184,6 +184,7 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
   if (!L.n_ret && !L.n_loc) return ok();
   if (L.n_ret && L.idx != kIdxDim)
     return fail(RTP_EUNSUPPORTED, "rtp_decode_step: idx_dim %d needs the separate calls (fused: 16)", L.idx);
+  if ((st = enqueue_gate("rtp_decode_step")) != RTP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   const int n = int(n_ctx);
@@ -398,6 +399,7 @@ extern "C" rtp_status rtp_decode_step_noalloc(const rtp_layer_desc* desc, int64_
     return fail(RTP_EUNSUPPORTED,
                 "rtp_decode_step_noalloc: this layer and context need %zu bytes of scratch; the library holds %zu "
                 "(use rtp_decode_step with a workspace)", need, kScratchBytes);
+  if ((st = enqueue_gate("rtp_decode_step_noalloc")) != RTP_OK) return st;
   void* ws = nullptr;
   if ((st = scratch_of_current_device(&ws)) != RTP_OK) return st;
   return decode_step_impl(desc, n_ctx, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,

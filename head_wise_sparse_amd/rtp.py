@@ -16,7 +16,9 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "librtp.so")
+# RTP_LIB_PATH names another build of the same library (the host-sanitized one of the CPU tests)
+LIB_PATH = os.environ.get("RTP_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                          "librtp.so")
 
 RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EDEVICE = range(5)
 CALL_INDEXER_SCORE, CALL_TOPP_SELECT, CALL_SPARSE_DECODE, CALL_WINDOW_SINK, CALL_PREFILL, CALL_DECODE_STEP = range(6)

@@ -39,6 +39,11 @@
  *    default stream).  There is no implicit synchronisation and no host<->device
  *    copy; counts and thresholds stay on the device.  RTP_EDEVICE reports a
  *    failed launch; faults inside kernels surface at the caller's next sync.
+ *    Fault injection: when the environment variable RTP_FAULT_INJECT is set to a
+ *    non-empty value, every call that passes its host checks returns RTP_EDEVICE
+ *    ("injected device failure") where it would first touch the device, with
+ *    nothing enqueued, so callers can test their device-error paths on a host
+ *    without a GPU.
  *  - Heads: G = n_q_heads / n_kv_heads; KV head g serves query heads
  *    g*G .. g*G+G-1.  Retrieval KV heads (kv_role[g] == 1) are numbered by rank
  *    r = 0,1,.. in increasing g; retrieval query head g*G+t has the compact index

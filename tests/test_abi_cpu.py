@@ -185,3 +185,59 @@ def test_binding_raises_with_message():
     L = _layer(head_dim=96)
     with pytest.raises(rtp.RtpError, match="RTP_EUNSUPPORTED: head_dim"):
         rtp._check(_call_score(L))
+
+
+def test_injected_device_failure(monkeypatch):
+    """With RTP_FAULT_INJECT set, every entry point whose host checks pass returns
+    RTP_EDEVICE where it would first touch the device (nothing is launched, so this runs
+    without a GPU), and the binding turns that status into RtpError.  Host checks still
+    come first: a bad argument keeps its own status."""
+    lib = _lib()
+    monkeypatch.setenv("RTP_FAULT_INJECT", "1")
+    L = _layer()
+    L1 = _layer(batch=1, n_cap=32768)
+    Ls = _layer(batch=1, n_cap=8192)                 # fits the allocation-free step's scratch
+    big = 1 << 30
+    fl = C.c_double(0.0)
+    gen = C.c_void_p(FAKE)
+    calls = {
+        "rtp_indexer_score": lambda: _call_score(L),
+        "rtp_topp_select": lambda: lib.rtp_topp_select(L.desc, 1000, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, None, FAKE,
+                                                       big, None),
+        "rtp_topk_select": lambda: lib.rtp_topk_select(L.desc, 1000, FAKE, 10, FAKE, FAKE, None, FAKE, big, None),
+        "rtp_sparse_decode_attn": lambda: lib.rtp_sparse_decode_attn(L.desc, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                                                     0.1, FAKE, FAKE, big, None),
+        "rtp_window_sink_attn": lambda: lib.rtp_window_sink_attn(L.desc, 1000, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, big,
+                                                                 None),
+        "rtp_prefill_attn": lambda: lib.rtp_prefill_attn(L1.desc, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 128 * 16,
+                                                         FAKE, 0.1, FAKE, FAKE, big, None),
+        "rtp_decode_step": lambda: _call_step(L),
+        "rtp_decode_step_dev": lambda: lib.rtp_decode_step_dev(L.desc, 1000, gen, FAKE, FAKE, 0, FAKE, 1.0, FAKE,
+                                                               FAKE, FAKE, None, None, 0.9, 0.1, FAKE, FAKE, FAKE,
+                                                               FAKE, FAKE, None, FAKE, FAKE, big, None),
+        "rtp_decode_step_noalloc": lambda: lib.rtp_decode_step_noalloc(Ls.desc, 1000, FAKE, FAKE, 0, FAKE, 1.0, FAKE,
+                                                                       FAKE, FAKE, None, None, 0.9, 0.1, FAKE, FAKE,
+                                                                       FAKE, FAKE, FAKE, None, FAKE, None),
+        "rtp_append_token": lambda: lib.rtp_append_token(L.desc, 100, FAKE, FAKE, FAKE, FAKE, 128 * 16, FAKE, FAKE,
+                                                         FAKE, None, None, None),
+        "rtp_append_token_dev": lambda: lib.rtp_append_token_dev(L.desc, gen, FAKE, FAKE, FAKE, FAKE, 128 * 16, FAKE,
+                                                                 FAKE, FAKE, None, None, None),
+        "rtp_mfma_probe": lambda: lib.rtp_mfma_probe(10, C.c_void_p(FAKE), C.byref(fl), None),
+        "rtp_hbm_read_probe": lambda: lib.rtp_hbm_read_probe(FAKE, 1 << 20, C.c_void_p(FAKE), None),
+    }
+    for name, call in calls.items():
+        st = call()
+        msg = lib.rtp_last_error().decode()
+        assert st == rtp.RTP_EDEVICE, f"{name}: status {st} ({msg})"
+        assert "injected" in msg, f"{name}: {msg}"
+        with pytest.raises(rtp.RtpError, match="RTP_EDEVICE: .*injected") as ei:
+            rtp._check(st)
+        assert ei.value.status == rtp.RTP_EDEVICE
+    # host checks come before the gate
+    assert _call_score(L, n_ctx=0) == rtp.RTP_EINVAL
+    assert _call_step(L, top_p=math.nan) == rtp.RTP_EINVAL
+    assert lib.rtp_mfma_probe(0, C.c_void_p(FAKE), C.byref(fl), None) == rtp.RTP_EINVAL
+    # every exported entry point that enqueues work is covered
+    enqueue = {n for n in rtp.EXPORTED if n not in ("rtp_workspace_bytes", "rtp_status_string", "rtp_last_error",
+                                                    "rtp_version", "rtp_decode_step_noalloc_max_bytes")}
+    assert enqueue == set(calls)
