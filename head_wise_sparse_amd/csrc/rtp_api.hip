@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include <cstdlib>
+#include <dlfcn.h>
 
 #include "rtp_internal.hpp"
 
@@ -23,6 +24,35 @@ rtp_status fail(rtp_status s, const char* fmt, ...) {
 rtp_status ok() {
   g_err[0] = '\0';
   return RTP_OK;
+}
+
+namespace {
+struct RoctxApi {
+  int (*push)(const char*);
+  int (*pop)();
+};
+const RoctxApi& roctx_api() {
+  static const RoctxApi api = [] {
+    RoctxApi a{nullptr, nullptr};
+    const char* e = getenv("RTP_ROCTX");
+    if (!e || !*e) return a;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_GLOBAL);
+    if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_GLOBAL);
+    if (!h) return a;
+    a.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    a.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!a.push || !a.pop) a = RoctxApi{nullptr, nullptr};
+    return a;
+  }();
+  return api;
+}
+}  // namespace
+
+TraceRange::TraceRange(const char* name) : active_(roctx_api().push != nullptr) {
+  if (active_) roctx_api().push(name);
+}
+TraceRange::~TraceRange() {
+  if (active_) roctx_api().pop();
 }
 
 rtp_status enqueue_gate(const char* who) {
@@ -250,6 +280,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_probe(uint32_t iters, float* __
 }  // namespace
 
 extern "C" rtp_status rtp_mfma_probe(uint32_t iters, float* sink, double* flops, void* stream) {
+  TraceRange trace_("rtp_mfma_probe");
   if (!sink || !flops) return fail(RTP_EINVAL, "rtp_mfma_probe: NULL sink or flops");
   if (iters < 1 || iters > (1u << 24)) return fail(RTP_EINVAL, "rtp_mfma_probe: iters must be in [1, 2^24]");
   rtp_status st = enqueue_gate("rtp_mfma_probe");
@@ -265,6 +296,7 @@ extern "C" rtp_status rtp_mfma_probe(uint32_t iters, float* sink, double* flops,
 }
 
 extern "C" rtp_status rtp_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  TraceRange trace_("rtp_hbm_read_probe");
   if (!buf || !sink || bytes < 16) return fail(RTP_EINVAL, "rtp_hbm_read_probe: NULL buffer or fewer than 16 bytes");
   if (!aligned(buf, 16)) return fail(RTP_EINVAL, "rtp_hbm_read_probe: buffer must be 16-byte aligned");
   rtp_status st = enqueue_gate("rtp_hbm_read_probe");

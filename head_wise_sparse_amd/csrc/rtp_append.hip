@@ -159,6 +159,7 @@ extern "C" rtp_status rtp_append_token(const rtp_layer_desc* desc, int64_t pos, 
                                        const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx,
                                        int64_t w_head_stride, uint16_t* k_cache, uint16_t* v_cache,
                                        uint16_t* k_idx_cache, uint16_t* k_loc, uint16_t* v_loc, void* stream) {
+  TraceRange trace_("rtp_append_token");
   return append_impl(desc, pos, nullptr, k_new, v_new, k_pre, w_k_idx, w_head_stride, k_cache, v_cache, k_idx_cache,
                      k_loc, v_loc, stream);
 }
@@ -167,6 +168,7 @@ extern "C" rtp_status rtp_append_token_dev(const rtp_layer_desc* desc, int64_t* 
                                            const uint16_t* v_new, const uint16_t* k_pre, const uint16_t* w_k_idx,
                                            int64_t w_head_stride, uint16_t* k_cache, uint16_t* v_cache,
                                            uint16_t* k_idx_cache, uint16_t* k_loc, uint16_t* v_loc, void* stream) {
+  TraceRange trace_("rtp_append_token_dev");
   if (!gen) return fail(RTP_EINVAL, "rtp_append_token_dev: NULL generation state");
   return append_impl(desc, 0, gen, k_new, v_new, k_pre, w_k_idx, w_head_stride, k_cache, v_cache, k_idx_cache, k_loc,
                      v_loc, stream);

@@ -124,6 +124,7 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
                                              const int32_t* sel_idx, const int32_t* sel_count,
                                              const int32_t* sel_starts, float sm_scale, uint16_t* out, void* ws,
                                              size_t ws_bytes, void* stream) {
+  TraceRange trace_("rtp_sparse_decode_attn");
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;
@@ -172,6 +173,7 @@ extern "C" rtp_status rtp_sparse_decode_attn(const rtp_layer_desc* desc, int64_t
 extern "C" rtp_status rtp_window_sink_attn(const rtp_layer_desc* desc, int64_t n_ctx, const uint16_t* q,
                                            const uint16_t* k_cache, const uint16_t* v_cache, float sm_scale,
                                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  TraceRange trace_("rtp_window_sink_attn");
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;

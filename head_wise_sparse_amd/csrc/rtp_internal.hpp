@@ -23,6 +23,19 @@ rtp_status check_launch(const char* what);
 // checks: RTP_EDEVICE ("injected") when the environment sets RTP_FAULT_INJECT to a
 // non-empty value, so that callers' device-error paths can be exercised without a GPU.
 rtp_status enqueue_gate(const char* who);
+// A roctx range around one C-ABI call, on when the environment sets RTP_ROCTX to a
+// non-empty value at the library's first call (the roctx library is then opened with
+// dlopen; the library does not link it).  Off, it costs one branch.
+class TraceRange {
+ public:
+  explicit TraceRange(const char* name);
+  ~TraceRange();
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+
+ private:
+  bool active_;
+};
 
 // Head bookkeeping derived from a validated descriptor.
 struct Layer {

@@ -613,6 +613,7 @@ extern "C" rtp_status rtp_prefill_attn(const rtp_layer_desc* desc, int64_t c0, i
                                        const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_pre,
                                        const uint16_t* w_k_idx, int64_t w_head_stride, uint16_t* k_idx_cache,
                                        float sm_scale, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  TraceRange trace_("rtp_prefill_attn");
   (void)ws;
   (void)ws_bytes;
   Layer L;

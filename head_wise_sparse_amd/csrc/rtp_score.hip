@@ -57,6 +57,7 @@ extern "C" rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ct
                                         const uint16_t* w_q_idx, int64_t w_head_stride, const uint16_t* k_idx,
                                         float idx_scale, float* scores, float* row_max, float* row_sum, void* ws,
                                         size_t ws_bytes, void* stream) {
+  TraceRange trace_("rtp_indexer_score");
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;

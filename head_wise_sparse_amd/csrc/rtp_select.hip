@@ -604,6 +604,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
                                       const float* row_max, const float* row_sum, float top_p, int32_t* sel_idx,
                                       int32_t* sel_count, int32_t* sel_starts, void* ws, size_t ws_bytes,
                                       void* stream) {
+  TraceRange trace_("rtp_topp_select");
   (void)row_sum;
   Layer L;
   rtp_status st = check_desc(desc, &L);
@@ -648,6 +649,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
 extern "C" rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx, const float* scores, int64_t k,
                                       int32_t* sel_idx, int32_t* sel_count, int32_t* sel_starts, void* ws,
                                       size_t ws_bytes, void* stream) {
+  TraceRange trace_("rtp_topk_select");
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;

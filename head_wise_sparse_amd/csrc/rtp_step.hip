@@ -325,6 +325,7 @@ extern "C" rtp_status rtp_decode_step(const rtp_layer_desc* desc, int64_t n_ctx,
                                       float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
                                       int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
                                       void* stream) {
+  TraceRange trace_("rtp_decode_step");
   return decode_step_impl(desc, n_ctx, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,
                           v_loc, top_p, sm_scale, scores, row_max, row_sum, sel_idx, sel_count, sel_starts, out, ws,
                           ws_bytes, stream, false);
@@ -339,6 +340,7 @@ extern "C" rtp_status rtp_decode_step_dev(const rtp_layer_desc* desc, int64_t n_
                                           float* row_max, float* row_sum, int32_t* sel_idx, int32_t* sel_count,
                                           int32_t* sel_starts, uint16_t* out, void* ws, size_t ws_bytes,
                                           void* stream) {
+  TraceRange trace_("rtp_decode_step_dev");
   if (!gen) return fail(RTP_EINVAL, "rtp_decode_step_dev: NULL generation state");
   if (!aligned(gen, 8)) return fail(RTP_EINVAL, "rtp_decode_step_dev: the generation state must be 8-byte aligned");
   return decode_step_impl(desc, n_max, q_pre, w_q_idx, w_head_stride, k_idx, idx_scale, q, k_cache, v_cache, k_loc,
@@ -388,6 +390,7 @@ extern "C" rtp_status rtp_decode_step_noalloc(const rtp_layer_desc* desc, int64_
                                               float top_p, float sm_scale, float* scores, float* row_max,
                                               float* row_sum, int32_t* sel_idx, int32_t* sel_count,
                                               int32_t* sel_starts, uint16_t* out, void* stream) {
+  TraceRange trace_("rtp_decode_step_noalloc");
   Layer L;
   rtp_status st = check_desc(desc, &L);
   if (st != RTP_OK) return st;

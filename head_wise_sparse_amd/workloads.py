@@ -314,10 +314,15 @@ class PrefillInputs:
         C = c1 - c0
         heads = range(cfg.n_q_heads) if heads is None else heads
         out = np.zeros((C, cfg.n_q_heads, cfg.head_dim), np.uint16)
-        pos = np.arange(c0, c1)
         for h in heads:
-            out[:, h] = _rope_bf16(_normal_bf16(_rng(cfg.cid, T_Q, c, h), (C, cfg.head_dim)), pos)
+            out[:, h] = self.q_head(c, h)
         return out
+
+    def q_head(self, c: int, h: int) -> np.ndarray:
+        """[C][D] bf16 bits (post-RoPE): query head h of chunk c (the same values as q_chunk)."""
+        cfg = self.cfg
+        c0, c1 = self.chunk_bounds(c)
+        return _rope_bf16(_normal_bf16(_rng(cfg.cid, T_Q, c, h), (c1 - c0, cfg.head_dim)), np.arange(c0, c1))
 
     def k_pre_chunk(self, c: int) -> np.ndarray:
         """[C][Hkv][D] bf16 bits, pre-RoPE keys of chunk c."""

@@ -44,6 +44,9 @@
  *    ("injected device failure") where it would first touch the device, with
  *    nothing enqueued, so callers can test their device-error paths on a host
  *    without a GPU.
+ *  - Tracing: with the environment variable RTP_ROCTX set to a non-empty value at
+ *    the first call, every call that enqueues work is wrapped in a roctx range
+ *    named after it (visible with rocprofv3 --marker-trace).
  *  - Heads: G = n_q_heads / n_kv_heads; KV head g serves query heads
  *    g*G .. g*G+G-1.  Retrieval KV heads (kv_role[g] == 1) are numbered by rank
  *    r = 0,1,.. in increasing g; retrieval query head g*G+t has the compact index

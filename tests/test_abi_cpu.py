@@ -241,3 +241,28 @@ def test_injected_device_failure(monkeypatch):
     enqueue = {n for n in rtp.EXPORTED if n not in ("rtp_workspace_bytes", "rtp_status_string", "rtp_last_error",
                                                     "rtp_version", "rtp_decode_step_noalloc_max_bytes")}
     assert enqueue == set(calls)
+
+
+def test_roctx_ranges_behind_env_flag():
+    """RTP_ROCTX=1 makes the library open the roctx library at its first call and wrap
+    every call in a range (here a call that fails its host checks); without the flag the
+    roctx library is never loaded."""
+    import subprocess
+    import sys
+    code = ("import ctypes as C\n"
+            "from head_wise_sparse_amd import rtp\n"
+            "lib = rtp.load()\n"
+            "L = rtp.Layer(1, 8, 2, 128, 4096, [1, 0], 4, 64)\n"
+            "assert lib.rtp_window_sink_attn(L.desc, 0, 16, 16, 16, 0.1, 16, 16, 1 << 20, None) == rtp.RTP_EINVAL\n"
+            "print('roctx' in open('/proc/self/maps').read())\n")
+    seen = {}
+    for flag in ("1", ""):
+        env = dict(os.environ, RTP_ROCTX=flag)
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                           timeout=120)
+        assert r.returncode == 0, r.stderr[-2000:]
+        seen[flag] = r.stdout.strip().splitlines()[-1]
+    assert seen[""] == "False"
+    roctx_present = any(os.path.exists(os.path.join(d, n)) for d in ("/opt/rocm/lib",)
+                        for n in ("librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"))
+    assert seen["1"] == str(roctx_present)

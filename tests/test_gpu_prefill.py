@@ -58,8 +58,8 @@ def _check_rows(cfg, pi, k, v, out, rows_of_head):
         for r in rows:
             c = r // cfg.chunk
             if c not in qs:
-                qs[c] = pi.q_chunk(c, heads=[h])
-        q_rows = np.stack([qs[r // cfg.chunk][r - (r // cfg.chunk) * cfg.chunk, h] for r in rows])
+                qs[c] = pi.q_head(c, h)
+        q_rows = np.stack([qs[r // cfg.chunk][r - (r // cfg.chunk) * cfg.chunk] for r in rows])
         ref = O.prefill_rows(q_rows, rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
         got = out[rows, h] if isinstance(out, np.ndarray) else np.stack([out[int(r)][h] for r in rows])
         e, _ = P.check_outputs(got, ref, f"head {h} ({'retrieval' if cfg.kv_role[g] else 'local'})")
@@ -114,7 +114,7 @@ def test_prefill_small_all_rows(over):
     for h in heads:
         g = h // G
         rows = np.arange(cfg.seq_len)
-        q_rows = np.concatenate([pi.q_chunk(c, heads=[h])[:, h] for c in range(cfg.n_chunks)])
+        q_rows = np.concatenate([pi.q_head(c, h) for c in range(cfg.n_chunks)])
         ref = O.prefill_rows(q_rows, rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
         P.check_outputs(out[:, h], ref, f"head {h}")
     _check_kidx(cfg, pi, kp, kidx)
@@ -136,7 +136,7 @@ def test_prefill_query_group_sizes(hq, hkv, retr):
     for h in sorted({0, 1, G - 1, G, hq // 2 + 1, hq - 1} & set(range(hq))):
         g = h // G
         rows = np.arange(cfg.seq_len)
-        q_rows = np.concatenate([pi.q_chunk(c, heads=[h])[:, h] for c in range(cfg.n_chunks)])
+        q_rows = np.concatenate([pi.q_head(c, h) for c in range(cfg.n_chunks)])
         ref = O.prefill_rows(q_rows, rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
         P.check_outputs(out[:, h], ref, f"head {h} (G={G})")
     _check_kidx(cfg, pi, kp, kidx)
@@ -163,7 +163,7 @@ def test_prefill_head_dim_64(over):
     for h in sorted({0, 1, G - 1, G, 3 * G, Hq // 2 + 1, Hq - 1} & set(range(Hq))):
         g = h // G
         rows = np.arange(cfg.seq_len)
-        q_rows = np.concatenate([pi.q_chunk(c, heads=[h])[:, h] for c in range(cfg.n_chunks)])
+        q_rows = np.concatenate([pi.q_head(c, h) for c in range(cfg.n_chunks)])
         ref = O.prefill_rows(q_rows, rows, k[g], v[g], bool(cfg.kv_role[g]), cfg.n_sinks, cfg.window)
         P.check_outputs(out[:, h], ref, f"head {h} (D=64, G={G})")
     _check_kidx(cfg, pi, kp, kidx)
@@ -201,7 +201,7 @@ def test_prefill_ignores_rows_past_the_chunk(retr):
         for h in (0, 1, G, Hq - 1):
             g = h // G
             rows = np.arange(c0, c1)
-            ref = O.prefill_rows(pi.q_chunk(c, heads=[h])[:, h], rows, k[g], v[g], bool(cfg.kv_role[g]),
+            ref = O.prefill_rows(pi.q_head(c, h), rows, k[g], v[g], bool(cfg.kv_role[g]),
                                  cfg.n_sinks, cfg.window)
             P.check_outputs(ob[:, h], ref, f"chunk {c} head {h}")
 
@@ -224,7 +224,7 @@ def test_prefill_all_local_heads():
         torch.cuda.synchronize()
         ob = rtp.from_device_bf16(o).reshape(c1 - c0, Hq, D)
         for h in (0, G + 1, Hq - 1):
-            ref = O.prefill_rows(pi.q_chunk(c, heads=[h])[:, h], np.arange(c0, c1), k[h // G], v[h // G], False,
+            ref = O.prefill_rows(pi.q_head(c, h), np.arange(c0, c1), k[h // G], v[h // G], False,
                                  cfg.n_sinks, cfg.window)
             P.check_outputs(ob[:, h], ref, f"chunk {c} head {h}")
 
@@ -251,6 +251,7 @@ def test_prefill_is_deterministic():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)         # 64 chunks on the GPU plus the oracle's rows over 1M keys on the host
 def test_prefill_1m_sampled_rows():
     P.require_gpu()
     cfg = W.CONFIGS["prefill_1m"]

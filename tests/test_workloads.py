@@ -60,5 +60,6 @@ def test_prefill_chunks_regenerate_identically():
     assert k.shape == (8, 600, 128) and kp.shape == (600, 8, 128)
     assert np.array_equal(p.k_chunk(2), k[:, 512:600])
     assert np.array_equal(p.q_chunk(1)[:, 3], p.q_chunk(1, heads=[3])[:, 3])
+    assert np.array_equal(p.q_chunk(1)[:, 3], p.q_head(1, 3))
     rows = p.sample_rows(0)
     assert len(rows) == 8 and rows.min() >= 0 and rows.max() < 600
