@@ -68,6 +68,8 @@ def parse():
                     help="generated tokens of the growing-context workload (0: skip it)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run only one part (for profiling); the JSON line is still printed")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timings of the other decode and prefill workloads in the default run")
     ap.add_argument("--report-configs", action="store_true",
                     help="per-config timings of every decode and prefill workload (one JSON report line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -470,17 +472,21 @@ def selection_rows(args):
     return out
 
 
-def report_configs(args):
-    """Per-config timings (not the headline line): the fused decode step of every decode
-    workload at its p, and the chunked prefill of both prefill workloads."""
+HEADLINE_DECODE, HEADLINE_PREFILL = "decode_b4_128k", "prefill_32k"   # the workloads `value` and `prefill` time
+DECODE_CONFIGS = (("decode_tiny_2k", 0.9, 3), ("decode_b8_32k", 0.95, 3), ("decode_b4_128k", 0.95, 3),
+                  ("decode_b1_1m", 0.95, 2))        # (workload, p, cache copies rotated across steps)
+PREFILL_CONFIGS = (("prefill_32k", 0, None), ("prefill_1m", 4, 2))  # (workload, distinct query chunks, passes)
+
+
+def config_timings(args, names):
+    """The fused decode step of each named decode workload at its p (args.steps steps after
+    warm-up, rotating cache copies), and the chunked prefill of each named prefill workload."""
     import torch
-    from head_wise_sparse_amd import rtp
-    torch.cuda.set_device(0)
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    out = {"report": "per-config timings", "device": torch.cuda.get_device_name(0), "rtp": rtp.rtp_version(),
-           "data": "synthetic (seeded)", "configs": {}}
-    for name, p, copies in (("decode_tiny_2k", 0.9, 3), ("decode_b8_32k", 0.95, 3), ("decode_b4_128k", 0.95, 3),
-                            ("decode_b1_1m", 0.95, 2)):
+    out = {}
+    for name, p, copies in DECODE_CONFIGS:
+        if name not in names:
+            continue
         dec = DecodeBench(copies, name)
         for i in range(max(args.warmup, len(dec.sets))):
             dec.step(p, i)
@@ -494,15 +500,17 @@ def report_configs(args):
         us = a.elapsed_time(b) / args.steps * 1e3
         ab = dec.algorithmic_bytes(p)
         gbs = ab["total"] / (us * 1e-6) / 1e9
-        out["configs"][name] = {"p": p, "us_per_step": round(us, 2), "hbm_GBps": round(gbs, 1),
-                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["total"],
-                                "union_tokens": ab["union_tokens"], "sel_mean": ab["sel_mean"],
-                                "sel_median": ab["sel_median"]}
+        out[name] = {"p": p, "us_per_step": round(us, 2), "hbm_GBps": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["total"],
+                     "union_tokens": ab["union_tokens"], "sel_mean": ab["sel_mean"], "sel_median": ab["sel_median"],
+                     "steps": args.steps}
         log(f"{name}: {us:.1f} us/step")
         del dec
         torch.cuda.empty_cache()
-    out["selection_rows"] = selection_rows(args)
-    for name, qd, passes in (("prefill_32k", 0, args.steps), ("prefill_1m", 4, 2)):
+    for name, qd, passes in PREFILL_CONFIGS:
+        if name not in names:
+            continue
+        passes = passes or args.steps
         pre = PrefillBench(name, qd)
         pre.run()
         torch.cuda.synchronize()
@@ -515,12 +523,25 @@ def report_configs(args):
         ms = a.elapsed_time(b) / passes
         fl = pre.flops()["total"]
         tf = fl / (ms * 1e-3) / 1e12
-        out["configs"][name] = {"ms": round(ms, 3), "tflops": round(tf, 1), "mfma_util": round(tf / BF16_PEAK_TFLOPS, 4),
-                                "algorithmic_flops": fl, "chunks": pre.cfg.n_chunks,
-                                "distinct_q_chunks": len(pre.q), "passes": passes}
+        out[name] = {"ms": round(ms, 3), "tflops": round(tf, 1), "mfma_util": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops": fl, "chunks": pre.cfg.n_chunks, "distinct_q_chunks": len(pre.q),
+                     "passes": passes}
         log(f"{name}: {ms:.2f} ms")
         del pre
         torch.cuda.empty_cache()
+    return out
+
+
+def report_configs(args):
+    """Per-config timings of every workload (one JSON report line, not the headline line),
+    plus top-p selection alone on two 1M-token rows."""
+    import torch
+    from head_wise_sparse_amd import rtp
+    torch.cuda.set_device(0)
+    names = [c[0] for c in DECODE_CONFIGS] + [c[0] for c in PREFILL_CONFIGS]
+    out = {"report": "per-config timings", "device": torch.cuda.get_device_name(0), "rtp": rtp.rtp_version(),
+           "data": "synthetic (seeded)", "configs": config_timings(args, names)}
+    out["selection_rows"] = selection_rows(args)
     print(json.dumps(out), flush=True)
 
 
@@ -733,6 +754,13 @@ def main():
     if dec and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dec, prefill=pre is not None)
     res["wall_s_timed"] = round(wall, 3)
+    if dec and pre and not args.no_configs:
+        # the other workloads, timed in this same run (not part of `value`)
+        dec = pre = None
+        torch.cuda.empty_cache()
+        others = [c[0] for c in DECODE_CONFIGS if c[0] != HEADLINE_DECODE] + \
+                 [c[0] for c in PREFILL_CONFIGS if c[0] != HEADLINE_PREFILL]
+        res["other_configs"] = config_timings(args, others)
     print(json.dumps(res))
 
 
