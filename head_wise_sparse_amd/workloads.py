@@ -273,13 +273,15 @@ def make_decode_inputs(cfg: DecodeConfig, n_cap: Optional[int] = None,
         v[b, g, :N] = _normal_bf16(_rng(cid, T_V, b, g), (N, D))
         if g in ret:
             r = ret.index(g)
-            proj = bf16_bits_to_f32(k_pre).astype(np.float64) @ wk64[r]
+            # products by numpy's own loops, not BLAS: BLAS called from several of these
+            # worker threads at once has returned differing results from run to run
+            proj = np.einsum("nd,di->ni", bf16_bits_to_f32(k_pre).astype(np.float64), wk64[r], optimize=False)
             k_idx[b, r, :N] = f32_to_bf16_bits(proj.astype(np.float32))
             if n_needles:
                 npos = np.sort(_rng(cid, T_NEEDLE, b, r).choice(N, size=n_needles, replace=False))
                 needle_pos[b, r] = npos
-                qi = [bf16_bits_to_f32(q_pre[b, g * G + t]).astype(np.float64) @ wq64[r * G + t]
-                      for t in range(G)]
+                qi = [np.einsum("d,di->i", bf16_bits_to_f32(q_pre[b, g * G + t]).astype(np.float64),
+                                wq64[r * G + t], optimize=False) for t in range(G)]
                 needle = 4.0 * np.mean(np.stack(qi), axis=0)
                 k_idx[b, r, npos] = f32_to_bf16_bits(needle.astype(np.float32))[None, :]
 
