@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0
 # changes the figure no longer describes the kernel and `traffic` is reported as null.
 COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
 MEASURED_KIB = {
-    "prefill_attn": {"src": ("rtp_prefill.hip", "509fac1fb066501a"),
-                     "fetch": 211098.1, "write": 41591.2},
+    "prefill_attn": {"src": ("rtp_prefill.hip", "9c8e4c2435f8d8e8"),
+                     "fetch": 210059.1, "write": 41721.7},
     "sparse_decode": {"src": ("decode_dev.hpp", "6a3a214974469809"),
-                      "fetch": 172611.3 + 1086.5, "write": 2176.3 + 8.0},
+                      "fetch": 172611.6 + 1086.5, "write": 2176.2 + 8.0},
 }
 
 
