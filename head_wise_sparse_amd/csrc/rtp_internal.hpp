@@ -96,12 +96,14 @@ __device__ __forceinline__ int live_ctx(const int64_t* live, int n_max) {
   return int(v < 1 ? 1 : (v > n_max ? int64_t(n_max) : v));
 }
 
-// Top-p selection (four launches; the workspace is zero before and after a call).
+// Top-p selection (four launches, or one for short rows; the workspace is zero before
+// and after a call).
 constexpr int kSelThreads = 256;
 constexpr int kSelItems = 16;
 constexpr int kSelTile = kSelThreads * kSelItems;               // tokens per block ...
 constexpr int kSelItemsLong = 32;                                // ... or twice that when a pass would
                                                                  // otherwise take more than one round of blocks
+constexpr int kSelSmallMax = kSelThreads * kSelItemsLong;       // rows up to this take one block each
 constexpr int kBins = 2048;                                     // 11-bit digits (last level 10 bits)
 constexpr int kTabDigits = 1024;                                // last-level digits (10 bits)
 struct SelLevelState {           // what is known after resolving one level's digit

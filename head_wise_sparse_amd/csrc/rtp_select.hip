@@ -35,6 +35,9 @@
 //             its candidate counts at or above each low digit, and the block reads the
 //             two entries at t from it: O(1) per earlier tile whatever the scores.
 //             It also writes the range index of every list when asked for.
+// Rows of at most kSelSmallMax tokens take one launch instead (k_sel_small): one block per
+// row keeps the row's scores in registers and each level's histogram in LDS, and applies
+// the same rules, so it writes the same lists, counts and range index.
 // The workspace is all zero when a call starts and when it ends: each launch clears
 // what earlier launches left and nobody reads any more (hist<2> the level-0
 // histogram, compact the level-1 histogram), and the last compaction block of a row
@@ -81,17 +84,30 @@ struct Resolved {            // result of resolving one level's digit
   uint32_t tied;             // count in the resolved bin (meaningful at level 2)
 };
 
-// Resolve the digit of `level` from the finished histogram of that level.  Called by
-// one full wave; every lane returns the same result.  `in` carries the state after
-// the previous level (ignored for level 0, where the target is ceil(p * Z), or k when
-// the bins are weighed by their counts for the static top-k rule).
-__device__ Resolved resolve_level(const SelRows& R, int row, int level, const Resolved& in, float top_p,
-                                  bool by_count, int64_t k_target, int lane) {
-  const int nc = level == 2 ? 32 : kCoarse;
-  const uint64_t* cm = R.cmass + (int64_t(row) * 3 + level) * kCoarse;
-  const uint32_t* cc = R.ccnt + (int64_t(row) * 3 + level) * kCoarse;
-  const uint32_t c_l = lane < nc ? ld_rlx(cc + lane) : 0u;
-  const uint64_t m_l = by_count ? uint64_t(c_l) : (lane < nc ? ld_rlx(cm + lane) : 0ull);
+// Loads of a finished histogram: global (relaxed atomics, written by earlier launches
+// through atomics) or LDS (the single-block path).
+struct LdGlobal {
+  __device__ __forceinline__ uint64_t operator()(const uint64_t* p) const { return ld_rlx(p); }
+  __device__ __forceinline__ uint32_t operator()(const uint32_t* p) const { return ld_rlx(p); }
+};
+struct LdShared {
+  __device__ __forceinline__ uint64_t operator()(const uint64_t* p) const { return *p; }
+  __device__ __forceinline__ uint32_t operator()(const uint32_t* p) const { return *p; }
+};
+
+// Resolve the digit of `level` from a finished histogram: its coarse summary (nc bins
+// of kFinePer fine bins each: cm, cc) and its fine bins (fm, fc).  Called by one full
+// wave; every lane returns the same result.  `in` carries the state after the previous
+// level (ignored for level 0, where the target is ceil(p * Z), or k when the bins are
+// weighed by their counts for the static top-k rule).  The digit is the one where the
+// mass accumulated from the top first reaches what is still needed: unique, so any
+// split of the bins into coarse groups finds the same one.
+template <typename LD>
+__device__ __forceinline__ Resolved resolve_digit(const uint64_t* cm, const uint32_t* cc, const uint64_t* fm0,
+                                                  const uint32_t* fc0, int nc, int level, const Resolved& in,
+                                                  float top_p, bool by_count, int64_t k_target, int lane, LD ld) {
+  const uint32_t c_l = lane < nc ? ld(cc + lane) : 0u;
+  const uint64_t m_l = by_count ? uint64_t(c_l) : (lane < nc ? ld(cm + lane) : 0ull);
   Resolved o = in;
   if (level == 0) {
     const uint64_t z = wave_sum<uint64_t>(m_l);
@@ -117,10 +133,10 @@ __device__ Resolved resolve_level(const SelRows& R, int row, int level, const Re
   const uint32_t cnt_above_c = __shfl(SC - c_l, cs, 64);
   need -= above_c;
   // fine bins under the chosen coarse bin
-  const uint64_t* fm = R.mass + (int64_t(row) * 3 + level) * kBins + cs * kFinePer;
-  const uint32_t* fc = R.cnt + (int64_t(row) * 3 + level) * kBins + cs * kFinePer;
-  const uint32_t fc_l = lane < kFinePer ? ld_rlx(fc + lane) : 0u;
-  const uint64_t fm_l = by_count ? uint64_t(fc_l) : (lane < kFinePer ? ld_rlx(fm + lane) : 0ull);
+  const uint64_t* fm = fm0 + cs * kFinePer;
+  const uint32_t* fc = fc0 + cs * kFinePer;
+  const uint32_t fc_l = lane < kFinePer ? ld(fc + lane) : 0u;
+  const uint64_t fm_l = by_count ? uint64_t(fc_l) : (lane < kFinePer ? ld(fm + lane) : 0ull);
   const uint64_t FS = wave_suffix_incl<uint64_t>(fm_l, lane);
   const uint32_t FSC = wave_suffix_incl<uint32_t>(fc_l, lane);
   const uint64_t fown = __ballot(lane < kFinePer && FS >= need && FS - fm_l < need);
@@ -131,6 +147,14 @@ __device__ Resolved resolve_level(const SelRows& R, int row, int level, const Re
   o.tied = __shfl(fc_l, fs, 64);
   o.prefix = level == 0 ? digit : ((o.prefix << (level == 1 ? 11 : 10)) | digit);
   return o;
+}
+
+// The same from a row's histogram in the workspace.
+__device__ Resolved resolve_level(const SelRows& R, int row, int level, const Resolved& in, float top_p,
+                                  bool by_count, int64_t k_target, int lane) {
+  const int64_t h = int64_t(row) * 3 + level;
+  return resolve_digit(R.cmass + h * kCoarse, R.ccnt + h * kCoarse, R.mass + h * kBins, R.cnt + h * kBins,
+                       level == 2 ? 32 : kCoarse, level, in, top_p, by_count, k_target, lane, LdGlobal{});
 }
 
 // Level 2 (1024 bins, histogram complete since the previous launch) in one round trip:
@@ -572,6 +596,163 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   }
 }
 
+// Rows of at most kSelSmallMax tokens: one block holds the whole row in registers, so the
+// three levels and the compaction run in one launch, with each level's histogram in LDS
+// and no workspace.  The keys, fixed-point weights, row max, owner rule and tie count are
+// those of the four-launch path; the list, its count and the range index are unique
+// functions of them, so both paths write the same bits.
+template <int LEVEL, int ITEMS>
+__device__ __forceinline__ Resolved small_level(const SelArgs& a, const float (&sv)[ITEMS], float m, float wscale,
+                                                int n_ctx, const Resolved& in, uint64_t* h_m, uint32_t* h_c,
+                                                uint64_t* c_m, uint32_t* c_c, Resolved* s_res) {
+  constexpr int NB = LEVEL == 2 ? 1024 : 2048;
+  constexpr int SHIFT = LEVEL == 0 ? 21 : (LEVEL == 1 ? 10 : 0);
+  constexpr int PSHIFT = LEVEL == 1 ? 21 : 10;
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < NB; i += kSelThreads) {
+    h_m[i] = 0;
+    h_c[i] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int j = it * kSelThreads + tid;
+    const uint32_t key = score_key(sv[it]);
+    if (j < n_ctx && (LEVEL == 0 || (key >> PSHIFT) == in.prefix)) {
+      const uint32_t d = (key >> SHIFT) & uint32_t(NB - 1);
+      if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m, wscale));
+      atomicAdd(&h_c[d], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid < NB / kFinePer) {
+    uint64_t sm = 0;
+    uint32_t sc = 0;
+#pragma unroll 8
+    for (int i = 0; i < kFinePer; ++i) {
+      const int f = tid * kFinePer + ((i + tid) & (kFinePer - 1));
+      sm += h_m[f];
+      sc += h_c[f];
+    }
+    c_m[tid] = sm;
+    c_c[tid] = sc;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const Resolved o =
+        resolve_digit(c_m, c_c, h_m, h_c, NB / kFinePer, LEVEL, in, a.top_p, a.by_count, a.k_target, lane, LdShared{});
+    if (lane == 0) *s_res = o;
+  }
+  __syncthreads();
+  return *s_res;
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kSelThreads) void k_sel_small(SelArgs a) {
+  constexpr int NW = kSelThreads / 64;
+  constexpr int PL = ITEMS * NW / 64;                 // (item, wave) counts per lane of the scanning wave
+  static_assert(ITEMS * NW % 64 == 0 && ITEMS * kSelThreads <= kSelSmallMax, "one block, one scanning wave");
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int row = blockIdx.x;
+  __shared__ uint64_t h_m[kBins];
+  __shared__ uint32_t h_c[kBins];
+  __shared__ uint64_t c_m[kCoarse];
+  __shared__ uint32_t c_c[kCoarse];
+  __shared__ Resolved s_res;
+  __shared__ float s_red[NW];
+  __shared__ uint32_t s_wa[ITEMS * NW], s_we[ITEMS * NW];   // counts, then exclusive prefixes
+  __shared__ uint32_t s_r;
+  const int n_ctx = live_ctx(a.live, a.n_ctx);
+  const int nsplit = (n_ctx + kDecRange - 1) / kDecRange;         // ranges of the live context
+  const float wscale = mass_wscale(n_ctx);
+  const float* sp = a.scores + int64_t(row) * a.n_cap;
+  float sv[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int j = it * kSelThreads + tid;
+    sv[it] = sp[j < n_ctx ? j : n_ctx - 1];
+  }
+  float m = 0.0f;                                   // unused by the static top-k rule
+  if (!a.by_count) m = a.score_part ? row_max_from_partials(a, row, 0, tid, s_red, n_ctx) : a.row_max[row];
+  Resolved res{};
+  res = small_level<0, ITEMS>(a, sv, m, wscale, n_ctx, res, h_m, h_c, c_m, c_c, &s_res);
+  res = small_level<1, ITEMS>(a, sv, m, wscale, n_ctx, res, h_m, h_c, c_m, c_c, &s_res);
+  res = small_level<2, ITEMS>(a, sv, m, wscale, n_ctx, res, h_m, h_c, c_m, c_c, &s_res);
+  const uint32_t t = res.prefix;
+  if (tid == 0) {
+    // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
+    const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(t), m, wscale);
+    const uint64_t rem = res.target - res.above;
+    uint64_t r = (w == 0) ? res.tied : (rem + w - 1) / w;
+    if (r < 1) r = 1;
+    if (r > res.tied) r = res.tied;
+    s_r = uint32_t(r);
+    const uint32_t cnt = res.cnt_above + uint32_t(r);
+    a.sel_count[row] = int32_t(cnt);
+    if (a.starts) a.starts[int64_t(row) * (a.nsplit + 1) + nsplit] = int32_t(cnt);
+  }
+  uint32_t fa = 0, fe = 0;
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int j = it * kSelThreads + tid;
+    const uint32_t key = score_key(sv[it]);
+    const bool above = j < n_ctx && key > t, tied = j < n_ctx && key == t;
+    fa |= uint32_t(above) << it;
+    fe |= uint32_t(tied) << it;
+    const uint64_t ba = __ballot(above), be = __ballot(tied);
+    if (lane == 0) {
+      s_wa[it * NW + wave] = __popcll(ba);
+      s_we[it * NW + wave] = __popcll(be);
+    }
+  }
+  __syncthreads();
+  // exclusive prefix of the per-(item, wave) counts, in token order (item-major)
+  if (wave == 0) {
+    uint32_t va[PL], ve[PL], sa = 0, se = 0;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      va[k] = s_wa[PL * lane + k];
+      ve[k] = s_we[PL * lane + k];
+      sa += va[k];
+      se += ve[k];
+    }
+    uint32_t xa = sa, xe = se;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t ya = __shfl_up(xa, o, 64), ye = __shfl_up(xe, o, 64);
+      if (lane >= o) {
+        xa += ya;
+        xe += ye;
+      }
+    }
+    xa -= sa;
+    xe -= se;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      s_wa[PL * lane + k] = xa;
+      s_we[PL * lane + k] = xe;
+      xa += va[k];
+      xe += ve[k];
+    }
+  }
+  __syncthreads();
+  const uint32_t r = s_r;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* out = a.sel_idx + int64_t(row) * a.n_cap;
+  constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const uint32_t ca = s_wa[it * NW + wave], ce = s_we[it * NW + wave];
+    if (a.starts && it % IT_PER_RANGE == 0 && tid == 0 && it / IT_PER_RANGE < nsplit)
+      a.starts[int64_t(row) * (a.nsplit + 1) + it / IT_PER_RANGE] = int32_t(ca + (ce < r ? ce : r));
+    const bool above = (fa >> it) & 1u, tied = (fe >> it) & 1u;
+    const uint32_t a_before = ca + __popcll(__ballot(above) & lt);
+    const uint32_t e_before = ce + __popcll(__ballot(tied) & lt);
+    const bool take = above || (tied && e_before < r);
+    if (take) out[a_before + (e_before < r ? e_before : r)] = it * kSelThreads + tid;
+  }
+}
+
 // top_p >= 1: every token, in order.
 // (nsplit: the range index's row stride - 1; live: the device-length step's context word)
 __global__ __launch_bounds__(256) void k_sel_all(int n_max, const int64_t* live, int64_t n_cap,
@@ -692,6 +873,13 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
     hipLaunchKernelGGL(k_sel_all, dim3(unsigned((a.n_ctx + 255) / 256 + 1), rows), dim3(256), 0, s, a.n_ctx,
                        a.live, a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
     return check_launch("k_sel_all");
+  }
+  if (a.n_ctx <= kSelSmallMax) {         // one block per row
+    if (a.n_ctx <= kSelThreads * kSelItems)
+      hipLaunchKernelGGL((k_sel_small<kSelItems>), dim3(rows), dim3(kSelThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_sel_small<kSelItemsLong>), dim3(rows), dim3(kSelThreads), 0, s, a);
+    return check_launch("k_sel_small");
   }
   // tile size: 16 scores per thread, or 32 when that keeps a pass to one round of blocks
   SelArgs b = a;

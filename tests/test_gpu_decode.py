@@ -187,6 +187,19 @@ def _edge_rows():
     z[:, ::7] = 0.0
     z[:, 3::7] = -0.0
     yield "signed_zeros", z, 0.8
+    # rows of at most 8192 tokens take the single-block path: its boundaries (4096 and 8192
+    # tokens: 16 or 32 scores per thread), a narrow spread that leaves the cut to the last
+    # digit, a wide one, and near-equal clusters
+    rs = np.random.default_rng(12)
+    yield "short_narrow", (5 + rs.standard_normal((3, 8192)) * 1e-3).astype(np.float32), 0.9
+    yield "short_wide", (rs.standard_normal((2, 8191)) * 300).astype(np.float32), 0.95
+    yield "short_at_4096", (rs.standard_normal((2, 4096)) * 3).astype(np.float32), 0.9
+    yield "short_at_4097", np.round(rs.standard_normal((2, 4097)) * 3, 1).astype(np.float32), 0.7
+    c = np.full((2, 7000), -12.0, np.float32)
+    pos = rs.choice(7000, 600, replace=False)
+    c[:, pos] = (np.float32(1.0).view(np.uint32) + rs.integers(0, 40, 600).astype(np.uint32)).view(np.float32)
+    yield "short_clustered", c, 0.5
+    yield "short_many_rows", rs.standard_normal((300, 1500)).astype(np.float32) * 2, 0.9
     yield "wide_spread", (rng.standard_normal((2, 9000)) * 300).astype(np.float32), 0.95
     yield "narrow_spread", (5 + rng.standard_normal((2, 20000)) * 1e-3).astype(np.float32), 0.9
     yield "ragged_many_tiles", rng.standard_normal((4, 2048 * 5 + 3)).astype(np.float32) * 3, 0.99
@@ -657,6 +670,18 @@ def test_topk_select_exact(k):
     s32[2] = 0.0                                          # everything tied
     s32[3, 1000:1300] = -0.0
     L = rtp.Layer(s32.shape[0], 1, 1, 64, n + 100, [1], 0, 1)
+    _run_topk(L, n, s32, k)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 1), (8192, 7), (8192, 3000), (8191, 8190), (4096, 1000), (1000, 999)])
+def test_topk_select_exact_short_rows(n, k):
+    """Static top-k on rows short enough for the single-block path, with exact ties."""
+    P.require_gpu()
+    rng = np.random.default_rng(n + k)
+    s32 = np.round(rng.standard_normal((4, n)) * 3, 1).astype(np.float32)
+    s32[1, ::3] = 9.0                                     # a tie group at the top
+    s32[2] = -1.5                                         # everything tied
+    L = rtp.Layer(s32.shape[0], 1, 1, 64, n + 64, [1], 0, 1)
     _run_topk(L, n, s32, k)
 
 
