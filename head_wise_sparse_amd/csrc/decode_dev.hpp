@@ -44,6 +44,13 @@ struct DecArgs {
   const uint16_t* v;
   const int32_t* sel_idx;     // sparse only
   const int32_t* starts;      // sparse only: [rows][nsplit + 1]
+  // sparse, members taken from the scores (the decode step): the scores [rows][n_cap], the
+  // threshold key of every row, and the lists to write (null: not written); all_tokens:
+  // every token of the context is a member (top_p >= 1)
+  const float* scores;
+  const uint32_t* thr;
+  int32_t* sel_out;
+  int all_tokens;
   float* part;                // [rows][nsplit * nsub][D + 4]: accumulator, max, sum (16-byte rows)
   int n_ctx;                  // the context (device-length step: its bound n_max)
   const int64_t* live;        // device-length step: the context's device word, else null
@@ -69,7 +76,12 @@ struct DecArgs {
 // One block of split-K decode: partial slot `slot` of group `grp` (= b * n_heads_of_kind
 // + rank).  Sparse path: slot = range * nsub + sub; the block builds the union list of
 // index range `range` and takes the sub-th of nsub equal slices of it (whole stages).
-template <int D, int G, bool SPARSE>
+// A head's members of the range come from its selected list (FROM_SCORES false) or, in
+// the decode step, from its scores, threshold key t and range index (FROM_SCORES true):
+// every token with key > t, and the first (starts[q+1] - starts[q] - #above) tokens with
+// key == t, which is the list the compaction writes.  The block with sub == 0 writes that
+// part of the list, last.
+template <int D, int G, bool SPARSE, bool FROM_SCORES = false>
 __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp) {
   const int split = SPARSE ? slot / a.nsub : slot;       // index range (sparse) / list slice (window)
   const int sub = SPARSE ? slot % a.nsub : 0;
@@ -104,6 +116,16 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
   __shared__ int s_wcnt[NW];
   __shared__ float s_wm[NW][G], s_wl[NW][G];
   __shared__ float s_wacc[NW][G][D];
+  // decode step (members from the membership words): per (head, item, wave) above / tied
+  // counts, then their exclusive prefixes; ties taken per head; list bounds; member flags
+  constexpr int NE = (RANGE / kDecThreads) * NW;
+  constexpr int GF = (SPARSE && FROM_SCORES) ? G : 1;
+  static_assert(!(SPARSE && FROM_SCORES) || (G * NE <= kDecThreads && 64 % NE == 0), "one lane per entry");
+  __shared__ __align__(16) uint32_t s_ca[GF * NE];
+  __shared__ __align__(16) uint32_t s_ce[GF * NE];
+  __shared__ uint32_t s_take[GF];
+  __shared__ int s_lo[GF], s_hi[GF];
+  __shared__ uint64_t s_wd[GF][RANGE / kDecThreads][NW][2];      // above / tied words of (head, item, wave)
 
   uint32_t qw[G][4];
 #pragma unroll
@@ -118,40 +140,156 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
   int U, j0 = 0, p0 = 0, e0 = 0;
   if constexpr (SPARSE) {
     j0 = split * RANGE;
-    for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
-    __syncthreads();
-    uint8_t* hm = reinterpret_cast<uint8_t*>(s_hm);
     // A head's selected indices are distinct, so at most RANGE of them fall in the
     // range: SP per thread.  All loads are issued before any membership byte is set.
     constexpr int SP = RANGE / kDecThreads;
+    // range index entries: loaded unconditionally (every launched range has both), so that
+    // they are one batch of loads rather than a chain of guarded ones
+    // (a zero held in a vector register makes them vector loads, whose wait is separate from
+    // that of the scalar loads of the kernel arguments and membership words)
+    int vz = 0;
+    asm volatile("" : "+v"(vz));
     int lo[G], hi[G];
 #pragma unroll
     for (int t = 0; t < G; ++t) {
-      const int64_t so = int64_t(grp * G + t) * (a.nsplit + 1) + split;
-      // clamped: the range index may come from the caller; a range past the live context is empty
-      hi[t] = split < nsplit_live ? min(max(a.starts[so + 1], 0), n_ctx) : 0;
-      lo[t] = split < nsplit_live ? min(max(a.starts[so], 0), hi[t]) : 0;
+      const int64_t so = int64_t(grp * G + t) * (a.nsplit + 1) + split + vz;
+      lo[t] = a.starts[so];
+      hi[t] = a.starts[so + 1];
     }
-    int pos[G][SP];
+    // members from the scores: the range's scores (position u * kDecThreads + tid) and the
+    // threshold keys of every head
+    float sc[FROM_SCORES ? G : 1][SP];
+    uint32_t thr[FROM_SCORES ? G : 1];
+    if constexpr (FROM_SCORES) {
+      if (!a.all_tokens) {
 #pragma unroll
-    for (int t = 0; t < G; ++t) {
-      const int32_t* sr = a.sel_idx + int64_t(grp * G + t) * a.n_cap;
+        for (int t = 0; t < G; ++t) {
+          const float* sr = a.scores + int64_t(grp * G + t) * a.n_cap;
 #pragma unroll
-      for (int u = 0; u < SP; ++u) {
-        // unconditional load (index 0 stands in for out-of-range slots) so that the
-        // compiler keeps every load in flight instead of waiting inside a branch
-        const int k = lo[t] + u * kDecThreads + tid;
-        const int v = sr[k < hi[t] ? k : 0];
-        // an index outside [0, n_ctx) (a malformed list from the caller) is dropped, so no
-        // cache row at or past n_ctx is ever read
-        pos[t][u] = (k < hi[t] && v >= 0 && v < n_ctx) ? v - j0 : -1;
+          for (int u = 0; u < SP; ++u) {
+            const int j = j0 + u * kDecThreads + tid;
+            sc[t][u] = sr[j < n_ctx ? j : n_ctx - 1];             // unconditional, clamped
+          }
+          thr[t] = a.thr[grp * G + t];
+        }
       }
     }
+    for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
+    __syncthreads();
+    uint8_t* hm = reinterpret_cast<uint8_t*>(s_hm);
 #pragma unroll
-    for (int t = 0; t < G; ++t)
+    for (int t = 0; t < G; ++t) {
+      // clamped: the range index may come from the caller; a range past the live context is empty
+      hi[t] = split < nsplit_live ? min(max(hi[t], 0), n_ctx) : 0;
+      lo[t] = split < nsplit_live ? min(max(lo[t], 0), hi[t]) : 0;
+    }
+    if constexpr (FROM_SCORES) {
+      // position u * kDecThreads + tid of the range, for every head; a range past the live
+      // context is empty
+      const bool live_range = split < nsplit_live;
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      if (tid == 0) {
 #pragma unroll
-      for (int u = 0; u < SP; ++u)
-        if (pos[t][u] >= 0 && pos[t][u] < RANGE) hm[t * RANGE + pos[t][u]] = 1;
+        for (int t = 0; t < G; ++t) {
+          s_lo[t] = lo[t];
+          s_hi[t] = hi[t];
+        }
+      }
+      if (a.all_tokens) {
+#pragma unroll
+        for (int u = 0; u < SP; ++u) {
+          const bool in = live_range && j0 + u * kDecThreads + tid < n_ctx;
+#pragma unroll
+          for (int t = 0; t < G; ++t)
+            if (in) hm[t * RANGE + u * kDecThreads + tid] = 1;
+        }
+      } else {
+        // This wave's 64 tokens of item u as words (ballots): above t (A) and tied with t (T);
+        // tokens above t are members at once, tied ones once the range's take is known
+        uint64_t wT[G][SP];
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+#pragma unroll
+          for (int u = 0; u < SP; ++u) {
+            const bool in = live_range && j0 + u * kDecThreads + tid < n_ctx;
+            const uint32_t key = score_key(sc[t][u]);
+            const bool above = in && key > thr[t], tied = in && key == thr[t];
+            const uint64_t wA = __ballot(above);
+            wT[t][u] = __ballot(tied);
+            if (above) hm[t * RANGE + u * kDecThreads + tid] = 1;
+            if (lane == 0) {
+              s_ca[t * NE + u * NW + wave] = __popcll(wA);
+              s_ce[t * NE + u * NW + wave] = __popcll(wT[t][u]);
+              s_wd[t][u][wave][0] = wA;
+              s_wd[t][u][wave][1] = wT[t][u];
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < G) {                   // thread h: exclusive prefixes of head h's NE entries
+          uint4* pa = reinterpret_cast<uint4*>(s_ca + tid * NE);
+          uint4* pe = reinterpret_cast<uint4*>(s_ce + tid * NE);
+          uint4 va[NE / 4], ve[NE / 4];
+#pragma unroll
+          for (int k = 0; k < NE / 4; ++k) {
+            va[k] = pa[k];
+            ve[k] = pe[k];
+          }
+          uint32_t xa = 0, xe = 0;
+#pragma unroll
+          for (int k = 0; k < NE / 4; ++k) {
+            const uint32_t a0 = va[k].x, a1 = va[k].y, a2 = va[k].z, a3 = va[k].w;
+            const uint32_t e0 = ve[k].x, e1 = ve[k].y, e2 = ve[k].z, e3 = ve[k].w;
+            pa[k] = make_uint4(xa, xa + a0, xa + a0 + a1, xa + a0 + a1 + a2);
+            pe[k] = make_uint4(xe, xe + e0, xe + e0 + e1, xe + e0 + e1 + e2);
+            xa += a0 + a1 + a2 + a3;
+            xe += e0 + e1 + e2 + e3;
+          }
+          // ties this range takes: its list length minus its tokens above t
+          int lo_h = lo[0], hi_h = hi[0];
+#pragma unroll
+          for (int t = 1; t < G; ++t)
+            if (tid == t) {
+              lo_h = lo[t];
+              hi_h = hi[t];
+            }
+          const int take_i = hi_h - lo_h - int(xa);
+          s_take[tid] = take_i < 0 ? 0u : (uint32_t(take_i) > xe ? xe : uint32_t(take_i));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+#pragma unroll
+          for (int u = 0; u < SP; ++u) {
+            if (wT[t][u]) {              // ties among these tokens: the range takes its first take
+              const uint32_t e_before = s_ce[t * NE + u * NW + wave] + __popcll(wT[t][u] & lt);
+              if (((wT[t][u] >> lane) & 1ull) && e_before < s_take[t]) hm[t * RANGE + u * kDecThreads + tid] = 1;
+            }
+          }
+        }
+      }
+    } else {
+      int pos[G][SP];
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        const int32_t* sr = a.sel_idx + int64_t(grp * G + t) * a.n_cap;
+#pragma unroll
+        for (int u = 0; u < SP; ++u) {
+          // unconditional load (index 0 stands in for out-of-range slots) so that the
+          // compiler keeps every load in flight instead of waiting inside a branch
+          const int k = lo[t] + u * kDecThreads + tid;
+          const int v = sr[k < hi[t] ? k : 0];
+          // an index outside [0, n_ctx) (a malformed list from the caller) is dropped, so no
+          // cache row at or past n_ctx is ever read
+          pos[t][u] = (k < hi[t] && v >= 0 && v < n_ctx) ? v - j0 : -1;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int u = 0; u < SP; ++u)
+          if (pos[t][u] >= 0 && pos[t][u] < RANGE) hm[t * RANGE + pos[t][u]] = 1;
+    }
     __syncthreads();
     // ordered union of the G membership arrays: thread tid owns positions tid*8 .. tid*8+7
     constexpr int PER = RANGE / kDecThreads;
@@ -340,6 +478,31 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
     if (d == 0) {
       pr[D] = M;
       pr[D + 1] = Lsum;
+    }
+  }
+  if constexpr (SPARSE && FROM_SCORES) {
+    // this range's part of the selected lists, written last: a barrier waits for every
+    // store in flight, and none follows here
+    if (a.sel_out && sub == 0 && !a.all_tokens) {
+      constexpr int SP = RANGE / kDecThreads;
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        const uint32_t take = s_take[t];
+        const int lo_t = s_lo[t], hi_t = s_hi[t];
+        int32_t* out = a.sel_out + int64_t(grp * G + t) * a.n_cap;
+#pragma unroll
+        for (int u = 0; u < SP; ++u) {
+          const uint64_t wA = s_wd[t][u][wave][0], wT = s_wd[t][u][wave][1];
+          const bool above = (wA >> lane) & 1ull, tied = (wT >> lane) & 1ull;
+          const uint32_t a_before = s_ca[t * NE + u * NW + wave] + __popcll(wA & lt);
+          const uint32_t e_before = s_ce[t * NE + u * NW + wave] + __popcll(wT & lt);
+          if (above || (tied && e_before < take)) {
+            const int at = lo_t + int(a_before + (e_before < take ? e_before : take));
+            if (at < hi_t) out[at] = j0 + u * kDecThreads + tid;
+          }
+        }
+      }
     }
   }
 }

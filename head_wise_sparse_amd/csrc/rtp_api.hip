@@ -134,7 +134,7 @@ size_t score_ws_bytes(const Layer& L, int64_t n_ctx) {
 SelLayout sel_layout(const Layer& L) {
   SelLayout s{};
   const size_t rows = size_t(L.B) * L.n_ret * L.G;
-  s.nblk_max = int((L.n_cap + kSelTile - 1) / kSelTile);
+  s.nrec_max = int((L.n_cap + kRecTok - 1) / kRecTok);
   size_t off = 0;
   s.hist_mass = off;
   off = round_up(off + rows * 3 * kBins * sizeof(uint64_t), 256);
@@ -149,9 +149,9 @@ SelLayout sel_layout(const Layer& L) {
   s.ctr = off;
   off = round_up(off + rows * 2 * sizeof(uint32_t), 256);
   s.tilerec = off;
-  off = round_up(off + rows * size_t(s.nblk_max) * sizeof(uint4), 256);
+  off = round_up(off + rows * size_t(s.nrec_max) * sizeof(uint4), 256);
   s.tiletab = off;
-  off = round_up(off + rows * size_t(s.nblk_max) * kTabDigits * sizeof(uint16_t), 256);
+  off = round_up(off + rows * size_t(s.nrec_max) * kTabDigits * sizeof(uint16_t), 256);
   s.total = off;
   return s;
 }

@@ -106,6 +106,11 @@ constexpr int kSelItemsLong = 32;                                // ... or twice
 constexpr int kSelSmallMax = kSelThreads * kSelItemsLong;       // rows up to this take one block each
 constexpr int kBins = 2048;                                     // 11-bit digits (last level 10 bits)
 constexpr int kTabDigits = 1024;                                // last-level digits (10 bits)
+// The last radix pass leaves one record per kRecTok tokens (one decode range), so that
+// the range index can be formed from the records alone.
+constexpr int kRecTok = RTP_SEL_RANGE;
+static_assert(kRecTok % kSelThreads == 0 && (kSelItems * kSelThreads) % (2 * kRecTok) == 0,
+              "whole records per tile, an even number of them");
 struct SelLevelState {           // what is known after resolving one level's digit
   uint32_t prefix;               // key bits resolved so far
   uint32_t cnt_above;            // tokens strictly above the prefix
@@ -120,7 +125,7 @@ struct SelRowState {             // one per score row, lives in the workspace
 static_assert(sizeof(SelRowState) == 56, "row state layout");
 struct SelLayout {                // depends on the layer only (n_cap), not on n_ctx: the
   size_t hist_mass, hist_cnt, coarse_mass, coarse_cnt, state, ctr, tilerec, tiletab, total;
-  int nblk_max;                   // zero-filled region stays in place while n_ctx grows
+  int nrec_max;                   // zero-filled region stays in place while n_ctx grows
 };
 SelLayout sel_layout(const Layer& L);
 struct SelRows {                 // device views of the selection workspace
@@ -130,8 +135,8 @@ struct SelRows {                 // device views of the selection workspace
   uint32_t* ccnt;                // [rows][3][64]
   SelRowState* state;            // [rows]
   uint32_t* ctr;                 // [rows][2]       compaction: [1] blocks done ([0] unused, kept zero)
-  uint4* tilerec;                // [rows][nblk]    per tile: counts against the level-1 prefix (hist<2>)
-  uint16_t* tiletab;             // [rows][nblk][kTabDigits] tiles whose record overflowed: candidates
+  uint4* tilerec;                // [rows][nrec]    per kRecTok tokens: counts against the level-1 prefix (hist<2>)
+  uint16_t* tiletab;             // [rows][nrec][kTabDigits] records that overflowed: candidates
                                  //                 with low digit >= d (hist<2>), zero otherwise
 };
 struct SelArgs {
@@ -149,11 +154,13 @@ struct SelArgs {
   int64_t n_cap;
   int nblk;                      // selection tiles per row (from n_ctx; set by launch_select)
   int items;                     // scores per thread per tile (kSelItems or kSelItemsLong; set by launch_select)
-  int rec_stride;                // tile records per row (from n_cap)
+  int rec_stride;                // records per row (from n_cap)
   int32_t* sel_idx;
   int32_t* sel_count;
   int32_t* starts;               // [rows][nsplit + 1] range index of the selected lists, or null
   int nsplit;                    // ranges of n_ctx (row stride of starts: nsplit + 1)
+  uint32_t* thr_out;             // decode step: [rows] threshold keys for the gather, which then
+                                 // writes the lists itself (requires starts); null: the lists here
   SelRows R;
 };
 SelRows sel_rows(void* ws, const SelLayout& lay);

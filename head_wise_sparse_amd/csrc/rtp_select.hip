@@ -20,20 +20,21 @@
 //             from the 32 fine bins under the chosen coarse bin (two small reads): the
 //             digit is where the mass accumulated from the top first reaches what is
 //             still needed.  The kernel boundary is the only synchronisation.
-//             hist<2> also leaves one record per tile: how many of its tokens lie above
-//             the 22-bit prefix (certainly selected) and, for up to kRecPairs distinct
-//             low 10-bit digits among the tokens that share it (candidates), the digit
-//             and its count; a tile with more such digits than that, its table.
+//             hist<2> also leaves one record per kRecTok tokens (one decode range): how
+//             many of them lie above the 22-bit prefix (certainly selected) and, for up
+//             to kRecPairs distinct low 10-bit digits among the tokens that share it
+//             (candidates), the digit and its count; a record with more such digits
+//             than that also gets a table.
 //   compact   resolves the last digit (t is now the full key), the tie count r in
 //             closed form (tied tokens carry equal weight), and writes the selected
 //             indices in increasing order.  A tile's output offset comes from the
 //             records of the earlier tiles (written by the previous launch: no waiting
 //             on other blocks): tokens above the prefix, plus candidates above t, plus
-//             at most r ties.  Candidates share 22 key bits with t, so a tile holds few
-//             distinct ones (exact ties collapse into one pair).  A tile with more
-//             distinct candidates than its record keeps ("heavy") also left a table of
-//             its candidate counts at or above each low digit, and the block reads the
-//             two entries at t from it: O(1) per earlier tile whatever the scores.
+//             at most r ties.  Candidates share 22 key bits with t, so a record holds few
+//             distinct ones (exact ties collapse into one pair).  A record with more
+//             distinct candidates than it keeps ("heavy") comes with a table of its
+//             candidate counts at or above each low digit, and the block reads the two
+//             entries at t from it: O(1) per earlier record whatever the scores.
 //             It also writes the range index of every list when asked for.
 // Rows of at most kSelSmallMax tokens take one launch instead (k_sel_small): one block per
 // row keeps the row's scores in registers and each level's histogram in LDS, and applies
@@ -242,6 +243,30 @@ __device__ __forceinline__ void clear_level(const SelRows& R, int row, int level
   }
 }
 
+// Clear records [0, nrec) of a row and the tables of the heavy ones among them, a round of
+// kSelThreads records at a time (the whole block; s_hl holds kSelThreads entries).
+__device__ void clear_records(const SelRows& R, int row, int rec_stride, int nrec, uint32_t* s_hl,
+                              uint32_t* s_nh) {
+  const int tid = threadIdx.x;
+  uint4* rrow = R.tilerec + int64_t(row) * rec_stride;
+  uint4* trow = reinterpret_cast<uint4*>(R.tiletab + int64_t(row) * rec_stride * kTabDigits);
+  constexpr int kTab16 = kTabDigits * int(sizeof(uint16_t)) / 16;
+  for (int c0 = 0; c0 < nrec; c0 += kSelThreads) {
+    if (tid == 0) *s_nh = 0;
+    __syncthreads();
+    const int i = c0 + tid;
+    if (i < nrec) {
+      if ((rrow[i].x >> 16) > uint32_t(kRecPairs)) s_hl[atomicAdd(s_nh, 1u)] = uint32_t(i);
+      rrow[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    const int nh = int(*s_nh);
+    for (int k = tid; k < nh * kTab16; k += kSelThreads)
+      trow[int64_t(s_hl[k / kTab16]) * kTab16 + k % kTab16] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+  }
+}
+
 // Row max (and, by the first block, the row statistics) from the scoring's per-block
 // (max, sum of exp) partials.
 __device__ float row_max_from_partials(const SelArgs& a, int row, int blk, int tid, float* s_red, int n_ctx) {
@@ -265,14 +290,21 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   constexpr int NB = LEVEL == 2 ? 1024 : 2048;
   constexpr int SHIFT = LEVEL == 0 ? 21 : (LEVEL == 1 ? 10 : 0);
   constexpr int PSHIFT = LEVEL == 1 ? 21 : 10;                     // prefix bits start (levels 1, 2)
+  constexpr int IPR = kRecTok / kSelThreads;                       // items per record
+  constexpr int NR = LEVEL == 2 ? ITEMS / IPR : 1;                 // level 2: records per tile (even)
+  constexpr int NW = kSelThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int blk = blockIdx.x, row = blockIdx.y;
   __shared__ uint64_t h_m[NB];
   __shared__ uint32_t h_c[NB];
   __shared__ uint32_t s_prefix;
-  __shared__ float s_red[kSelThreads / 64];
-  __shared__ uint32_t s_na[kSelThreads / 64], s_np, s_pair[kRecPairs];   // level 2: tile record
-  __shared__ uint32_t s_wt[kSelThreads / 64];                               // level 2: heavy-tile table
+  __shared__ float s_red[NW];
+  // level 2: per record, tokens above the prefix (per wave), distinct candidate digits and
+  // the first kRecPairs (digit, count) pairs; candidate counts per low digit, two records
+  // per word (16-bit halves: a record holds at most kRecTok tokens); cross-wave sums
+  __shared__ uint32_t s_na[NR][NW], s_np[NR], s_pair[NR][kRecPairs];
+  __shared__ uint32_t h_s[LEVEL == 2 ? NR / 2 : 1][LEVEL == 2 ? 1024 : 1];
+  __shared__ uint32_t s_wt[LEVEL == 2 ? NR / 2 : 1][NW];
   const int n_ctx = live_ctx(a.live, a.n_ctx);
   const int nblk = int((int64_t(n_ctx) + TILE - 1) / TILE);       // tiles of the live context
   if (blk >= nblk) return;
@@ -291,7 +323,10 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
     h_m[i] = 0;
     h_c[i] = 0;
   }
-  if (LEVEL == 2 && tid == 0) s_np = 0;
+  if constexpr (LEVEL == 2) {
+    for (int i = tid; i < NR / 2 * 1024; i += kSelThreads) (&h_s[0][0])[i] = 0;
+    if (tid < NR) s_np[tid] = 0;
+  }
   float m = 0.0f;                                   // unused by the static top-k rule
   if constexpr (LEVEL == 0) {
     if (!a.by_count) m = a.score_part ? row_max_from_partials(a, row, blk, tid, s_red, n_ctx) : a.row_max[row];
@@ -323,7 +358,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
   }
   __syncthreads();
   const uint32_t prefix = LEVEL > 0 ? s_prefix : 0u;
-  uint32_t n_above = 0;                             // level 2: tokens above the 22-bit prefix
+  uint32_t n_above[NR] = {};                        // level 2: tokens above the 22-bit prefix, per record
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int64_t j = base + it * kSelThreads + tid;
@@ -333,12 +368,16 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
       const uint32_t d = (key >> SHIFT) & uint32_t(NB - 1);
       if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(&h_m[d]), (unsigned long long)fixed_weight(sv[it], m, wscale));
       atomicAdd(&h_c[d], 1u);
+      if constexpr (LEVEL == 2) atomicAdd(&h_s[it / IPR / 2][d], 1u << (16 * ((it / IPR) & 1)));
     }
-    if constexpr (LEVEL == 2) n_above += uint32_t((j < n_ctx) && (key >> PSHIFT) > prefix);
+    if constexpr (LEVEL == 2) n_above[it / IPR] += uint32_t((j < n_ctx) && (key >> PSHIFT) > prefix);
   }
   if constexpr (LEVEL == 2) {
-    n_above = wave_sum(n_above);
-    if (lane == 0) s_na[tid / 64] = n_above;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const uint32_t na = wave_sum(n_above[k]);
+      if (lane == 0) s_na[k][tid / 64] = na;
+    }
   }
   __syncthreads();
 
@@ -348,39 +387,67 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelArgs a) {
     if (h_c[i]) {
       if (!a.by_count) atomicAdd(reinterpret_cast<unsigned long long*>(gm + i), (unsigned long long)h_m[i]);
       atomicAdd(gc + i, h_c[i]);
-      if constexpr (LEVEL == 2) {              // this tile's distinct candidate digits
-        const uint32_t k = atomicAdd(&s_np, 1u);
-        if (k < uint32_t(kRecPairs)) s_pair[k] = uint32_t(i) | (h_c[i] << 10);
+      if constexpr (LEVEL == 2) {              // each record's distinct candidate digits
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const uint32_t c = (h_s[k / 2][i] >> (16 * (k & 1))) & 0xFFFFu;
+          if (c) {
+            const uint32_t e = atomicAdd(&s_np[k], 1u);
+            if (e < uint32_t(kRecPairs)) s_pair[k][e] = uint32_t(i) | (c << 10);
+          }
+        }
       }
     }
   }
   if constexpr (LEVEL == 2) {
     __syncthreads();
-    if (tid == 0) {
+    const int64_t rec0 = int64_t(blk) * NR;                       // this tile's first record
+    if (tid < NR && (rec0 + tid) * kRecTok < n_ctx) {             // records of the live context
       uint32_t na = 0;
 #pragma unroll
-      for (int w = 0; w < kSelThreads / 64; ++w) na += s_na[w];
-      const uint32_t np = s_np;
+      for (int w = 0; w < NW; ++w) na += s_na[tid][w];
+      const uint32_t np = s_np[tid];
       uint32_t pw[kRecPairs];
 #pragma unroll
-      for (int k = 0; k < kRecPairs; ++k) pw[k] = uint32_t(k) < np ? s_pair[k] : 0u;
-      a.R.tilerec[int64_t(row) * a.rec_stride + blk] = make_uint4(na | (np << 16), pw[0], pw[1], pw[2]);
+      for (int k = 0; k < kRecPairs; ++k) pw[k] = uint32_t(k) < np ? s_pair[tid][k] : 0u;
+      a.R.tilerec[int64_t(row) * a.rec_stride + rec0 + tid] = make_uint4(na | (np << 16), pw[0], pw[1], pw[2]);
     }
-    if (s_np > uint32_t(kRecPairs)) {
-      // The record cannot hold this tile's candidates: leave their counts at or above every
-      // low digit d (inclusive suffix sums of the tile's level-2 counts, < 2^16 per tile),
-      // from which the compaction reads the two it needs once the threshold digit is known.
-      // Thread tid owns digits 4 tid .. 4 tid + 3; higher threads hold higher digits.
-      const uint32_t c0 = h_c[4 * tid], c1 = h_c[4 * tid + 1], c2 = h_c[4 * tid + 2], c3 = h_c[4 * tid + 3];
-      const uint32_t own = c0 + c1 + c2 + c3;
-      const uint32_t in_wave = wave_suffix_incl<uint32_t>(own, lane);   // own + higher lanes of the wave
-      if (lane == 0) s_wt[tid / 64] = in_wave;
+    bool heavy = false;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) heavy |= s_np[k] > uint32_t(kRecPairs);
+    if (heavy) {
+      // A record that cannot hold its candidates: leave their counts at or above every low
+      // digit d (inclusive suffix sums of the record's level-2 counts, <= kRecTok), from
+      // which the range index reads the two it needs once the threshold digit is known.
+      // Two records per word are summed at once (16-bit halves never carry).  Thread tid
+      // owns digits 4 tid .. 4 tid + 3; higher threads hold higher digits.
+      uint32_t c[NR / 2][4], own[NR / 2], in_wave[NR / 2];
+#pragma unroll
+      for (int w = 0; w < NR / 2; ++w) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[w][k] = h_s[w][4 * tid + k];
+        own[w] = c[w][0] + c[w][1] + c[w][2] + c[w][3];
+        in_wave[w] = wave_suffix_incl<uint32_t>(own[w], lane);   // own + higher lanes of the wave
+        if (lane == 0) s_wt[w][tid / 64] = in_wave[w];
+      }
       __syncthreads();
-      uint32_t hi = in_wave - own;                                   // digits above this thread's four
-      for (int w = tid / 64 + 1; w < kSelThreads / 64; ++w) hi += s_wt[w];
-      const uint32_t s3 = hi + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
-      uint2* tab = reinterpret_cast<uint2*>(a.R.tiletab + (int64_t(row) * a.rec_stride + blk) * kTabDigits);
-      tab[tid] = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
+#pragma unroll
+      for (int w = 0; w < NR / 2; ++w) {
+        uint32_t hi = in_wave[w] - own[w];                         // digits above this thread's four
+        for (int v = tid / 64 + 1; v < NW; ++v) hi += s_wt[w][v];
+        const uint32_t s3 = hi + c[w][3], s2 = s3 + c[w][2], s1 = s2 + c[w][1], s0 = s1 + c[w][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (s_np[2 * w + h] > uint32_t(kRecPairs)) {
+            const int sh = 16 * h;
+            const uint32_t e0 = (s0 >> sh) & 0xFFFFu, e1 = (s1 >> sh) & 0xFFFFu;
+            const uint32_t e2 = (s2 >> sh) & 0xFFFFu, e3 = (s3 >> sh) & 0xFFFFu;
+            uint2* tab = reinterpret_cast<uint2*>(a.R.tiletab +
+                                                  (int64_t(row) * a.rec_stride + rec0 + 2 * w + h) * kTabDigits);
+            tab[tid] = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+          }
+        }
+      }
     }
   }
   // coarse summary: thread c < NB/32 sums its 32 fine bins, starting at a different
@@ -431,8 +498,9 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     const int64_t j = base + it * kSelThreads + tid;
     sv[it] = sp[j < n_ctx ? j : n_ctx - 1];
   }
-  uint4 rec0 = make_uint4(0u, 0u, 0u, 0u);           // records of the first 64 earlier tiles
-  if (wave == 1 && lane < tile) rec0 = rec[lane];
+  const int nrec = tile * (TILE / kRecTok);           // records of the earlier tiles
+  uint4 rec0 = make_uint4(0u, 0u, 0u, 0u);           // the first 64 of them
+  if (wave == 1 && lane < nrec) rec0 = rec[lane];
   if (wave == 0) {
     const SelLevelState& ls = a.R.state[row].lvl[1];
     Resolved in{};
@@ -461,14 +529,14 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   clear_level(a.R, row, 1, tile, nblk);             // read last by hist<2>
   const uint32_t t = s_t, r = s_r;
   // ---- tokens of earlier tiles with key > t (pa) and key == t (pe), from their records,
-  // or, for a tile whose record overflowed ("heavy"), from two entries of its table
+  // or, for a record that overflowed ("heavy"), from two entries of its table
   const uint16_t* tab = a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits;
   if (wave == 1) {
     const uint32_t tl = t & 1023u;
     uint32_t ca = 0, ce = 0;
-    for (int c = 0; c < tile; c += 64) {
+    for (int c = 0; c < nrec; c += 64) {
       const int i = c + lane;
-      const uint4 q = (c == 0) ? rec0 : (i < tile ? rec[i] : make_uint4(0u, 0u, 0u, 0u));
+      const uint4 q = (c == 0) ? rec0 : (i < nrec ? rec[i] : make_uint4(0u, 0u, 0u, 0u));
       const uint32_t np = q.x >> 16;
       ca += q.x & 0xFFFFu;
       if (np > uint32_t(kRecPairs)) {
@@ -567,25 +635,9 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   if (tid == 0) s_last = (done_before == uint32_t(nblk - 1));
   __syncthreads();
   if (s_last) {
-    // tile records, and the tables of the heavy tiles among them (kTabDigits / 8 16-byte
-    // stores each), a round of kSelThreads tiles at a time
-    uint4* rrow = a.R.tilerec + int64_t(row) * a.rec_stride;
-    uint4* trow = reinterpret_cast<uint4*>(a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits);
-    constexpr int kTab16 = kTabDigits * int(sizeof(uint16_t)) / 16;
-    for (int c0 = 0; c0 < nblk; c0 += kSelThreads) {
-      if (tid == 0) s_nh = 0;
-      __syncthreads();
-      const int i = c0 + tid;
-      if (i < nblk) {
-        if ((rrow[i].x >> 16) > uint32_t(kRecPairs)) s_hl[atomicAdd(&s_nh, 1u)] = uint32_t(i);
-        rrow[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      __syncthreads();
-      const int nh = int(s_nh);
-      for (int k = tid; k < nh * kTab16; k += kSelThreads)
-        trow[int64_t(s_hl[k / kTab16]) * kTab16 + k % kTab16] = make_uint4(0u, 0u, 0u, 0u);
-      __syncthreads();
-    }
+    // records of the live context, and the tables of the heavy ones among them
+    // (kTabDigits / 8 16-byte stores each), a round of kSelThreads records at a time
+    clear_records(a.R, row, a.rec_stride, (n_ctx + kRecTok - 1) / kRecTok, s_hl, &s_nh);
     uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
     if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
     clear_level(a.R, row, 2, 0, 1);
@@ -594,6 +646,149 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
       ctr[1] = 0;
     }
   }
+}
+
+// Decode step, after hist<2>: one block per row resolves the last digit and the tie count,
+// writes the count, the threshold key t and the range index, and clears the row's
+// workspace.  Range q's entry is the number of selected tokens below its start: the
+// tokens above t and at most r of the ties in the records of ranges 0 .. q-1 (a scan
+// over the records).  The gather then takes range q's members from its own scores: every
+// token with key > t, and the first (starts[q+1] - starts[q] - #above) with key == t --
+// the same list the compaction writes.
+__global__ __launch_bounds__(kSelThreads) void k_sel_resolve(SelArgs a) {
+  constexpr int NW = kSelThreads / 64;
+  constexpr int RPT = 4;                                         // records per thread per round
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int row = blockIdx.x;
+  __shared__ uint32_t s_t, s_r;
+  __shared__ uint32_t s_wa[NW], s_we[NW];
+  __shared__ uint32_t s_hl[kSelThreads * RPT], s_nh;
+  const int n_ctx = live_ctx(a.live, a.n_ctx);
+  const int nrec = (n_ctx + kRecTok - 1) / kRecTok;              // records = ranges of the live context
+  const float wscale = mass_wscale(n_ctx);
+  const uint4* rec = a.R.tilerec + int64_t(row) * a.rec_stride;
+  const uint16_t* tab = a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits;
+  int32_t* st_out = a.starts + int64_t(row) * (a.nsplit + 1);
+  uint4 q[RPT];                                                  // the first round, loaded beside the resolve
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int i = tid * RPT + k;
+    q[k] = i < nrec ? rec[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (wave == 0) {
+    const SelLevelState& ls = a.R.state[row].lvl[1];
+    Resolved in{};
+    in.prefix = ls.prefix;
+    in.above = ls.above;
+    in.cnt_above = ls.cnt_above;
+    in.target = ls.target;
+    const Resolved o = resolve_level2_direct(a.R, row, in, a.by_count, lane);
+    if (lane == 0) {
+      // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
+      const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(o.prefix), a.R.state[row].ref_max, wscale);
+      const uint64_t rem = o.target - o.above;
+      uint64_t r = (w == 0) ? o.tied : (rem + w - 1) / w;
+      if (r < 1) r = 1;
+      if (r > o.tied) r = o.tied;
+      s_t = o.prefix;
+      s_r = uint32_t(r);
+      const uint32_t cnt = o.cnt_above + uint32_t(r);
+      a.sel_count[row] = int32_t(cnt);
+      st_out[nrec] = int32_t(cnt);
+      a.thr_out[row] = o.prefix;
+    }
+  }
+  __syncthreads();
+  const uint32_t t = s_t, r = s_r, tl = t & 1023u;
+  uint32_t carry_a = 0, carry_e = 0;                             // counts of the earlier rounds
+  for (int c0 = 0; c0 < nrec; c0 += kSelThreads * RPT) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int i = c0 + tid * RPT + k;
+        q[k] = i < nrec ? rec[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    // each record's tokens above t (ca) and tied with t (ce): the pairs, or two entries of
+    // its table when it overflowed
+    uint32_t ca[RPT], ce[RPT], ta = 0, te = 0;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int i = c0 + tid * RPT + k;
+      ca[k] = q[k].x & 0xFFFFu;
+      ce[k] = 0;
+      if ((q[k].x >> 16) > uint32_t(kRecPairs)) {
+        const uint16_t* ti = tab + int64_t(i) * kTabDigits;
+        const uint32_t ge = ti[tl], gt = tl < 1023u ? uint32_t(ti[tl + 1]) : 0u;   // digit >= tl, > tl
+        ca[k] += gt;
+        ce[k] = ge - gt;
+      } else {
+        const uint32_t pw[kRecPairs] = {q[k].y, q[k].z, q[k].w};
+#pragma unroll
+        for (int e = 0; e < kRecPairs; ++e) {
+          const uint32_t dig = pw[e] & 1023u, cnt = pw[e] >> 10;   // empty pairs have cnt 0
+          ca[k] += dig > tl ? cnt : 0u;
+          ce[k] += dig == tl ? cnt : 0u;
+        }
+      }
+      ta += ca[k];
+      te += ce[k];
+    }
+    // exclusive prefix over the records in index order (thread-major, RPT per thread)
+    uint32_t ia = ta, ie = te;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t ya = __shfl_up(ia, o, 64), ye = __shfl_up(ie, o, 64);
+      if (lane >= o) {
+        ia += ya;
+        ie += ye;
+      }
+    }
+    if (lane == 63) {
+      s_wa[wave] = ia;
+      s_we[wave] = ie;
+    }
+    __syncthreads();
+    uint32_t xa = carry_a + ia - ta, xe = carry_e + ie - te;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) {
+        xa += s_wa[w];
+        xe += s_we[w];
+      }
+      carry_a += s_wa[w];
+      carry_e += s_we[w];
+    }
+    if (tid == 0) s_nh = 0;
+    __syncthreads();                                             // (s_nh) and the wave sums are read
+    uint4* rw = a.R.tilerec + int64_t(row) * a.rec_stride;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int i = c0 + tid * RPT + k;
+      if (i < nrec) {
+        st_out[i] = int32_t(xa + (xe < r ? xe : r));
+        // this block is the records' last reader: clear them, and list the heavy ones' tables
+        if ((q[k].x >> 16) > uint32_t(kRecPairs)) s_hl[atomicAdd(&s_nh, 1u)] = uint32_t(i);
+        rw[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      xa += ca[k];
+      xe += ce[k];
+    }
+    __syncthreads();
+    {
+      constexpr int kTab16 = kTabDigits * int(sizeof(uint16_t)) / 16;
+      uint4* trow = reinterpret_cast<uint4*>(a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits);
+      const int nh = int(s_nh);
+      for (int k = tid; k < nh * kTab16; k += kSelThreads)
+        trow[int64_t(s_hl[k / kTab16]) * kTab16 + k % kTab16] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();                                             // s_wa / s_we / s_hl are reused
+  }
+  // this block was the only reader of the level-2 histogram and the state
+  clear_level(a.R, row, 1, 0, 1);
+  clear_level(a.R, row, 2, 0, 1);
+  uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
+  if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
 }
 
 // Rows of at most kSelSmallMax tokens: one block holds the whole row in registers, so the
@@ -679,6 +874,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_small(SelArgs a) {
   res = small_level<1, ITEMS>(a, sv, m, wscale, n_ctx, res, h_m, h_c, c_m, c_c, &s_res);
   res = small_level<2, ITEMS>(a, sv, m, wscale, n_ctx, res, h_m, h_c, c_m, c_c, &s_res);
   const uint32_t t = res.prefix;
+  constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
   if (tid == 0) {
     // tied tokens share one weight (1 for top-k): take just enough of them to reach the target
     const uint64_t w = a.by_count ? 1ull : fixed_weight(key_score(t), m, wscale);
@@ -690,6 +886,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_small(SelArgs a) {
     const uint32_t cnt = res.cnt_above + uint32_t(r);
     a.sel_count[row] = int32_t(cnt);
     if (a.starts) a.starts[int64_t(row) * (a.nsplit + 1) + nsplit] = int32_t(cnt);
+    if (a.thr_out) a.thr_out[row] = t;
   }
   uint32_t fa = 0, fe = 0;
 #pragma unroll
@@ -739,7 +936,6 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_small(SelArgs a) {
   const uint32_t r = s_r;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = a.sel_idx + int64_t(row) * a.n_cap;
-  constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const uint32_t ca = s_wa[it * NW + wave], ce = s_we[it * NW + wave];
@@ -749,7 +945,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_small(SelArgs a) {
     const uint32_t a_before = ca + __popcll(__ballot(above) & lt);
     const uint32_t e_before = ce + __popcll(__ballot(tied) & lt);
     const bool take = above || (tied && e_before < r);
-    if (take) out[a_before + (e_before < r ? e_before : r)] = it * kSelThreads + tid;
+    if (take && !a.thr_out) out[a_before + (e_before < r ? e_before : r)] = it * kSelThreads + tid;
   }
 }
 
@@ -818,7 +1014,7 @@ extern "C" rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.top_p = top_p;
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
-  a.rec_stride = lay.nblk_max;
+  a.rec_stride = lay.nrec_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.starts = sel_starts;
@@ -855,7 +1051,7 @@ extern "C" rtp_status rtp_topk_select(const rtp_layer_desc* desc, int64_t n_ctx,
   a.k_target = k;
   a.n_ctx = int(n_ctx);
   a.n_cap = L.n_cap;
-  a.rec_stride = lay.nblk_max;
+  a.rec_stride = lay.nrec_max;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.starts = sel_starts;
@@ -874,7 +1070,7 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
                        a.live, a.n_cap, a.sel_idx, a.sel_count, a.starts, a.nsplit);
     return check_launch("k_sel_all");
   }
-  if (a.n_ctx <= kSelSmallMax) {         // one block per row
+  if (a.n_ctx <= kSelSmallMax) {         // one block per row (with thr_out: no lists, the gather writes them)
     if (a.n_ctx <= kSelThreads * kSelItems)
       hipLaunchKernelGGL((k_sel_small<kSelItems>), dim3(rows), dim3(kSelThreads), 0, s, a);
     else
@@ -894,6 +1090,10 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
     if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
     hipLaunchKernelGGL((k_sel_hist<2, kSelItems>), grid, dim3(kSelThreads), 0, s, b);
     if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
+    if (b.thr_out) {
+      hipLaunchKernelGGL(k_sel_resolve, dim3(rows), dim3(kSelThreads), 0, s, b);
+      return check_launch("k_sel_resolve");
+    }
     hipLaunchKernelGGL((k_sel_compact<kSelItems>), grid, dim3(kSelThreads), 0, s, b);
   } else {
     hipLaunchKernelGGL((k_sel_hist<0, kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
@@ -902,6 +1102,10 @@ rtp_status launch_select(const SelArgs& a0, int rows, hipStream_t s) {
     if ((st = check_launch("k_sel_hist<1>")) != RTP_OK) return st;
     hipLaunchKernelGGL((k_sel_hist<2, kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
     if ((st = check_launch("k_sel_hist<2>")) != RTP_OK) return st;
+    if (b.thr_out) {
+      hipLaunchKernelGGL(k_sel_resolve, dim3(rows), dim3(kSelThreads), 0, s, b);
+      return check_launch("k_sel_resolve");
+    }
     hipLaunchKernelGGL((k_sel_compact<kSelItemsLong>), grid, dim3(kSelThreads), 0, s, b);
   }
   return check_launch("k_sel_compact");

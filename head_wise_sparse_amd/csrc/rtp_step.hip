@@ -2,14 +2,17 @@
 // top-p sets, sparse attention of the retrieval heads and sink+window attention of
 // the local heads (abstract, observations (1)-(3); research-map summary, "Approach").
 //
-// It computes exactly what the four calls compute one after the other, with the
-// same kernel bodies, in seven launches instead of thirteen:
+// It writes exactly what the four calls write one after the other, in seven launches
+// instead of thirteen (four for contexts of at most 8192 tokens, whose selection takes
+// one launch):
 //   1. scoring blocks and the local heads' split-K blocks in one grid: both stream
 //      HBM (indexer keys / sink+window K,V) and do not depend on each other;
 //   2. the first radix pass, which also reduces the scoring partials to the row
 //      statistics (no separate finalize launch);
-//   3-4. the two further radix passes;  5. compaction, which also writes the range
-//      index of every selected list;  6. the retrieval heads' split-K blocks;
+//   3-4. the two further radix passes;  5. one block per row resolves the threshold
+//      and writes the range index of every selected list from the last pass's records;
+//   6. the retrieval heads' split-K blocks, which take each range's members from its
+//      scores and write that part of the selected lists;
 //   7. one merge launch for the split partials of both head kinds (preceded, when a
 //      retrieval row has more than 128 split partials, by a launch that combines
 //      them 32 at a time).
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void k_step_score_window(ScoreArgs 
 
 template <int D, int G>
 __global__ __launch_bounds__(kDecThreads, 4) void k_step_sparse(DecArgs a) {
-  decode_block<D, G, true>(a, blockIdx.x, blockIdx.y);
+  decode_block<D, G, true, true>(a, blockIdx.x, blockIdx.y);
 }
 
 template <int D>
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(64) void k_step_finalize(const float2* __restrict__
 }
 
 struct StepLayout {
-  size_t sel, score, sparse, window, total;
+  size_t sel, score, sparse, window, thr, total;
 };
 
 // The selection region comes first and depends on the layer only, so the part of the
@@ -80,6 +83,8 @@ StepLayout step_layout(const Layer& L, int64_t n_ctx) {
   off = round_up(off + (L.n_ret ? dec_ws_bytes(L, n_ctx, true) : 0), 256);
   s.window = off;
   off = round_up(off + (L.n_loc ? dec_ws_bytes(L, n_ctx, false) : 0), 256);
+  s.thr = off;                                    // threshold key per retrieval row, for the gather
+  off = round_up(off + size_t(L.B) * L.n_ret * L.G * sizeof(uint32_t), 256);
   s.total = off;
   return s;
 }
@@ -257,11 +262,12 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     a.n_ctx = n;
     a.live = live;
     a.n_cap = L.n_cap;
-      a.rec_stride = sl.nblk_max;
+    a.rec_stride = sl.nrec_max;
     a.sel_idx = sel_idx;
     a.sel_count = sel_count;
     a.starts = starts;
     a.nsplit = nsplit;
+    a.thr_out = reinterpret_cast<uint32_t*>(w + lay.thr);   // the gather writes the lists
     a.R = sel_rows(w + lay.sel, sl);
     if (top_p >= 1.0f) {           // no radix pass runs: reduce the partials here
       hipLaunchKernelGGL(k_step_finalize, dim3(rows_s), dim3(64), 0, s, sa.part, score_gx, n, live, row_max,
@@ -275,8 +281,11 @@ rtp_status decode_step_impl(const rtp_layer_desc* desc, int64_t n_ctx, const uin
     da.q = q;
     da.k = k_cache;
     da.v = v_cache;
-    da.sel_idx = sel_idx;
     da.starts = starts;
+    da.scores = scores;
+    da.thr = a.thr_out;
+    da.all_tokens = top_p >= 1.0f;                  // every token: the lists are already written
+    da.sel_out = top_p >= 1.0f ? nullptr : sel_idx;
     da.part = reinterpret_cast<float*>(w + lay.sparse);
     da.n_ctx = n;
     da.live = live;

@@ -24,7 +24,7 @@
  *  - Ownership: the library allocates nothing.  Scratch space comes from the
  *    caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned); size it with
  *    rtp_workspace_bytes().  rtp_topp_select and rtp_decode_step keep radix
- *    histograms, counters and per-tile records in their workspace that their
+ *    histograms, counters and per-range records in their workspace that their
  *    kernels reset themselves: such a workspace must be ZERO-FILLED before its
  *    first use, every call that completes leaves that region zero again, and it
  *    must not be handed to another kind of call in between.  The region depends
@@ -170,9 +170,9 @@ rtp_status rtp_indexer_score(const rtp_layer_desc* desc, int64_t n_ctx,
  *            given, rtp_sparse_decode_attn can take it instead of rebuilding it.
  * The row_max values are the reference of every weight exp(s - row_max): pass the
  * row maxima rtp_indexer_score wrote (a smaller value saturates weights at 1).
- * The workspace holds the radix histograms, row states, counters, per-tile
- * records and per-tile digit tables of the search (rtp_workspace_bytes grows by
- * 0.5 byte per token of n_cap per row for the tables); see the zero-fill rule above.
+ * The workspace holds the radix histograms, row states, counters, per-range
+ * records and per-range digit tables of the search (rtp_workspace_bytes grows by
+ * 2 bytes per token of n_cap per row for the tables); see the zero-fill rule above.
  */
 rtp_status rtp_topp_select(const rtp_layer_desc* desc, int64_t n_ctx,
                            const float* scores, const float* row_max, const float* row_sum,

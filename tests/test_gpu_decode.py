@@ -586,6 +586,43 @@ def test_fused_step_matches_separate_calls(name, p, over):
     _assert_same(res[0], res[1], name)
 
 
+@pytest.mark.parametrize("p", [0.5, 0.97])
+def test_fused_step_tie_groups_across_ranges(p):
+    """Exact ties at the threshold that span several index ranges (one indexer key repeated):
+    the fused step, which takes each range's members from its scores and the range index,
+    writes the lists and outputs the separate calls write, whose compaction takes tied
+    tokens lowest index first."""
+    P.require_gpu()
+    torch = _torch()
+    x, d = _inputs("decode_b8_32k", batch=1, n_ctx=9000)
+    cfg = x.cfg
+    L = P.layer_for(cfg)
+    B, R, G = cfg.batch, cfg.n_kv_r * cfg.group, cfg.group
+    kidx = x.k_idx.copy()
+    for r in range(cfg.n_kv_r):
+        g = cfg.retrieval_kv[r]
+        for h, (lo, hi) in enumerate(((900, 3100), (5000, 6200))):
+            # the key of head h's largest |score|, sign-flipped if needed and doubled (both exact
+            # in bf16): its copies outscore every other token of that head
+            qi = O.indexer_query(O.bf16_to_f64(x.q_pre[0, g * G + h]), O.bf16_to_f64(x.w_q_idx[r * G + h]))
+            sc = O.indexer_scores(qi, O.bf16_to_f64(x.k_idx[0, r, :cfg.n_ctx]))
+            j = int(np.argmax(np.abs(sc)))
+            key = O.bf16_to_f64(x.k_idx[0, r, j]) * (2.0 if sc[j] > 0 else -2.0)
+            kidx[0, r, lo:hi] = O.f64_to_bf16(key)
+    k_dev = P.dev(kidx)
+    res = []
+    for fused in (False, True):
+        step = rtp.DecodeStep(L, cfg.n_ctx, p, fused=fused)
+        step.run(d.q_pre, d.q, d.k, d.v, k_dev, d.w_q_idx)
+        torch.cuda.synchronize()
+        res.append(_step_outputs(step, B, R, cfg.n_ctx))
+    _assert_same(res[0], res[1], f"p={p}")
+    if p == 0.5:         # some row takes only part of a tie group that crosses ranges
+        part = [s for s in res[0]["sets"] if 0 < np.isin(np.arange(900, 3100), s).sum() < 2200 or
+                0 < np.isin(np.arange(5000, 6200), s).sum() < 1200]
+        assert part, "no tie group is cut"
+
+
 def test_fused_step_growing_context_one_workspace():
     """One fused step object (one workspace) over a growing context: every step equals a
     fresh run of the separate calls at that length."""
