@@ -112,7 +112,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
 
   __shared__ uint16_t s_list[SPARSE ? RANGE : 1];
   __shared__ uint8_t s_lmask[SPARSE ? RANGE : 1];
-  __shared__ uint32_t s_hm[SPARSE ? G * RANGE / 4 : 1];
+  __shared__ uint32_t s_hm[(SPARSE && !FROM_SCORES) ? G * RANGE / 4 : 1];
   __shared__ int s_wcnt[NW];
   __shared__ float s_wm[NW][G], s_wl[NW][G];
   __shared__ float s_wacc[NW][G][D];
@@ -126,6 +126,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
   __shared__ uint32_t s_take[GF];
   __shared__ int s_lo[GF], s_hi[GF];
   __shared__ uint64_t s_wd[GF][RANGE / kDecThreads][NW][2];      // above / tied words of (head, item, wave)
+  __shared__ __align__(16) uint32_t s_uc[(SPARSE && FROM_SCORES) ? NE : 4];   // union count per (item, wave)
 
   uint32_t qw[G][4];
 #pragma unroll
@@ -174,9 +175,6 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
         }
       }
     }
-    for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
-    __syncthreads();
-    uint8_t* hm = reinterpret_cast<uint8_t*>(s_hm);
 #pragma unroll
     for (int t = 0; t < G; ++t) {
       // clamped: the range index may come from the caller; a range past the live context is empty
@@ -184,10 +182,33 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
       lo[t] = split < nsplit_live ? min(max(lo[t], 0), hi[t]) : 0;
     }
     if constexpr (FROM_SCORES) {
-      // position u * kDecThreads + tid of the range, for every head; a range past the live
-      // context is empty
+      // Position u * kDecThreads + tid of the range; wave w holds positions u * kDecThreads +
+      // 64 w + lane of item u, so (item, wave, lane) order is position order.  Per head and
+      // item, this wave's tokens as words (ballots): above t (A) and tied with t (T).
       const bool live_range = split < nsplit_live;
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      uint64_t wA[G][SP], wT[G][SP];
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+#pragma unroll
+        for (int u = 0; u < SP; ++u) {
+          const bool in = live_range && j0 + u * kDecThreads + tid < n_ctx;
+          bool above = in, tied = false;                        // every token (top_p >= 1)
+          if (!a.all_tokens) {
+            const uint32_t key = score_key(sc[t][u]);
+            above = in && key > thr[t];
+            tied = in && key == thr[t];
+          }
+          wA[t][u] = __ballot(above);
+          wT[t][u] = __ballot(tied);
+          if (lane == 0) {
+            s_ca[t * NE + u * NW + wave] = __popcll(wA[t][u]);
+            s_ce[t * NE + u * NW + wave] = __popcll(wT[t][u]);
+            s_wd[t][u][wave][0] = wA[t][u];
+            s_wd[t][u][wave][1] = wT[t][u];
+          }
+        }
+      }
       if (tid == 0) {
 #pragma unroll
         for (int t = 0; t < G; ++t) {
@@ -195,80 +216,90 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
           s_hi[t] = hi[t];
         }
       }
-      if (a.all_tokens) {
+      __syncthreads();
+      if (tid < G) {                     // thread h: exclusive prefixes of head h's NE entries
+        uint4* pa = reinterpret_cast<uint4*>(s_ca + tid * NE);
+        uint4* pe = reinterpret_cast<uint4*>(s_ce + tid * NE);
+        uint4 va[NE / 4], ve[NE / 4];
 #pragma unroll
-        for (int u = 0; u < SP; ++u) {
-          const bool in = live_range && j0 + u * kDecThreads + tid < n_ctx;
-#pragma unroll
-          for (int t = 0; t < G; ++t)
-            if (in) hm[t * RANGE + u * kDecThreads + tid] = 1;
+        for (int k = 0; k < NE / 4; ++k) {
+          va[k] = pa[k];
+          ve[k] = pe[k];
         }
-      } else {
-        // This wave's 64 tokens of item u as words (ballots): above t (A) and tied with t (T);
-        // tokens above t are members at once, tied ones once the range's take is known
-        uint64_t wT[G][SP];
+        uint32_t xa = 0, xe = 0;
+#pragma unroll
+        for (int k = 0; k < NE / 4; ++k) {
+          const uint32_t a0 = va[k].x, a1 = va[k].y, a2 = va[k].z, a3 = va[k].w;
+          const uint32_t e0 = ve[k].x, e1 = ve[k].y, e2 = ve[k].z, e3 = ve[k].w;
+          pa[k] = make_uint4(xa, xa + a0, xa + a0 + a1, xa + a0 + a1 + a2);
+          pe[k] = make_uint4(xe, xe + e0, xe + e0 + e1, xe + e0 + e1 + e2);
+          xa += a0 + a1 + a2 + a3;
+          xe += e0 + e1 + e2 + e3;
+        }
+        // ties this range takes: its list length minus its tokens above t (every tie, for
+        // the all-tokens lists, which hold no ties)
+        int lo_h = lo[0], hi_h = hi[0];
+#pragma unroll
+        for (int t = 1; t < G; ++t)
+          if (tid == t) {
+            lo_h = lo[t];
+            hi_h = hi[t];
+          }
+        const int take_i = hi_h - lo_h - int(xa);
+        s_take[tid] = take_i < 0 ? 0u : (uint32_t(take_i) > xe ? xe : uint32_t(take_i));
+      }
+      __syncthreads();
+      // members: A, and the first take ties of the range; the union over the heads, with each
+      // position's head mask, and its count per (item, wave)
+      uint64_t wU[SP];
+      uint32_t mk[SP];
+#pragma unroll
+      for (int u = 0; u < SP; ++u) {
+        wU[u] = 0;
+        mk[u] = 0;
 #pragma unroll
         for (int t = 0; t < G; ++t) {
-#pragma unroll
-          for (int u = 0; u < SP; ++u) {
-            const bool in = live_range && j0 + u * kDecThreads + tid < n_ctx;
-            const uint32_t key = score_key(sc[t][u]);
-            const bool above = in && key > thr[t], tied = in && key == thr[t];
-            const uint64_t wA = __ballot(above);
-            wT[t][u] = __ballot(tied);
-            if (above) hm[t * RANGE + u * kDecThreads + tid] = 1;
-            if (lane == 0) {
-              s_ca[t * NE + u * NW + wave] = __popcll(wA);
-              s_ce[t * NE + u * NW + wave] = __popcll(wT[t][u]);
-              s_wd[t][u][wave][0] = wA;
-              s_wd[t][u][wave][1] = wT[t][u];
-            }
+          uint64_t wm = wA[t][u];
+          if (wT[t][u]) {
+            const uint32_t e_before = s_ce[t * NE + u * NW + wave] + __popcll(wT[t][u] & lt);
+            wm |= __ballot(((wT[t][u] >> lane) & 1ull) && e_before < s_take[t]);
           }
+          wU[u] |= wm;
+          mk[u] |= uint32_t((wm >> lane) & 1ull) << t;
         }
-        __syncthreads();
-        if (tid < G) {                   // thread h: exclusive prefixes of head h's NE entries
-          uint4* pa = reinterpret_cast<uint4*>(s_ca + tid * NE);
-          uint4* pe = reinterpret_cast<uint4*>(s_ce + tid * NE);
-          uint4 va[NE / 4], ve[NE / 4];
+        if (lane == 0) s_uc[u * NW + wave] = __popcll(wU[u]);
+      }
+      __syncthreads();
+      // list offsets: counts of the (item, wave) pairs before, in position order
+      uint32_t uc[SP * NW];
 #pragma unroll
-          for (int k = 0; k < NE / 4; ++k) {
-            va[k] = pa[k];
-            ve[k] = pe[k];
-          }
-          uint32_t xa = 0, xe = 0;
+      for (int k = 0; k < SP * NW / 4; ++k) {
+        const uint4 v = reinterpret_cast<const uint4*>(s_uc)[k];
+        uc[4 * k] = v.x;
+        uc[4 * k + 1] = v.y;
+        uc[4 * k + 2] = v.z;
+        uc[4 * k + 3] = v.w;
+      }
+      uint32_t total = 0;
 #pragma unroll
-          for (int k = 0; k < NE / 4; ++k) {
-            const uint32_t a0 = va[k].x, a1 = va[k].y, a2 = va[k].z, a3 = va[k].w;
-            const uint32_t e0 = ve[k].x, e1 = ve[k].y, e2 = ve[k].z, e3 = ve[k].w;
-            pa[k] = make_uint4(xa, xa + a0, xa + a0 + a1, xa + a0 + a1 + a2);
-            pe[k] = make_uint4(xe, xe + e0, xe + e0 + e1, xe + e0 + e1 + e2);
-            xa += a0 + a1 + a2 + a3;
-            xe += e0 + e1 + e2 + e3;
-          }
-          // ties this range takes: its list length minus its tokens above t
-          int lo_h = lo[0], hi_h = hi[0];
+      for (int u = 0; u < SP; ++u) {
+        uint32_t off = total;
 #pragma unroll
-          for (int t = 1; t < G; ++t)
-            if (tid == t) {
-              lo_h = lo[t];
-              hi_h = hi[t];
-            }
-          const int take_i = hi_h - lo_h - int(xa);
-          s_take[tid] = take_i < 0 ? 0u : (uint32_t(take_i) > xe ? xe : uint32_t(take_i));
+        for (int w = 0; w < NW; ++w) {
+          if (w < wave) off += uc[u * NW + w];
+          total += uc[u * NW + w];
         }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < G; ++t) {
-#pragma unroll
-          for (int u = 0; u < SP; ++u) {
-            if (wT[t][u]) {              // ties among these tokens: the range takes its first take
-              const uint32_t e_before = s_ce[t * NE + u * NW + wave] + __popcll(wT[t][u] & lt);
-              if (((wT[t][u] >> lane) & 1ull) && e_before < s_take[t]) hm[t * RANGE + u * kDecThreads + tid] = 1;
-            }
-          }
+        if (mk[u]) {
+          const uint32_t at = off + __popcll(wU[u] & lt);
+          s_list[at] = uint16_t(u * kDecThreads + tid);
+          s_lmask[at] = uint8_t(mk[u]);
         }
       }
+      U = int(total);
     } else {
+      for (int i = tid; i < G * RANGE / 4; i += kDecThreads) s_hm[i] = 0;
+      __syncthreads();
+      uint8_t* hm = reinterpret_cast<uint8_t*>(s_hm);
       int pos[G][SP];
 #pragma unroll
       for (int t = 0; t < G; ++t) {
@@ -289,45 +320,45 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
 #pragma unroll
         for (int u = 0; u < SP; ++u)
           if (pos[t][u] >= 0 && pos[t][u] < RANGE) hm[t * RANGE + pos[t][u]] = 1;
-    }
-    __syncthreads();
-    // ordered union of the G membership arrays: thread tid owns positions tid*8 .. tid*8+7
-    constexpr int PER = RANGE / kDecThreads;
-    uint8_t mk[PER];
-    int c = 0;
+      __syncthreads();
+      // ordered union of the G membership arrays: thread tid owns positions tid*PER .. tid*PER+PER-1
+      constexpr int PER = RANGE / kDecThreads;
+      uint8_t mk[PER];
+      int c = 0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int p = tid * PER + e;
-      uint32_t m = 0;
+      for (int e = 0; e < PER; ++e) {
+        const int p = tid * PER + e;
+        uint32_t m = 0;
 #pragma unroll
-      for (int t = 0; t < G; ++t) m |= uint32_t(hm[t * RANGE + p]) << t;
-      mk[e] = uint8_t(m);
-      c += (m != 0);
-    }
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) s_wcnt[wave] = incl;
-    __syncthreads();
-    int off = incl - c;
-    int total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) off += s_wcnt[w];
-      total += s_wcnt[w];
-    }
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      if (mk[e]) {
-        s_list[off] = uint16_t(tid * PER + e);
-        s_lmask[off] = mk[e];
-        ++off;
+        for (int t = 0; t < G; ++t) m |= uint32_t(hm[t * RANGE + p]) << t;
+        mk[e] = uint8_t(m);
+        c += (m != 0);
       }
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) s_wcnt[wave] = incl;
+      __syncthreads();
+      int off = incl - c;
+      int total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w < wave) off += s_wcnt[w];
+        total += s_wcnt[w];
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        if (mk[e]) {
+          s_list[off] = uint16_t(tid * PER + e);
+          s_lmask[off] = mk[e];
+          ++off;
+        }
+      }
+      U = total;
     }
-    U = total;
     __syncthreads();
     if (a.nsub > 1) {          // this block's slice of the union list: positions [e0, e0 + U)
       constexpr int STEP0 = kDecUnroll * NLG;
