@@ -125,7 +125,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
   __shared__ __align__(16) uint32_t s_ce[GF * NE];
   __shared__ uint32_t s_take[GF];
   __shared__ int s_lo[GF], s_hi[GF];
-  __shared__ uint64_t s_wd[GF][RANGE / kDecThreads][NW][2];      // above / tied words of (head, item, wave)
+  __shared__ uint16_t s_sel[GF][(SPARSE && FROM_SCORES) ? RANGE : 1];   // the range's list part per head
   __shared__ __align__(16) uint32_t s_uc[(SPARSE && FROM_SCORES) ? NE : 4];   // union count per (item, wave)
 
   uint32_t qw[G][4];
@@ -204,8 +204,6 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
           if (lane == 0) {
             s_ca[t * NE + u * NW + wave] = __popcll(wA[t][u]);
             s_ce[t * NE + u * NW + wave] = __popcll(wT[t][u]);
-            s_wd[t][u][wave][0] = wA[t][u];
-            s_wd[t][u][wave][1] = wT[t][u];
           }
         }
       }
@@ -249,8 +247,19 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
         s_take[tid] = take_i < 0 ? 0u : (uint32_t(take_i) > xe ? xe : uint32_t(take_i));
       }
       __syncthreads();
-      // members: A, and the first take ties of the range; the union over the heads, with each
-      // position's head mask, and its count per (item, wave)
+      // members: A, and the first take ties of the range; each member's place in its head's
+      // list part (kept in LDS, written out after the attention); the union over the heads,
+      // with each position's head mask, and its count per (item, wave)
+      uint32_t pa[G][SP], pe[G][SP], take[G];
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        take[t] = s_take[t];
+#pragma unroll
+        for (int u = 0; u < SP; ++u) {
+          pa[t][u] = s_ca[t * NE + u * NW + wave];
+          pe[t][u] = s_ce[t * NE + u * NW + wave];
+        }
+      }
       uint64_t wU[SP];
       uint32_t mk[SP];
 #pragma unroll
@@ -259,13 +268,13 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
         mk[u] = 0;
 #pragma unroll
         for (int t = 0; t < G; ++t) {
-          uint64_t wm = wA[t][u];
-          if (wT[t][u]) {
-            const uint32_t e_before = s_ce[t * NE + u * NW + wave] + __popcll(wT[t][u] & lt);
-            wm |= __ballot(((wT[t][u] >> lane) & 1ull) && e_before < s_take[t]);
-          }
+          const uint32_t a_before = pa[t][u] + __popcll(wA[t][u] & lt);
+          const uint32_t e_before = pe[t][u] + __popcll(wT[t][u] & lt);
+          const bool mem = ((wA[t][u] >> lane) & 1ull) || (((wT[t][u] >> lane) & 1ull) && e_before < take[t]);
+          if (mem) s_sel[t][a_before + (e_before < take[t] ? e_before : take[t])] = uint16_t(u * kDecThreads + tid);
+          const uint64_t wm = wT[t][u] ? __ballot(mem) : wA[t][u];
           wU[u] |= wm;
-          mk[u] |= uint32_t((wm >> lane) & 1ull) << t;
+          mk[u] |= uint32_t(mem) << t;
         }
         if (lane == 0) s_uc[u * NW + wave] = __popcll(wU[u]);
       }
@@ -512,27 +521,14 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, int slot, int grp
     }
   }
   if constexpr (SPARSE && FROM_SCORES) {
-    // this range's part of the selected lists, written last: a barrier waits for every
-    // store in flight, and none follows here
+    // this range's part of the selected lists, written last (a barrier waits for every
+    // store in flight, and none follows here), from its copy in LDS
     if (a.sel_out && sub == 0 && !a.all_tokens) {
-      constexpr int SP = RANGE / kDecThreads;
-      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
       for (int t = 0; t < G; ++t) {
-        const uint32_t take = s_take[t];
-        const int lo_t = s_lo[t], hi_t = s_hi[t];
-        int32_t* out = a.sel_out + int64_t(grp * G + t) * a.n_cap;
-#pragma unroll
-        for (int u = 0; u < SP; ++u) {
-          const uint64_t wA = s_wd[t][u][wave][0], wT = s_wd[t][u][wave][1];
-          const bool above = (wA >> lane) & 1ull, tied = (wT >> lane) & 1ull;
-          const uint32_t a_before = s_ca[t * NE + u * NW + wave] + __popcll(wA & lt);
-          const uint32_t e_before = s_ce[t * NE + u * NW + wave] + __popcll(wT & lt);
-          if (above || (tied && e_before < take)) {
-            const int at = lo_t + int(a_before + (e_before < take ? e_before : take));
-            if (at < hi_t) out[at] = j0 + u * kDecThreads + tid;
-          }
-        }
+        const int lo_t = s_lo[t], n_t = s_hi[t] - s_lo[t];      // its members: the list part [lo, hi)
+        int32_t* out = a.sel_out + int64_t(grp * G + t) * a.n_cap + lo_t;
+        for (int i = tid; i < n_t; i += kDecThreads) out[i] = j0 + s_sel[t][i];
       }
     }
   }
