@@ -38,9 +38,9 @@ BF16_PEAK_TFLOPS = 2500.0
 COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
 MEASURED_KIB = {
     "prefill_attn": {"src": ("rtp_prefill.hip", "9c8e4c2435f8d8e8"),
-                     "fetch": 210059.1, "write": 41721.7},
-    "sparse_decode": {"src": ("decode_dev.hpp", "6a3a214974469809"),
-                      "fetch": 172611.6 + 1086.5, "write": 2176.2 + 8.0},
+                     "fetch": 212424.8, "write": 41408.9},
+    "sparse_decode": {"src": ("decode_dev.hpp", "e31967e96b51ec13"),
+                      "fetch": 172546.0 + 1086.5, "write": 2176.3 + 8.0},
 }
 
 

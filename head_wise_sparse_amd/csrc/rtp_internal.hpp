@@ -137,7 +137,8 @@ struct SelRows {                 // device views of the selection workspace
   uint32_t* ctr;                 // [rows][2]       compaction: [1] blocks done ([0] unused, kept zero)
   uint4* tilerec;                // [rows][nrec]    per kRecTok tokens: counts against the level-1 prefix (hist<2>)
   uint16_t* tiletab;             // [rows][nrec][kTabDigits] records that overflowed: candidates
-                                 //                 with low digit >= d (hist<2>), zero otherwise
+                                 //                 with low digit >= d (hist<2>; written whole before
+                                 //                 it is read, never cleared: the end of the region)
 };
 struct SelArgs {
   const float* scores;           // [rows][n_cap]

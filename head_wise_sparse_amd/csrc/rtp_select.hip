@@ -39,11 +39,12 @@
 // Rows of at most kSelSmallMax tokens take one launch instead (k_sel_small): one block per
 // row keeps the row's scores in registers and each level's histogram in LDS, and applies
 // the same rules, so it writes the same lists, counts and range index.
-// The workspace is all zero when a call starts and when it ends: each launch clears
-// what earlier launches left and nobody reads any more (hist<2> the level-0
-// histogram, compact the level-1 histogram), and the last compaction block of a row
-// to finish clears the rest of that row (level-2 histogram, tile records and the
-// heavy tiles' tables, row state and counters).
+// The workspace is all zero when a call starts and when it ends, but for the heavy
+// records' tables, which the last pass writes whole before anyone reads them: each launch
+// clears what earlier launches left and nobody reads any more (hist<2> the level-0
+// histogram, compact the level-1 histogram), and the last compaction block of a row to
+// finish clears the rest of that row (level-2 histogram, records, row state and
+// counters).
 #include <cmath>
 
 #include "rtp_internal.hpp"
@@ -243,28 +244,11 @@ __device__ __forceinline__ void clear_level(const SelRows& R, int row, int level
   }
 }
 
-// Clear records [0, nrec) of a row and the tables of the heavy ones among them, a round of
-// kSelThreads records at a time (the whole block; s_hl holds kSelThreads entries).
-__device__ void clear_records(const SelRows& R, int row, int rec_stride, int nrec, uint32_t* s_hl,
-                              uint32_t* s_nh) {
-  const int tid = threadIdx.x;
+// Clear records [0, nrec) of a row (the whole block).  The heavy records' tables are left:
+// the last pass writes a record's table whole before anyone reads it.
+__device__ __forceinline__ void clear_records(const SelRows& R, int row, int rec_stride, int nrec) {
   uint4* rrow = R.tilerec + int64_t(row) * rec_stride;
-  uint4* trow = reinterpret_cast<uint4*>(R.tiletab + int64_t(row) * rec_stride * kTabDigits);
-  constexpr int kTab16 = kTabDigits * int(sizeof(uint16_t)) / 16;
-  for (int c0 = 0; c0 < nrec; c0 += kSelThreads) {
-    if (tid == 0) *s_nh = 0;
-    __syncthreads();
-    const int i = c0 + tid;
-    if (i < nrec) {
-      if ((rrow[i].x >> 16) > uint32_t(kRecPairs)) s_hl[atomicAdd(s_nh, 1u)] = uint32_t(i);
-      rrow[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
-    const int nh = int(*s_nh);
-    for (int k = tid; k < nh * kTab16; k += kSelThreads)
-      trow[int64_t(s_hl[k / kTab16]) * kTab16 + k % kTab16] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-  }
+  for (int i = threadIdx.x; i < nrec; i += kSelThreads) rrow[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Row max (and, by the first block, the row statistics) from the scoring's per-block
@@ -481,8 +465,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   static_assert(ITEMS * NW % 64 == 0 && ITEMS <= 32, "one wave scans the per-(item, wave) counts");
   __shared__ uint32_t s_t, s_r;
   __shared__ uint32_t s_wa[ITEMS * NW], s_we[ITEMS * NW];   // counts, then exclusive prefixes
-  __shared__ uint32_t s_pa, s_pe, s_last, s_nh;
-  __shared__ uint32_t s_hl[kSelThreads];
+  __shared__ uint32_t s_pa[NW], s_pe[NW], s_last;
   const int n_ctx = live_ctx(a.live, a.n_ctx);
   const int nblk = int((int64_t(n_ctx) + TILE - 1) / TILE);       // tiles of the live context
   if (tile >= nblk) return;
@@ -499,8 +482,13 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     sv[it] = sp[j < n_ctx ? j : n_ctx - 1];
   }
   const int nrec = tile * (TILE / kRecTok);           // records of the earlier tiles
-  uint4 rec0 = make_uint4(0u, 0u, 0u, 0u);           // the first 64 of them
-  if (wave == 1 && lane < nrec) rec0 = rec[lane];
+  constexpr int RPT = 4;                              // records per thread per round
+  uint4 rq[RPT];                                      // the first round, issued before the resolve
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int i = tid * RPT + k;
+    rq[k] = i < nrec ? rec[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
   if (wave == 0) {
     const SelLevelState& ls = a.R.state[row].lvl[1];
     Resolved in{};
@@ -529,36 +517,45 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   clear_level(a.R, row, 1, tile, nblk);             // read last by hist<2>
   const uint32_t t = s_t, r = s_r;
   // ---- tokens of earlier tiles with key > t (pa) and key == t (pe), from their records,
-  // or, for a record that overflowed ("heavy"), from two entries of its table
+  // or, for a record that overflowed ("heavy"), from two entries of its table; the whole
+  // block takes RPT records per thread per round
   const uint16_t* tab = a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits;
-  if (wave == 1) {
+  {
     const uint32_t tl = t & 1023u;
     uint32_t ca = 0, ce = 0;
-    for (int c = 0; c < nrec; c += 64) {
-      const int i = c + lane;
-      const uint4 q = (c == 0) ? rec0 : (i < nrec ? rec[i] : make_uint4(0u, 0u, 0u, 0u));
-      const uint32_t np = q.x >> 16;
-      ca += q.x & 0xFFFFu;
-      if (np > uint32_t(kRecPairs)) {
-        const uint16_t* ti = tab + int64_t(i) * kTabDigits;
-        const uint32_t ge = ti[tl], gt = tl < 1023u ? uint32_t(ti[tl + 1]) : 0u;   // digit >= tl, > tl
-        ca += gt;
-        ce += ge - gt;
-      } else {
-        const uint32_t pw[kRecPairs] = {q.y, q.z, q.w};
+    for (int c0 = 0; c0 < nrec; c0 += kSelThreads * RPT) {
+      if (c0 > 0) {
 #pragma unroll
-        for (int k = 0; k < kRecPairs; ++k) {
-          const uint32_t dig = pw[k] & 1023u, cnt = pw[k] >> 10;   // empty pairs have cnt 0
-          ca += dig > tl ? cnt : 0u;
-          ce += dig == tl ? cnt : 0u;
+        for (int k = 0; k < RPT; ++k) {
+          const int i = c0 + tid * RPT + k;
+          rq[k] = i < nrec ? rec[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const uint4 q = rq[k];
+        ca += q.x & 0xFFFFu;
+        if ((q.x >> 16) > uint32_t(kRecPairs)) {
+          const uint16_t* ti = tab + int64_t(c0 + tid * RPT + k) * kTabDigits;
+          const uint32_t ge = ti[tl], gt = tl < 1023u ? uint32_t(ti[tl + 1]) : 0u;   // digit >= tl, > tl
+          ca += gt;
+          ce += ge - gt;
+        } else {
+          const uint32_t pw[kRecPairs] = {q.y, q.z, q.w};
+#pragma unroll
+          for (int e = 0; e < kRecPairs; ++e) {
+            const uint32_t dig = pw[e] & 1023u, cnt = pw[e] >> 10;   // empty pairs have cnt 0
+            ca += dig > tl ? cnt : 0u;
+            ce += dig == tl ? cnt : 0u;
+          }
         }
       }
     }
     ca = wave_sum(ca);
     ce = wave_sum(ce);
     if (lane == 0) {
-      s_pa = ca;
-      s_pe = ce;
+      s_pa[wave] = ca;
+      s_pe[wave] = ce;
     }
   }
   // this thread's tokens above t / tied with t, one bit per item (ballots are taken again
@@ -612,7 +609,12 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     }
   }
   __syncthreads();
-  const uint32_t pa = s_pa, pe = s_pe;                 // counts of every earlier token
+  uint32_t pa = 0, pe = 0;                            // counts of every earlier token
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    pa += s_pa[w];
+    pe += s_pe[w];
+  }
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = a.sel_idx + int64_t(row) * a.n_cap;
   constexpr int IT_PER_RANGE = kDecRange / kSelThreads;      // items per decode range
@@ -635,9 +637,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
   if (tid == 0) s_last = (done_before == uint32_t(nblk - 1));
   __syncthreads();
   if (s_last) {
-    // records of the live context, and the tables of the heavy ones among them
-    // (kTabDigits / 8 16-byte stores each), a round of kSelThreads records at a time
-    clear_records(a.R, row, a.rec_stride, (n_ctx + kRecTok - 1) / kRecTok, s_hl, &s_nh);
+    clear_records(a.R, row, a.rec_stride, (n_ctx + kRecTok - 1) / kRecTok);   // those of the live context
     uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);
     if (tid < int(sizeof(SelRowState) / 4)) st[tid] = 0;
     clear_level(a.R, row, 2, 0, 1);
@@ -662,7 +662,6 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_resolve(SelArgs a) {
   const int row = blockIdx.x;
   __shared__ uint32_t s_t, s_r;
   __shared__ uint32_t s_wa[NW], s_we[NW];
-  __shared__ uint32_t s_hl[kSelThreads * RPT], s_nh;
   const int n_ctx = live_ctx(a.live, a.n_ctx);
   const int nrec = (n_ctx + kRecTok - 1) / kRecTok;              // records = ranges of the live context
   const float wscale = mass_wscale(n_ctx);
@@ -759,32 +758,21 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_resolve(SelArgs a) {
       carry_a += s_wa[w];
       carry_e += s_we[w];
     }
-    if (tid == 0) s_nh = 0;
-    __syncthreads();                                             // (s_nh) and the wave sums are read
     uint4* rw = a.R.tilerec + int64_t(row) * a.rec_stride;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int i = c0 + tid * RPT + k;
       if (i < nrec) {
         st_out[i] = int32_t(xa + (xe < r ? xe : r));
-        // this block is the records' last reader: clear them, and list the heavy ones' tables
-        if ((q[k].x >> 16) > uint32_t(kRecPairs)) s_hl[atomicAdd(&s_nh, 1u)] = uint32_t(i);
-        rw[i] = make_uint4(0u, 0u, 0u, 0u);
+        rw[i] = make_uint4(0u, 0u, 0u, 0u);                      // this block is the records' last reader
       }
       xa += ca[k];
       xe += ce[k];
     }
-    __syncthreads();
-    {
-      constexpr int kTab16 = kTabDigits * int(sizeof(uint16_t)) / 16;
-      uint4* trow = reinterpret_cast<uint4*>(a.R.tiletab + int64_t(row) * a.rec_stride * kTabDigits);
-      const int nh = int(s_nh);
-      for (int k = tid; k < nh * kTab16; k += kSelThreads)
-        trow[int64_t(s_hl[k / kTab16]) * kTab16 + k % kTab16] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();                                             // s_wa / s_we / s_hl are reused
+    __syncthreads();                                             // s_wa / s_we are reused
   }
-  // this block was the only reader of the level-2 histogram and the state
+  // this block was the only reader of the level-2 histogram and the state (the heavy records'
+  // tables are left: each is written whole before it is read)
   clear_level(a.R, row, 1, 0, 1);
   clear_level(a.R, row, 2, 0, 1);
   uint32_t* st = reinterpret_cast<uint32_t*>(a.R.state + row);

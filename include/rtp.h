@@ -27,7 +27,11 @@
  *    histograms, counters and per-range records in their workspace that their
  *    kernels reset themselves: such a workspace must be ZERO-FILLED before its
  *    first use, every call that completes leaves that region zero again, and it
- *    must not be handed to another kind of call in between.  The region depends
+ *    must not be handed to another kind of call in between.  (The exception is
+ *    the selection region's last part, the digit tables of ranges with many
+ *    distinct candidates, B * Hq_r * ceil(n_cap / RTP_SEL_RANGE) * 2 KiB rounded
+ *    up to 256 bytes: a call writes a table whole before it reads it, and leaves
+ *    the tables as they are.)  The region depends
  *    on the descriptor only (not on n_ctx), so one workspace serves a growing
  *    context.  The other calls need no particular content.  A workspace may be
  *    reused by later calls on the same stream; calls that run concurrently need

@@ -117,6 +117,15 @@ def check_prefix(gpu_sel: np.ndarray, scores32: np.ndarray, what: str = ""):
         f"(ties are taken lowest index first)"
 
 
+def sel_zero_bytes(L, n_ctx) -> int:
+    """Bytes at the start of the selection region that every call leaves zero: all of it but
+    the trailing digit tables (B * Hq_r * ceil(n_cap / RTP_SEL_RANGE) * 2 KiB), which calls
+    write whole before they read them and leave as they are."""
+    from head_wise_sparse_amd import rtp
+    tables = L.batch * L.n_kv_r * L.group * (-(-L.n_cap // rtp.SEL_RANGE)) * 2048
+    return rtp.rtp_workspace_bytes(L, n_ctx, rtp.CALL_TOPP_SELECT) - tables
+
+
 class DeviceDecode:
     """Generator inputs of one decode configuration, resident on the GPU."""
 

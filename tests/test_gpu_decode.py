@@ -124,7 +124,7 @@ def _run_select(L, n_ctx, scores32: np.ndarray, p: float, n_cap=None):
     ws = rtp.workspace(L, n_ctx, rtp.CALL_TOPP_SELECT)
     rtp.rtp_topp_select(L, n_ctx, st, m, z, p, sel, cnt, starts, ws)
     torch.cuda.synchronize()
-    assert not ws.any().item(), "the selection workspace must be left zero-filled"
+    assert not ws[:P.sel_zero_bytes(L, n_ctx)].any().item(), "the selection workspace must be left zero-filled"
     seln, cntn = sel.view(rows, cap).cpu().numpy(), cnt.cpu().numpy()
     stn = starts.view(rows, nsplit + 1).cpu().numpy()
     out = []
@@ -215,9 +215,9 @@ def _edge_rows():
             ulps = rng.integers(0, 4, per)
             c[:, pos] = (np.float32(1.0).view(np.uint32) + ulps.astype(np.uint32)).view(np.float32)
         yield name, c, 0.5
-    # a narrow spread over more than 256 tiles: every tile holds many distinct candidates
-    # (a heavy tile, counted from its table), and the last compaction block clears the
-    # tables in two rounds of 256 tiles
+    # a narrow spread over more than 256 tiles: every range holds many distinct candidates
+    # (a heavy record, counted from its table), and the last compaction block clears the
+    # records in several rounds of 256
     yield "narrow_many_heavy_tiles", (5 + rng.standard_normal((1, 4096 * 268 + 100)) * 1e-3).astype(np.float32), 0.9
     # enough rows x tiles that the passes use 8192-token tiles: plain, tied and narrow rows,
     # ragged tail
@@ -581,7 +581,7 @@ def test_fused_step_matches_separate_calls(name, p, over):
         torch.cuda.synchronize()
         res.append(_step_outputs(step, B, R, cfg.n_ctx))
         if fused:
-            assert not step.ws[rtp.CALL_DECODE_STEP][:rtp.rtp_workspace_bytes(L, cfg.n_ctx, rtp.CALL_TOPP_SELECT)] \
+            assert not step.ws[rtp.CALL_DECODE_STEP][:P.sel_zero_bytes(L, cfg.n_ctx)] \
                 .any().item(), "the selection region must be left zero-filled"
     _assert_same(res[0], res[1], name)
 
@@ -683,7 +683,7 @@ def _run_topk(L, n_ctx, scores32, k):
     ws = rtp.workspace(L, n_ctx, rtp.CALL_TOPP_SELECT)
     rtp.rtp_topk_select(L, n_ctx, torch.from_numpy(s).cuda(), k, sel, cnt, starts, ws)
     torch.cuda.synchronize()
-    assert not ws.any().item(), "the selection workspace must be left zero-filled"
+    assert not ws[:P.sel_zero_bytes(L, n_ctx)].any().item(), "the selection workspace must be left zero-filled"
     seln, cntn = sel.view(rows, cap).cpu().numpy(), cnt.cpu().numpy()
     stn = starts.view(rows, nsplit + 1).cpu().numpy()
     for r in range(rows):
