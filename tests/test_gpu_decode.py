@@ -623,6 +623,35 @@ def test_fused_step_tie_groups_across_ranges(p):
         assert part, "no tie group is cut"
 
 
+def test_fused_step_beyond_1m_tokens():
+    """More than 1024 ranges per row (2^21 + 1234 tokens): the resolve block scans the row's
+    records in more than one round, and the radix passes use 8192-token tiles of eight
+    records.  Fused step against the separate calls, bit for bit, on a layer of one KV head
+    (two query heads, head_dim 64) with inputs drawn on the device."""
+    P.require_gpu()
+    torch = _torch()
+    n, G, D = (1 << 21) + 1234, 2, 64
+    L = rtp.Layer(1, G, 1, D, n, [1], 4, 64)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    bf = lambda *shape, s=1.0: (torch.randn(*shape, generator=gen, device="cuda") * s).to(torch.bfloat16)
+    q_pre, q = bf(1, G, D), bf(1, G, D)
+    w_q_idx = bf(G, D, 16, s=0.125)
+    k_idx = bf(1, 1, n, 16)
+    k, v = bf(1, 1, n, D), bf(1, 1, n, D)
+    res = []
+    for fused in (False, True):
+        step = rtp.DecodeStep(L, n, 0.9, fused=fused)
+        step.run(q_pre, q, k, v, k_idx, w_q_idx)
+        torch.cuda.synchronize()
+        res.append(_step_outputs(step, 1, G, n))
+        if fused:
+            assert not step.ws[rtp.CALL_DECODE_STEP][:P.sel_zero_bytes(L, n)].any().item()
+        del step
+    assert all(1 < c.size < n for c in res[0]["sets"])
+    _assert_same(res[0], res[1], "2M tokens")
+
+
 def test_fused_step_growing_context_one_workspace():
     """One fused step object (one workspace) over a growing context: every step equals a
     fresh run of the separate calls at that length."""
