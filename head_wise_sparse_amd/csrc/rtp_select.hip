@@ -36,6 +36,9 @@
 //             candidate counts at or above each low digit, and the block reads the two
 //             entries at t from it: O(1) per earlier record whatever the scores.
 //             It also writes the range index of every list when asked for.
+// The decode step replaces the compaction with k_sel_resolve: one block per row resolves
+// t and r and forms the range index from the records alone (the step's gather then takes
+// each range's members from its scores and writes the lists).
 // Rows of at most kSelSmallMax tokens take one launch instead (k_sel_small): one block per
 // row keeps the row's scores in registers and each level's histogram in LDS, and applies
 // the same rules, so it writes the same lists, counts and range index.
@@ -43,8 +46,8 @@
 // records' tables, which the last pass writes whole before anyone reads them: each launch
 // clears what earlier launches left and nobody reads any more (hist<2> the level-0
 // histogram, compact the level-1 histogram), and the last compaction block of a row to
-// finish clears the rest of that row (level-2 histogram, records, row state and
-// counters).
+// finish (in the decode step, the row's resolve block) clears the rest of that row
+// (level-2 histogram, records, row state and counters).
 #include <cmath>
 
 #include "rtp_internal.hpp"
@@ -57,7 +60,7 @@ namespace {
 
 constexpr int kCoarse = 64;          // coarse bins of levels 0/1 (32 at level 2)
 constexpr int kFinePer = 32;         // fine bins under one coarse bin
-constexpr int kRecPairs = 3;         // (digit, count) pairs a tile record holds (one per 32-bit word)
+constexpr int kRecPairs = 3;         // (digit, count) pairs a record holds (one per 32-bit word)
 
 __device__ __forceinline__ uint64_t ld_rlx(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     }
   }
   __syncthreads();
-  // This block reads no more of the tile records and tables, the level-2 histogram or the row state:
+  // This block reads no more of the records and tables, the level-2 histogram or the row state:
   // count it as done now, and learn whether it was the last one only at the end.
   uint32_t done_before = 0;
   if (tid == 0) done_before = atomicAdd(ctr + 1, 1u);
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_compact(SelArgs a) {
     if (take) out[a_before + (e_before < r ? e_before : r)] = int32_t(base + it * kSelThreads + tid);
   }
   // the last block of the row to be counted clears what this launch read: every other
-  // block has finished its reads of the tile records, the level-2 histogram and the state
+  // block has finished its reads of the records, the level-2 histogram and the state
   if (tid == 0) s_last = (done_before == uint32_t(nblk - 1));
   __syncthreads();
   if (s_last) {
