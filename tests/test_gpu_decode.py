@@ -623,6 +623,47 @@ def test_fused_step_tie_groups_across_ranges(p):
         assert part, "no tie group is cut"
 
 
+def test_fused_step_near_flat_scores():
+    """Near-flat scores: the query indexer vector is (1, 2^-14 (h+1), 0, ...) and every key
+    (5, r_j, 0, ...) with r_j spread over [-1, 1], so the scores are 5 + r_j 2^-14 (h+1) (up
+    to the indexer scale): all within a few 22-bit key prefixes, with many distinct low digits
+    in every range.  The resolve then reads the heavy ranges' tables.  Fused step against the
+    separate calls, bit for bit, twice on one workspace (the tables are scratch that the
+    second call overwrites)."""
+    P.require_gpu()
+    torch = _torch()
+    n, G, D = 40000, 4, 128
+    L = rtp.Layer(2, G, 1, D, n, [1], 4, 64)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    bf = lambda *shape, s=1.0: (torch.randn(*shape, generator=gen, device="cuda") * s).to(torch.bfloat16)
+    q = bf(2, G, D)
+    q_pre = torch.zeros(2, G, D, device="cuda")
+    q_pre[:, :, 0] = 1.0
+    w_q_idx = torch.zeros(G, D, 16, device="cuda")
+    w_q_idx[:, 0, 0] = 1.0
+    w_q_idx[:, 0, 1] = torch.tensor([2.0 ** -14 * (h + 1) for h in range(G)], device="cuda")
+    k_idx = torch.zeros(2, 1, n, 16, device="cuda")
+    k_idx[..., 0] = 5.0
+    k_idx[..., 1] = torch.rand(2, 1, n, generator=gen, device="cuda") * 2 - 1
+    q_pre, w_q_idx, k_idx = q_pre.to(torch.bfloat16), w_q_idx.to(torch.bfloat16), k_idx.to(torch.bfloat16)
+    k, v = bf(2, 1, n, D), bf(2, 1, n, D)
+    ref = rtp.DecodeStep(L, n, 0.9, fused=False)
+    ref.run(q_pre, q, k, v, k_idx, w_q_idx)
+    fused = rtp.DecodeStep(L, n, 0.9, fused=True)
+    for rep in range(2):
+        fused.run(q_pre, q, k, v, k_idx, w_q_idx)
+        torch.cuda.synchronize()
+        _assert_same(_step_outputs(ref, 2, G, n), _step_outputs(fused, 2, G, n), f"near-flat, call {rep}")
+        assert not fused.ws[rtp.CALL_DECODE_STEP][:P.sel_zero_bytes(L, n)].any().item()
+    # the rows are near-flat indeed: a large share of the context is selected, and a range
+    # holds many distinct candidate scores
+    cnt = ref.sel_count.cpu().numpy()
+    assert cnt.min() > n // 4, cnt
+    sc = ref.scores.view(2, G, -1)[0, 0, :1024].cpu().numpy()
+    assert np.unique(sc).size > 100
+
+
 def test_fused_step_beyond_1m_tokens():
     """More than 1024 ranges per row (2^21 + 1234 tokens): the resolve block scans the row's
     records in more than one round, and the radix passes use 8192-token tiles of eight
