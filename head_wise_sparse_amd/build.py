@@ -74,6 +74,16 @@ def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR, extra=()) -> s
     return obj
 
 
+def device_asm(src: str, out_path: str) -> str:
+    """gfx950 assembly of one source's device code, with the library's flags (for checks
+    of the generated instruction stream)."""
+    cmd = [hipcc()] + HIP_FLAGS + ["--cuda-device-only", "-S", src, "-o", out_path]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stdout}{r.stderr}")
+    return out_path
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
