@@ -27,8 +27,9 @@ namespace {
 
 static_assert(kScoreThreads == kDecThreads, "scoring and decode blocks share one launch");
 
+// (eight heads per group keep more accumulators than four waves per SIMD leave registers for)
 template <int G, int D>
-__global__ __launch_bounds__(kDecThreads, 4) void k_step_score_window(ScoreArgs sa, int n_score, int score_gx,
+__global__ __launch_bounds__(kDecThreads, G >= 8 ? 2 : 4) void k_step_score_window(ScoreArgs sa, int n_score, int score_gx,
                                                                       DecArgs wa, int win_gx) {
   const int i = blockIdx.x;
   if (i < n_score) {
