@@ -20,8 +20,9 @@ hand-worked golden rows (tests/golden/), p=1 and window>=N reduce to dense
 attention checked against torch's float64 scaled_dot_product_attention, q=0
 reduces to the mean of V over exactly the attended set, bilinearity and
 position-independence of indexer scores, torch's float32->bfloat16 RNE cast for
-the bf16 store.  The recall statistic is reported only: parity unpinned beyond
-its S = all-tokens special case.
+the bf16 store, and the recall statistic on a hand-worked three-key case (its
+softmax scale included) and the all-tokens case.  Recall is computed but not
+reported by the benchmark.
 """
 from __future__ import annotations
 
