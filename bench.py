@@ -637,7 +637,7 @@ def main():
                                       "traffic": measured_traffic("sparse_decode"), "algorithmic_bytes": sp_bytes,
                                       "kernel": "rtp_sparse_decode_attn (k_decode_partial + k_decode_merge)", "us": round(calls["sparse_decode"] * 1e3, 2)}
         # for reference: the four separate calls in one graph, and the fused call replayed
-        # from a HIP graph (the graph adds a gap between its kernels on this stack)
+        # from a HIP graph (consecutive replays leave the GPU idle between them on this stack)
         for i in range(len(dec.sets)):
             dec.graph(p0, i, "separate").replay()
             dec.step_graph(p0, i)
