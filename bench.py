@@ -38,7 +38,7 @@ BF16_PEAK_TFLOPS = 2500.0
 COPY_SCALE = {"fetch": 1.9999, "write": 1.0000}
 MEASURED_KIB = {
     "prefill_attn": {"src": ("rtp_prefill.hip", "9c8e4c2435f8d8e8"),
-                     "fetch": 212424.8, "write": 41408.9},
+                     "fetch": 211933.4, "write": 41691.5},
     "sparse_decode": {"src": ("decode_dev.hpp", "e31967e96b51ec13"),
                       "fetch": 172546.0 + 1086.5, "write": 2176.3 + 8.0},
 }
