@@ -66,8 +66,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the p = 0.9 / 0.99 decode timings")
     ap.add_argument("--gen-steps", type=int, default=128,
                     help="generated tokens of the growing-context workload (0: skip it)")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
-                    help="run only one part (for profiling); the JSON line is still printed")
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_1m"], default=None,
+                    help="run only one part (for profiling); the JSON line is still printed "
+                         "(prefill_1m: the 1M-token chunked prefill alone, as one timing report line)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the timings of the other decode and prefill workloads in the default run")
     ap.add_argument("--report-configs", action="store_true",
@@ -583,6 +584,11 @@ def main():
         return
     if args.report_configs:
         report_configs(args)
+        return
+    if args.only == "prefill_1m":          # the 1M-token prefill alone (for profiling): one report line
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({"report": "prefill_1m timing", "configs": config_timings(args, ["prefill_1m"])}), flush=True)
         return
     import torch
     from head_wise_sparse_amd import rtp
